@@ -1,0 +1,430 @@
+"""Plain fp64 CPU oracle for absorbed MLA decode (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this module.  It never calls the HIP library and the HIP library never calls
+it.  Every function states the passage of the pages it follows:
+
+  [huny]    blog.huny.dev, "DeepSeek Multi-Head Latent Attention(MLA) 해부:
+            저차원 KV 압축과 Decoupled RoPE를 통한 VRAM 98% 절감 및 행렬 흡수 ..."
+  [donmain] donmain.dev/llm/attention-variants, "KV Cache를 10분의 1로 줄인
+            MLA의 트릭"
+  [vllm]    blog.secrett2633.cloud/opensource/vllm/mla, "[vLLM] Multi-head
+            Latent Attention: KV 캐시를 압축하는 DeepSeek의 어텐션"
+  [thaki]   thakicloud.com/.../transformer-attention-kv-cache-math
+
+Parity pins (what each function is checked against, other than itself) are
+recorded in PIN_STATUS below and exercised by tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+__all__ = [
+    "PIN_STATUS", "FMT_F32", "FMT_BF16", "FMT_FP8_E4M3", "BLOCK",
+    "lib", "build_oracle",
+    "kv_bytes_per_token_layer", "kv_cache_bytes", "floats_per_token_all_layers",
+    "bf16_bits_to_f64", "e4m3_to_f64", "f64_to_e4m3", "block_bytes",
+    "gather", "decode", "combine", "decode_splits",
+    "rope", "project_kv", "project_queries_direct", "project_queries_lowrank",
+    "absorb_q", "absorb_out", "fused_out_weights", "absorb_out_fused",
+    "score_split", "unabsorbed_mha",
+]
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "mla_oracle.c"
+_SO = _HERE / "liboracle.so"
+
+FMT_F32, FMT_BF16, FMT_FP8_E4M3 = 0, 1, 2
+BLOCK = 64  # tokens per paged block ([vllm] "FlashMLABackend: 하드웨어 요구사항")
+
+# How each oracle function is pinned to something other than itself.
+PIN_STATUS = {
+    "kv_bytes_per_token_layer": "pinned: every cache size printed on the pages (tests/golden/cache_sizes.json)",
+    "bf16_bits_to_f64": "pinned: torch bf16->fp64 cast over all 65536 codes",
+    "e4m3_to_f64": "pinned: OCP E4M3 landmark values + torch float8_e4m3fn->fp64 over all 256 codes",
+    "f64_to_e4m3": "pinned: torch float8_e4m3fn cast (RNE, ties, subnormals, saturation)",
+    "gather": "pinned: contiguous logical rows scattered through a random block table come back bit-exact",
+    "decode": "pinned: torch SDPA fp64 (MQA, one KV head); S=1 and q=0 closed forms; "
+              "un-absorbed MHA equivalence; block-table permutation invariance; "
+              "causal q_len=2 == q_len=1 on the truncated sequence",
+    "combine": "pinned: split invariance against the unsplit decode for random partitions",
+    "rope": "pinned: norm preservation, relative-position property, complex-multiply form",
+    "absorb_q": "pinned: absorbed score equals score against explicitly reconstructed keys",
+    "absorb_out": "pinned: equals explicit per-head value reconstruction followed by W^O",
+    "absorb_out_fused": "pinned: W^UV W^O fusion equals the unfused path",
+    "unabsorbed_mha": "pinned: torch SDPA fp64 per head (textbook multi-head attention)",
+    "paper_case_values": "parity unpinned: the -22.3809850107 and -6.073908192658 values of the "
+                         "pages' five-case script have no seed or shapes",
+}
+
+
+# ----------------------------------------------------------------------------
+# Build / load the C part
+# ----------------------------------------------------------------------------
+
+def build_oracle(force: bool = False) -> Path:
+    """Compile mla_oracle.c with gcc (fp64, OpenMP over output rows)."""
+    if force or not _SO.exists() or _SO.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _SO.with_suffix(f".so.tmp{os.getpid()}")
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+             "-o", str(tmp), str(_SRC), "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        so = build_oracle()
+        L = ctypes.CDLL(str(so))
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f64.restype = dbl
+        L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_to_f64.restype = dbl
+        L.oracle_f64_to_e4m3.argtypes = [dbl]
+        L.oracle_f64_to_e4m3.restype = ctypes.c_uint8
+        L.oracle_block_bytes.argtypes = [i32, i32, i32]
+        L.oracle_block_bytes.restype = i64
+        L.oracle_gather.argtypes = [P, i32, i32, i32, P, i32, P, i32, i32, P]
+        L.oracle_gather.restype = i32
+        L.oracle_decode.argtypes = [P, i32, P, P, i32, P, i32, i32, i32, i32, i32,
+                                    P, P, dbl, P, P, P, i64, P, P]
+        L.oracle_decode.restype = i32
+        L.oracle_combine.argtypes = [P, P, i32, i64, i32, P, P]
+        L.oracle_combine.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _np(x, dtype=None):
+    """Host array view of a numpy array or CPU torch tensor (no arithmetic)."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu()
+        if dtype is not None and str(x.dtype) in ("torch.bfloat16", "torch.float8_e4m3fn"):
+            raise TypeError("pass raw bits for reduced formats")
+        x = x.numpy()
+    x = np.ascontiguousarray(x)
+    if dtype is not None:
+        x = np.ascontiguousarray(x, dtype=dtype)
+    return x
+
+
+# ----------------------------------------------------------------------------
+# Closed-form cache sizes
+# ----------------------------------------------------------------------------
+
+def kv_bytes_per_token_layer(kind: str, *, n_h: int = 0, d_h: int = 0, groups: int = 0,
+                             d_c: int = 0, d_r: int = 0, bytes_per: int = 2) -> int:
+    """Cache bytes one token occupies in one layer.
+
+    MHA keeps a key and a value per head: 2 * n_h * d_h * P ([huny] §1 memory
+    formula).  GQA keeps one pair per group: 2 * g * d_h * P ([huny] §1, §4
+    table; [thaki] "논문 공식을 코드로 옮기기").  MQA is GQA with g = 1
+    ([donmain] "공유의 한계": 2 * d_h floor).  MLA keeps the latent and the
+    shared RoPE key: (d_c + d_R) * P ([donmain] "MLA, 압축이라는 다른 길" 576
+    = 512 + 64; [huny] §4 table).
+    """
+    if kind == "mha":
+        return 2 * n_h * d_h * bytes_per
+    if kind == "gqa":
+        return 2 * groups * d_h * bytes_per
+    if kind == "mqa":
+        return 2 * d_h * bytes_per
+    if kind == "mla":
+        return (d_c + d_r) * bytes_per
+    raise ValueError(kind)
+
+
+def kv_cache_bytes(kind: str, *, layers: int, tokens: int, **kw) -> int:
+    """Whole-request cache: per-token-per-layer bytes x layers x tokens
+    ([huny] §1 memory formula, factors L and S)."""
+    return kv_bytes_per_token_layer(kind, **kw) * layers * tokens
+
+
+def floats_per_token_all_layers(kind: str, *, layers: int, kv_heads: int = 0,
+                                d_head: int = 0, d_latent: int = 0) -> int:
+    """Cache floats per token summed over layers as [thaki] counts them
+    ("논문 공식을 코드로 옮기기"): layers * kv_heads * 2 * d_head for MHA/GQA,
+    layers * d_L for the latent (one shared vector per token and layer)."""
+    if kind == "mla":
+        return layers * d_latent
+    return layers * kv_heads * 2 * d_head
+
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 (upper half of binary32), exact."""
+    L = lib()
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    out = np.array([L.oracle_bf16_to_f64(int(b)) for b in flat], dtype=np.float64)
+    return out.reshape(np.shape(bits))
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes -> float64, from the format definition."""
+    L = lib()
+    table = np.array([L.oracle_e4m3_to_f64(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def f64_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """float64 -> E4M3 codes, round-to-nearest-even, saturating at +-448."""
+    L = lib()
+    flat = np.asarray(x, dtype=np.float64).ravel()
+    out = np.array([L.oracle_f64_to_e4m3(float(v)) for v in flat], dtype=np.uint8)
+    return out.reshape(np.shape(x))
+
+
+def block_bytes(fmt: int, d_c: int, d_r: int) -> int:
+    return int(lib().oracle_block_bytes(fmt, d_c, d_r))
+
+
+# ----------------------------------------------------------------------------
+# Paged cache and decode (C part)
+# ----------------------------------------------------------------------------
+
+def gather(pool, fmt, d_c, d_r, block_table, seq_lens, max_tokens) -> np.ndarray:
+    """Bytes of each sequence's logical rows, out[b][p] for p < seq_lens[b]
+    (paged block table, [huny] §6; [vllm] "MLA의 MQA 디코딩 경로").
+    Rows past seq_lens[b] are zero."""
+    pool = _np(pool)
+    bt = _np(block_table, np.int32)
+    sl = _np(seq_lens, np.int32)
+    B, stride = bt.shape
+    row_bytes = block_bytes(fmt, d_c, d_r) // BLOCK
+    out = np.zeros((B, max_tokens, row_bytes), dtype=np.uint8)
+    rc = lib().oracle_gather(_ptr(pool), fmt, d_c, d_r, _ptr(bt), stride, _ptr(sl),
+                             B, max_tokens, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_gather failed ({rc})")
+    return out
+
+
+def decode(pool, fmt, block_table, seq_lens, q_lat, q_rope, scale, *, q_len=1,
+           block_scales=None, win_lo=None, win_hi=None, rows=None):
+    """Absorbed decode in fp64: see oracle_decode in mla_oracle.c.
+
+    q_lat: [B*q_len, n_h, d_c] and q_rope: [B*q_len, n_h, d_r], any real dtype
+    (converted to float64 exactly).  Returns (o_lat, lse) as float64 with shapes
+    [B*q_len, n_h, d_c] / [B*q_len, n_h], or [n_rows, d_c] / [n_rows] when
+    `rows` lists flat row indices.
+    """
+    pool = _np(pool)
+    bt = _np(block_table, np.int32)
+    sl = _np(seq_lens, np.int32)
+    ql = _np(q_lat, np.float64)
+    qr = _np(q_rope, np.float64)
+    T, n_h, d_c = ql.shape
+    d_r = qr.shape[2]
+    B = bt.shape[0]
+    assert T == B * q_len and qr.shape[:2] == (T, n_h)
+    bs = None if block_scales is None else _np(block_scales, np.float32)
+    lo = None if win_lo is None else _np(win_lo, np.int32)
+    hi = None if win_hi is None else _np(win_hi, np.int32)
+    rws = None if rows is None else _np(rows, np.int64)
+    n_out = T * n_h if rws is None else rws.size
+    o = np.empty((n_out, d_c), dtype=np.float64)
+    lse = np.empty((n_out,), dtype=np.float64)
+    rc = lib().oracle_decode(_ptr(pool), fmt, _ptr(bs), _ptr(bt), bt.shape[1], _ptr(sl),
+                             B, q_len, n_h, d_c, d_r, _ptr(ql), _ptr(qr), float(scale),
+                             _ptr(lo), _ptr(hi), _ptr(rws), 0 if rws is None else rws.size,
+                             _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle_decode failed ({rc})")
+    if rws is None:
+        return o.reshape(T, n_h, d_c), lse.reshape(T, n_h)
+    return o, lse
+
+
+def combine(o_part, lse_part):
+    """Merge per-split results: o_part [S][rows][d_c], lse_part [S][rows]."""
+    op = _np(o_part, np.float64)
+    lp = _np(lse_part, np.float64)
+    S, rows, d_c = op.shape
+    o = np.empty((rows, d_c), dtype=np.float64)
+    lse = np.empty((rows,), dtype=np.float64)
+    lib().oracle_combine(_ptr(op), _ptr(lp), S, rows, d_c, _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def decode_splits(pool, fmt, block_table, seq_lens, q_lat, q_rope, scale, bounds, *,
+                  q_len=1, block_scales=None):
+    """Per-split partials: bounds is a list of (win_lo[B], win_hi[B]) arrays.
+    Returns o_part [S][T*n_h][d_c], lse_part [S][T*n_h]."""
+    os_, ls_ = [], []
+    for lo, hi in bounds:
+        o, l = decode(pool, fmt, block_table, seq_lens, q_lat, q_rope, scale, q_len=q_len,
+                      block_scales=block_scales, win_lo=lo, win_hi=hi)
+        os_.append(o.reshape(-1, o.shape[-1]))
+        ls_.append(l.reshape(-1))
+    return np.stack(os_), np.stack(ls_)
+
+
+# ----------------------------------------------------------------------------
+# Projections, RoPE and the un-absorbed reference (numpy, fp64)
+# ----------------------------------------------------------------------------
+
+def rope(x: np.ndarray, positions: np.ndarray, base: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding of the last axis (decoupled RoPE input,
+    [huny] §2-3; [donmain] "위치 정보와 압축의 충돌").  The pages do not fix
+    the pairing: adjacent pairs (2j, 2j+1) are rotated by angle p * theta_j
+    with theta_j = base^(-2j/d).  positions broadcasts against x[..., 0]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % 2 == 0
+    j = np.arange(d // 2, dtype=np.float64)
+    theta = base ** (-2.0 * j / d)
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * theta
+    cos, sin = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * cos - x1 * sin
+    out[..., 1::2] = x0 * sin + x1 * cos
+    return out
+
+
+def project_kv(h: np.ndarray, w_dkv: np.ndarray, d_c: int, positions: np.ndarray):
+    """Cached row of each token: c = h W^DKV ([huny] §2-1 compression equation)
+    and k^R = RoPE(h W^KR) ([huny] §2-3 shared rotary key).  W^DKV and W^KR
+    are read as the first d_c and the remaining columns of one matrix."""
+    z = np.asarray(h, np.float64) @ np.asarray(w_dkv, np.float64)
+    c = z[:, :d_c]
+    kr = rope(z[:, d_c:], positions)
+    return c, kr
+
+
+def project_queries_direct(h: np.ndarray, w_q: np.ndarray, n_h: int, d_nope: int,
+                           d_r: int, positions: np.ndarray):
+    """Per-head query [q^C_i ; q^R_i] from one projection of h; q^R is rotated
+    at the query's position ([huny] §2-3 rotary query and concatenation)."""
+    z = (np.asarray(h, np.float64) @ np.asarray(w_q, np.float64)).reshape(-1, n_h, d_nope + d_r)
+    q_nope = z[:, :, :d_nope]
+    q_rope = rope(z[:, :, d_nope:], np.asarray(positions)[:, None])
+    return q_nope, q_rope
+
+
+def project_queries_lowrank(h, w_dq, w_uq, w_qr, n_h, d_nope, d_r, positions):
+    """Low-rank query path: c^Q = h W^DQ, q^C_i = c^Q W^UQ_i ([huny] §2-2), and
+    q^R_i = RoPE(h W^QR_i) ([huny] §2-3, read literally from h)."""
+    h = np.asarray(h, np.float64)
+    cq = h @ np.asarray(w_dq, np.float64)
+    q_nope = (cq @ np.asarray(w_uq, np.float64)).reshape(-1, n_h, d_nope)
+    q_rope = rope((h @ np.asarray(w_qr, np.float64)).reshape(-1, n_h, d_r),
+                  np.asarray(positions)[:, None])
+    return q_nope, q_rope
+
+
+def absorb_q(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """q~_{t,i} = q^C_{t,i} (W^UK_i)^T, one d_c-wide vector per head
+    ([huny] §3-1 absorption equation; [donmain] column form W^UK^T q).
+    q_nope [T][n_h][d_nope], w_uk [n_h][d_c][d_nope] -> [T][n_h][d_c]."""
+    q = np.asarray(q_nope, np.float64)
+    w = np.asarray(w_uk, np.float64)
+    out = np.empty((q.shape[0], q.shape[1], w.shape[1]), dtype=np.float64)
+    for i in range(q.shape[1]):
+        out[:, i, :] = q[:, i, :] @ w[i].T
+    return out
+
+
+def absorb_out(o_lat: np.ndarray, w_uv: np.ndarray, w_o: np.ndarray):
+    """u_{t,i} = (sum_j A c_j) W^UV_i ([huny] §3-2 value equation), then
+    Output_t = sum_i u_{t,i} W^O_i with W^O_i the i-th d_v-row block of W^O
+    ([huny] §3-2 output equation).  o_lat [T][n_h][d_c], w_uv [n_h][d_c][d_v],
+    w_o [n_h*d_v][d_model].  Returns (u [T][n_h][d_v], out [T][d_model])."""
+    o = np.asarray(o_lat, np.float64)
+    wv = np.asarray(w_uv, np.float64)
+    wo = np.asarray(w_o, np.float64)
+    T, n_h, _ = o.shape
+    d_v = wv.shape[2]
+    u = np.empty((T, n_h, d_v), dtype=np.float64)
+    for i in range(n_h):
+        u[:, i, :] = o[:, i, :] @ wv[i]
+    out = np.zeros((T, wo.shape[1]), dtype=np.float64)
+    for i in range(n_h):
+        out += u[:, i, :] @ wo[i * d_v:(i + 1) * d_v, :]
+    return u, out
+
+
+def fused_out_weights(w_uv: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """W^combined_i = W^UV_i W^O_i in R^{d_c x d} ([huny] §3-2 output equation)."""
+    wv = np.asarray(w_uv, np.float64)
+    wo = np.asarray(w_o, np.float64)
+    d_v = wv.shape[2]
+    return np.stack([wv[i] @ wo[i * d_v:(i + 1) * d_v, :] for i in range(wv.shape[0])])
+
+
+def absorb_out_fused(o_lat: np.ndarray, w_comb: np.ndarray) -> np.ndarray:
+    """Output_t = sum_i o_{t,i} W^combined_i ([huny] §3-2)."""
+    o = np.asarray(o_lat, np.float64)
+    out = np.zeros((o.shape[0], w_comb.shape[2]), dtype=np.float64)
+    for i in range(o.shape[1]):
+        out += o[:, i, :] @ w_comb[i]
+    return out
+
+
+def score_split(q_c, q_r, k_c, k_r):
+    """Concatenated-vector score and its content + position parts
+    ([huny] §2-3 decomposition equation).  Returns (full, content, position)."""
+    q = np.concatenate([q_c, q_r])
+    k = np.concatenate([k_c, k_r])
+    return float(q @ k), float(q_c @ k_c), float(q_r @ k_r)
+
+
+def unabsorbed_mha(c, kr, q_nope, q_rope, w_uk, w_uv, w_o, scale, query_pos):
+    """Textbook multi-head attention with explicitly reconstructed keys and
+    values, the path absorption removes ([huny] §2-1 up-projections,
+    §2-3 concatenated q/k; [huny] §6 'naive fallback').
+
+    c [S][d_c], kr [S][d_r] (already rotated), q_nope [T][n_h][d_nope],
+    q_rope [T][n_h][d_r] (rotated), query_pos [T]: query t sees positions
+    <= query_pos[t].  Returns (o_lat_equiv [T][n_h][d_c] = sum_j A c_j,
+    u [T][n_h][d_v], out [T][d_model], lse [T][n_h])."""
+    c = np.asarray(c, np.float64)
+    kr = np.asarray(kr, np.float64)
+    wk = np.asarray(w_uk, np.float64)
+    wv = np.asarray(w_uv, np.float64)
+    wo = np.asarray(w_o, np.float64)
+    T, n_h, _ = np.shape(q_nope)
+    d_v = wv.shape[2]
+    o_lat = np.zeros((T, n_h, c.shape[1]))
+    u = np.zeros((T, n_h, d_v))
+    lse = np.zeros((T, n_h))
+    for i in range(n_h):
+        k_full = np.concatenate([c @ wk[i], kr], axis=1)   # [S][d_nope + d_r]
+        v_full = c @ wv[i]                                 # [S][d_v]
+        for t in range(T):
+            n = int(query_pos[t]) + 1
+            qf = np.concatenate([np.asarray(q_nope[t, i], np.float64),
+                                 np.asarray(q_rope[t, i], np.float64)])
+            s = scale * (k_full[:n] @ qf)
+            m = s.max()
+            e = np.exp(s - m)
+            a = e / e.sum()
+            u[t, i] = a @ v_full[:n]
+            o_lat[t, i] = a @ c[:n]
+            lse[t, i] = m + math.log(e.sum())
+    out = np.zeros((T, wo.shape[1]))
+    for i in range(n_h):
+        out += u[:, i, :] @ wo[i * d_v:(i + 1) * d_v, :]
+    return o_lat, u, out, lse
