@@ -1,0 +1,241 @@
+/*
+ * mla.h — C ABI of the absorbed Multi-head Latent Attention decode library
+ * for AMD MI355X (gfx950).
+ *
+ * What it computes (the pages on DeepSeek MLA):
+ *   - every cached token is one row [c (d_c) | k^R (d_r)], the low-rank latent
+ *     and the shared rotary key (blog.huny.dev "DeepSeek MLA 해부" §2-1 and
+ *     §2-3; donmain.dev "KV Cache를 10분의 1로 줄인 MLA의 트릭", section
+ *     "위치 정보와 압축의 충돌": 512 + 64 = 576);
+ *   - the query's content part is absorbed through W^UK once per token
+ *     (huny §3-1 absorption equation): mla_absorb_q;
+ *   - all heads then attend MQA-style to the one latent "head"
+ *     (blog.secrett2633.cloud "[vLLM] Multi-head Latent Attention", section
+ *     "MLA의 MQA 디코딩 경로") with score q~.c + q^R.k^R (huny §2-3
+ *     decomposition equation) and a softmax: mla_decode;
+ *   - the latent output sum_j A c_j is mapped back through W^UV and W^O
+ *     (huny §3-2 value and output equations): mla_absorb_out.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are device pointers unless the name ends in _host.
+ *   - The caller owns every buffer; the library allocates nothing and keeps
+ *     no device state between calls.
+ *   - Calls are asynchronous on `stream`; host-side argument checks run before
+ *     any launch and a failing check launches nothing.
+ *   - Every call returns an mla_status_t; mla_last_error() returns a
+ *     thread-local message for the last failure on the calling thread.
+ *   - No C++ exception crosses the ABI.  Calls are thread-safe.
+ *   - Row-major layouts throughout; "T" is the number of query tokens
+ *     (B * q_len, sequence-major: token index = b * q_len + t).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *mla_stream_t; /* == hipStream_t */
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, empty cache, missing plan */
+    MLA_ERR_UNSUPPORTED = 2,  /* block size != 64, dtype or dims not instantiated */
+    MLA_ERR_ALIGN = 3,        /* pointer or row not 16-byte aligned */
+    MLA_ERR_WORKSPACE = 4,    /* workspace smaller than the plan needs */
+    MLA_ERR_HIP = 5           /* a HIP launch or runtime call failed */
+} mla_status_t;
+
+typedef enum {
+    MLA_DT_F32 = 0,
+    MLA_DT_BF16 = 1,
+    MLA_DT_FP8_E4M3 = 2       /* OCP E4M3 ("fn": no infinities, S.1111.111 = NaN) */
+} mla_dtype_t;
+
+/* Tokens per paged block.  The pages' decode kernel accepts only 64-token
+ * blocks, sized to its tile (vLLM MLA page, "FlashMLABackend: 하드웨어 요구사항");
+ * here too a block is exactly one decode tile. */
+#define MLA_BLOCK_SIZE 64
+
+/*
+ * Paged latent cache (huny §6 PagedAttention item; vLLM MLA page, the combined
+ * kv_c_and_k_pe cache of "FlashMLAImpl").  `base` holds num_blocks blocks of
+ * 64 token rows each:
+ *   kv_dtype F32 / BF16: block = [64][d_c + d_r] rows of [c | k^R] in that type
+ *                        (bf16 at d_c=512, d_r=64: 73,728 B per block);
+ *   kv_dtype FP8_E4M3:   block = c codes [64][d_c] (e4m3) followed by k^R
+ *                        [64][d_r] in bf16 (the rotary key keeps 16-bit
+ *                        precision, huny §6 FP8 item; 40,960 B per block), and
+ *                        block_scales[num_blocks] (fp32) holds the one
+ *                        dequantisation scale of each block: c = code * scale.
+ * Blocks are 256-byte aligned when base is (block bytes are multiples of 256
+ * for the instantiated dims).  Rows past a sequence's length may hold
+ * anything, including NaN: no result depends on them.
+ */
+typedef struct {
+    const void *base;
+    const float *block_scales;  /* FP8_E4M3 only, else NULL */
+    int64_t num_blocks;
+    int32_t block_size;         /* must be MLA_BLOCK_SIZE */
+    int32_t d_c;                /* latent width */
+    int32_t d_r;                /* rotary key width */
+    mla_dtype_t kv_dtype;
+} mla_cache_desc_t;
+
+/*
+ * Split-KV plan (the tile-scheduler metadata of the vLLM MLA page,
+ * get_mla_metadata / num_splits in "MLA의 MQA 디코딩 경로" and "FP8 MLA 지원").
+ * Filled by mla_decode_plan on the host.
+ */
+typedef struct {
+    int32_t B, q_len, n_h, d_c;
+    int32_t num_items;      /* work items (workgroups per row chunk) */
+    int32_t row_chunks;     /* query-row chunks per sequence (128 rows each on the MFMA path) */
+    int32_t num_partials;   /* partial-result slots (sequences with >1 split) */
+    int32_t needs_combine;  /* 1 if mla_decode launches the LSE combine */
+    int32_t max_splits;     /* largest split count of any sequence */
+    int32_t blocks_per_item;/* target blocks per work item */
+    int64_t plan_ints;      /* int32 entries of the device plan */
+    int64_t workspace_bytes;/* partial-result workspace mla_decode needs */
+} mla_plan_t;
+
+/*
+ * mla_decode_plan — host only, pure, makes no HIP call.
+ *
+ * Splits every sequence's ceil(seq_len/64) blocks into contiguous ranges so
+ * that the total work fills `num_cus` compute units (per-item share
+ * ceil(total_blocks * row_chunks / num_cus) blocks, at least 1), and lists
+ * one work item {b, blk_begin, blk_end, slot} per range.
+ *
+ * seq_lens_host [B]: tokens per sequence, counting the q_len query tokens
+ *                    (each query token's own row is already in the cache).
+ * plan_host:         int32 array of plan_capacity entries, or NULL to only
+ *                    size the plan (info is filled either way).
+ * Layout written: [num_items, B, row_chunks, num_partials],
+ *                 items[num_items][4] = {b, blk_begin, blk_end, slot (-1 = final)},
+ *                 split_off[B + 1] (partial slots of sequence b are
+ *                 split_off[b] .. split_off[b+1]-1),
+ *                 seq_flags[B] (1 = decode writes the final output directly).
+ * The caller copies plan_host to device memory (plan_ints int32 entries)
+ * and passes it to mla_decode with the same seq_lens.
+ * Errors: INVALID_ARG for B < 1, q_len < 1, n_h < 1, negative lengths,
+ * num_cus < 1, a too-small plan_capacity; UNSUPPORTED for dtypes.
+ */
+mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_len,
+                             int32_t n_h, int32_t d_c, int32_t d_r, mla_dtype_t kv_dtype,
+                             int32_t num_cus, int32_t *plan_host, int64_t plan_capacity,
+                             mla_plan_t *info);
+
+/*
+ * mla_decode — absorbed MLA decode over the paged latent cache.
+ *
+ * For query row (b, t, h): visible positions p <= seq_lens[b] - q_len + t
+ * (speculative multi-token queries are causal within the step, vLLM MLA
+ * page "FlashMLAImpl", reshape for spec decode);
+ *   s_p   = scale * (q_lat[b,t,h] . c_p + q_rope[b,t,h] . k^R_p)
+ *   o_lat = sum_p softmax(s)_p c_p       (latent-space value sum, huny §3-2)
+ *   lse   = ln sum_p exp(s_p)            (natural log; vLLM MLA page,
+ *                                         can_return_lse_for_decode)
+ * A row with no visible position gets o_lat = 0 and lse = -inf.
+ *
+ * q_lat  [T][n_h][d_c], q_rope [T][n_h][d_r] in q_dtype (F32 or BF16); the
+ *        pages pass q as the pair (q_nope_absorbed, q_pe) — here two pointers.
+ * cache  see mla_cache_desc_t.  Fast paths: kv BF16 or FP8_E4M3 with q BF16,
+ *        d_c = 512, d_r = 64 (MFMA); every other supported combination runs a
+ *        generic kernel (d_c <= 1024, d_r <= 256, d_c and d_r multiples of 4).
+ * block_table [B][bt_stride] int32 pool block ids; entries past
+ *        ceil(seq_lens[b]/64) are never read.
+ * seq_lens [B] int32 (device), the same values the plan was built from.
+ * scale  softmax scale; the pages give none — the absorbed score keeps the
+ *        un-absorbed logits, so pass 1/sqrt(d_nope + d_r) for those.
+ * plan / plan_dev  from mla_decode_plan (host struct, device copy).
+ * workspace  >= plan->workspace_bytes (may be NULL if that is 0), 256-B aligned.
+ * o_lat  [T][n_h][d_c] in q_dtype; lse [T][n_h] fp32.
+ * Errors: INVALID_ARG (nulls, sizes, plan mismatch, num_blocks < 1),
+ * UNSUPPORTED (block_size != 64, dims/dtypes), ALIGN, WORKSPACE, HIP.
+ */
+mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
+                        const mla_cache_desc_t *cache, const int32_t *block_table,
+                        int32_t bt_stride, const int32_t *seq_lens, int32_t B, int32_t q_len,
+                        int32_t n_h, float scale, const mla_plan_t *plan,
+                        const int32_t *plan_dev, void *workspace, int64_t workspace_bytes,
+                        void *o_lat, float *lse, mla_stream_t stream);
+
+/*
+ * mla_combine_lse — merge per-split partial results (the num_splits
+ * reduction named on the vLLM MLA page, "FP8 MLA 지원").  For each sequence b
+ * and row r, with slots k in [split_off[b], split_off[b+1]):
+ *   M = max_k lse_k;  w_k = exp(lse_k - M);
+ *   o = sum_k w_k o_k / sum_k w_k;  lse = M + ln sum_k w_k.
+ * Slots with lse = -inf carry no weight; a sequence whose slots are all -inf
+ * (or that has none) gets o = 0, lse = -inf.
+ * o_part [P][rows][d_c] fp32 (normalised partial outputs), lse_part [P][rows]
+ * fp32, split_off [B+1] int32, seq_flags [B] int32 or NULL: sequences with
+ * flag 1 are skipped (their output is already final).  rows = q_len * n_h.
+ * o_lat [B*rows][d_c] in out_dtype (F32 or BF16); lse [B*rows] fp32.
+ */
+mla_status_t mla_combine_lse(const float *o_part, const float *lse_part,
+                             const int32_t *split_off, const int32_t *seq_flags, int32_t B,
+                             int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dtype,
+                             float *lse, mla_stream_t stream);
+
+/*
+ * mla_absorb_q — W^UK query absorption (huny §3-1; donmain "위치 정보와
+ * 압축의 충돌", q~ = W^UK^T q):
+ *   q_lat[t][h][:] = q_nope[t][h][:] . W_UK[h]^T
+ * q_nope [T][n_h][d_nope] with token stride ld_q elements (>= n_h*d_nope),
+ * w_uk [n_h][d_c][d_nope] (W^UK_i maps the latent to head i's key,
+ * k = c W^UK_i), q_lat [T][n_h][d_c].  dt F32 or BF16 for all three;
+ * accumulation in fp32.  BF16 with d_c % 32 == 0 and d_nope % 16 == 0 runs
+ * on MFMA.
+ */
+mla_status_t mla_absorb_q(const void *q_nope, int64_t ld_q, const void *w_uk, void *q_lat,
+                          int32_t T, int32_t n_h, int32_t d_nope, int32_t d_c,
+                          mla_dtype_t dt, mla_stream_t stream);
+
+/*
+ * mla_absorb_out — map the latent output back (huny §3-2 value and output
+ * equations):
+ *   u[t][h][:] = o_lat[t][h][:] . W_UV[h]          (W_UV [n_h][d_c][d_v])
+ *   out[t][:]  = sum_h u[t][h][:] . W_O[h*d_v:(h+1)*d_v][:]  (W_O [n_h*d_v][d_model])
+ * u_ws [T][n_h][d_v] receives u (caller-provided, same dtype); out [T][d_model].
+ * f32_ws: fp32 scratch of at least mla_absorb_out_workspace() bytes (split-K
+ * partial sums of out); may be NULL when that is 0.
+ * dt F32 or BF16; accumulation in fp32.
+ */
+int64_t mla_absorb_out_workspace(int32_t T, int32_t n_h, int32_t d_v, int32_t d_model,
+                                 mla_dtype_t dt);
+mla_status_t mla_absorb_out(const void *o_lat, const void *w_uv, const void *w_o, void *u_ws,
+                            void *out, void *f32_ws, int64_t f32_ws_bytes, int32_t T,
+                            int32_t n_h, int32_t d_c, int32_t d_v, int32_t d_model,
+                            mla_dtype_t dt, mla_stream_t stream);
+
+/*
+ * mla_gather_paged — copy each sequence's logical rows out of the pool:
+ *   out[b][p][:] = row bytes of token p of sequence b, p < seq_lens[b]
+ * (block bt[b][p/64], slot p%64).  Row bytes: (d_c + d_r) * elem for F32 /
+ * BF16; for FP8_E4M3 the d_c code bytes followed by the 2*d_r bytes of the
+ * bf16 rotary key.  out is [B][max_tokens][row bytes]; rows past seq_lens[b]
+ * are not written.  Bit-exact byte copy.
+ */
+mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *block_table,
+                              int32_t bt_stride, const int32_t *seq_lens, int32_t B,
+                              int32_t max_tokens, void *out, mla_stream_t stream);
+
+/* Bytes of the whole pool described by `cache` (0 on bad arguments). */
+int64_t mla_cache_bytes(const mla_cache_desc_t *cache);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char *mla_last_error(void);
+
+/* Library version string. */
+const char *mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,168 @@
+"""Thin torch binding over libmla's C ABI (same names as the C entry points).
+
+torch supplies device memory and the current HIP stream; every computation
+runs in libmla's kernels.  Functions validate nothing beyond what is needed
+to marshal arguments: the library's own host checks report errors, raised
+here as MLAError.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.DT_F32, torch.bfloat16: L.DT_BF16}
+_KV = {"f32": L.DT_F32, "bf16": L.DT_BF16, "fp8_e4m3": L.DT_FP8_E4M3}
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def num_cus(device=None) -> int:
+    return torch.cuda.get_device_properties(device or torch.cuda.current_device()).multi_processor_count
+
+
+@dataclass
+class DeviceCache:
+    """A paged latent cache resident on the device (see mla_cache_desc_t)."""
+    pool: torch.Tensor                 # uint8 [num_blocks, block_bytes]
+    block_scales: torch.Tensor | None  # float32 [num_blocks] (fp8 only)
+    kv_dtype: str
+    d_c: int
+    d_r: int
+
+    @property
+    def num_blocks(self) -> int:
+        return self.pool.shape[0]
+
+    def desc(self) -> L.CacheDesc:
+        return L.CacheDesc(self.pool.data_ptr(),
+                           None if self.block_scales is None else self.block_scales.data_ptr(),
+                           self.num_blocks, L.BLOCK_SIZE, self.d_c, self.d_r, _KV[self.kv_dtype])
+
+    @staticmethod
+    def from_host(cache, device) -> "DeviceCache":
+        return DeviceCache(cache.pool.to(device),
+                           None if cache.block_scales is None else cache.block_scales.to(device),
+                           cache.kv_dtype, cache.d_c, cache.d_r)
+
+
+def decode_plan(seq_lens_host, q_len: int, n_h: int, d_c: int, d_r: int, kv_dtype: str,
+                cus: int):
+    """mla_decode_plan: returns (Plan, int32 host tensor of plan_ints entries)."""
+    sl = torch.as_tensor(seq_lens_host, dtype=torch.int32).contiguous().cpu()
+    B = sl.numel()
+    lib = L.load()
+    info = L.Plan()
+    L.check(lib.mla_decode_plan(_p(sl), B, q_len, n_h, d_c, d_r, _KV[kv_dtype], cus, None, 0,
+                                ctypes.byref(info)))
+    plan = torch.empty(info.plan_ints, dtype=torch.int32)
+    L.check(lib.mla_decode_plan(_p(sl), B, q_len, n_h, d_c, d_r, _KV[kv_dtype], cus, _p(plan),
+                                plan.numel(), ctypes.byref(info)))
+    return info, plan
+
+
+class Decoder:
+    """Holds the plan (host + device copy) and the partial-result workspace
+    for repeated mla_decode calls over one batch shape."""
+
+    def __init__(self, seq_lens_host, q_len, n_h, d_c, d_r, kv_dtype, device, cus=None):
+        self.device = torch.device(device)
+        self.info, self.plan_host = decode_plan(seq_lens_host, q_len, n_h, d_c, d_r, kv_dtype,
+                                                cus or num_cus(self.device))
+        self.plan_dev = self.plan_host.to(self.device)
+        ws = max(256, self.info.workspace_bytes)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        self.q_len, self.n_h = q_len, n_h
+
+    def __call__(self, q_lat, q_rope, cache: DeviceCache, block_table, seq_lens, scale,
+                 o_lat=None, lse=None, stream=None):
+        return decode(q_lat, q_rope, cache, block_table, seq_lens, self.q_len, self.n_h, scale,
+                      self.info, self.plan_dev, self.workspace, o_lat=o_lat, lse=lse,
+                      stream=stream)
+
+
+def decode(q_lat, q_rope, cache: DeviceCache, block_table, seq_lens, q_len, n_h, scale, plan,
+           plan_dev, workspace, o_lat=None, lse=None, stream=None):
+    """mla_decode: returns (o_lat [T, n_h, d_c] in q's dtype, lse [T, n_h] fp32)."""
+    T = q_lat.shape[0]
+    if o_lat is None:
+        o_lat = torch.empty((T, n_h, cache.d_c), dtype=q_lat.dtype, device=q_lat.device)
+    if lse is None:
+        lse = torch.empty((T, n_h), dtype=torch.float32, device=q_lat.device)
+    B = block_table.shape[0]
+    desc = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    L.check(L.load().mla_decode(_p(q_lat), _p(q_rope), _DT[q_lat.dtype], ctypes.byref(desc),
+                                _p(block_table), block_table.stride(0), _p(seq_lens), B, q_len, n_h,
+                                float(scale), ctypes.byref(plan), _p(plan_dev), _p(workspace),
+                                ws_bytes, _p(o_lat), _p(lse), _stream(stream)))
+    return o_lat, lse
+
+
+def combine_lse(o_part, lse_part, split_off, B, rows, out_dtype=torch.float32, seq_flags=None,
+                stream=None):
+    """mla_combine_lse over partials o_part [P, rows, d_c] / lse_part [P, rows]."""
+    d_c = o_part.shape[-1]
+    o = torch.empty((B * rows, d_c), dtype=out_dtype, device=o_part.device)
+    lse = torch.empty((B * rows,), dtype=torch.float32, device=o_part.device)
+    L.check(L.load().mla_combine_lse(_p(o_part), _p(lse_part), _p(split_off), _p(seq_flags), B,
+                                     rows, d_c, _p(o), _DT[out_dtype], _p(lse), _stream(stream)))
+    return o, lse
+
+
+def absorb_q(q_nope, w_uk, out=None, stream=None):
+    """mla_absorb_q: q_nope [T, n_h, d_nope] (token stride may exceed n_h*d_nope),
+    w_uk [n_h, d_c, d_nope] -> q_lat [T, n_h, d_c]."""
+    T, n_h, d_nope = q_nope.shape
+    d_c = w_uk.shape[1]
+    assert q_nope.stride(2) == 1 and q_nope.stride(1) == d_nope
+    if out is None:
+        out = torch.empty((T, n_h, d_c), dtype=q_nope.dtype, device=q_nope.device)
+    L.check(L.load().mla_absorb_q(_p(q_nope), q_nope.stride(0), _p(w_uk), _p(out), T, n_h, d_nope,
+                                  d_c, _DT[q_nope.dtype], _stream(stream)))
+    return out
+
+
+def absorb_out_workspace_bytes(T, n_h, d_v, d_model, dtype) -> int:
+    return int(L.load().mla_absorb_out_workspace(T, n_h, d_v, d_model, _DT[dtype]))
+
+
+def absorb_out(o_lat, w_uv, w_o, u=None, out=None, ws=None, stream=None):
+    """mla_absorb_out: o_lat [T, n_h, d_c], w_uv [n_h, d_c, d_v], w_o [n_h*d_v, d_model]
+    -> (u [T, n_h, d_v], out [T, d_model])."""
+    T, n_h, d_c = o_lat.shape
+    d_v = w_uv.shape[2]
+    d_model = w_o.shape[1]
+    dev, dt = o_lat.device, o_lat.dtype
+    if u is None:
+        u = torch.empty((T, n_h, d_v), dtype=dt, device=dev)
+    if out is None:
+        out = torch.empty((T, d_model), dtype=dt, device=dev)
+    need = absorb_out_workspace_bytes(T, n_h, d_v, d_model, dt)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    L.check(L.load().mla_absorb_out(_p(o_lat), _p(w_uv), _p(w_o), _p(u), _p(out), _p(ws), ws_bytes,
+                                    T, n_h, d_c, d_v, d_model, _DT[dt], _stream(stream)))
+    return u, out
+
+
+def gather_paged(cache: DeviceCache, block_table, seq_lens, max_tokens, stream=None):
+    """mla_gather_paged: [B, max_tokens, row_bytes] uint8 (rows past seq_len untouched: zero)."""
+    B = block_table.shape[0]
+    row_bytes = L.load().mla_cache_bytes(ctypes.byref(cache.desc())) // cache.num_blocks // L.BLOCK_SIZE
+    out = torch.zeros((B, max_tokens, row_bytes), dtype=torch.uint8, device=cache.pool.device)
+    desc = cache.desc()
+    L.check(L.load().mla_gather_paged(ctypes.byref(desc), _p(block_table), block_table.stride(0),
+                                      _p(seq_lens), B, max_tokens, _p(out), _stream(stream)))
+    return out

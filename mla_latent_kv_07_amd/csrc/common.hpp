@@ -1,0 +1,76 @@
+// Internal declarations shared by the host layer and the kernels of libmla.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+constexpr int kBlock = MLA_BLOCK_SIZE;   // tokens per paged block == decode tile
+constexpr int kRowsPerChunk = 128;       // query rows handled by one workgroup
+
+// Everything a decode kernel needs, resolved and validated on the host.
+struct DecodeArgs {
+    const void *q_lat;
+    const void *q_rope;
+    const void *pool;
+    const float *block_scales;
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    const int32_t *plan;       // device plan (header, items, split_off, seq_flags)
+    float *o_part;             // [num_partials][rows][d_c]
+    float *lse_part;           // [num_partials][rows]
+    void *o_lat;
+    float *lse;
+    int64_t block_bytes;
+    int64_t num_pool_blocks;   // block ids are clamped to [0, num_pool_blocks)
+    int32_t bt_stride, B, q_len, n_h, d_c, d_r;
+    int32_t rows;              // q_len * n_h
+    int32_t num_items, row_chunks;
+    float scale_log2;          // scale * log2(e)
+    mla_dtype_t q_dtype, kv_dtype;
+};
+
+// Plan layout offsets (int32 entries).
+__host__ __device__ inline int64_t plan_items_off() { return 4; }
+__host__ __device__ inline int64_t plan_split_off(int32_t num_items) { return 4 + 4 * (int64_t)num_items; }
+__host__ __device__ inline int64_t plan_flags_off(int32_t num_items, int32_t B) {
+    return plan_split_off(num_items) + B + 1;
+}
+
+hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_bf16_mfma(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_fp8_mfma(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_combine(const float *o_part, const float *lse_part, const int32_t *split_off,
+                          const int32_t *seq_flags, int32_t B, int32_t rows, int32_t d_c,
+                          void *o_lat, mla_dtype_t out_dt, float *lse, hipStream_t s);
+hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int32_t c_bytes,
+                         int32_t r_bytes, bool split_rows, const int32_t *bt, int32_t bt_stride,
+                         const int32_t *seq_lens, int32_t B, int32_t max_tokens, uint8_t *out,
+                         hipStream_t s);
+hipError_t launch_absorb_q(const void *q_nope, int64_t ld_q, const void *w_uk, void *q_lat,
+                           int32_t T, int32_t n_h, int32_t d_nope, int32_t d_c, mla_dtype_t dt,
+                           hipStream_t s);
+int64_t absorb_out_workspace(int32_t T, int32_t n_h, int32_t d_v, int32_t d_model,
+                             mla_dtype_t dt);
+hipError_t launch_absorb_out(const void *o_lat, const void *w_uv, const void *w_o, void *u_ws,
+                             void *out, float *ws, int32_t T, int32_t n_h, int32_t d_c,
+                             int32_t d_v, int32_t d_model, mla_dtype_t dt, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace mla

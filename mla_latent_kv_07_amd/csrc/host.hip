@@ -1,0 +1,312 @@
+// C ABI of libmla: host-side validation, the split-KV planner and launch
+// dispatch.  Argument checks and the planner make no HIP call, so they run
+// (and are tested) on machines without a GPU.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "common.hpp"
+
+using namespace mla;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status_t fail(mla_status_t st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+mla_status_t ok() {
+    g_err[0] = '\0';
+    return MLA_OK;
+}
+
+mla_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elem_bytes(mla_dtype_t dt) {
+    switch (dt) {
+    case MLA_DT_F32: return 4;
+    case MLA_DT_BF16: return 2;
+    case MLA_DT_FP8_E4M3: return 1;
+    }
+    return 0;
+}
+
+int64_t block_bytes_of(mla_dtype_t kv, int32_t d_c, int32_t d_r) {
+    switch (kv) {
+    case MLA_DT_F32: return (int64_t)kBlock * (d_c + d_r) * 4;
+    case MLA_DT_BF16: return (int64_t)kBlock * (d_c + d_r) * 2;
+    case MLA_DT_FP8_E4M3: return (int64_t)kBlock * d_c + (int64_t)kBlock * d_r * 2;
+    }
+    return -1;
+}
+
+bool is_fast_shape(mla_dtype_t kv, int32_t d_c, int32_t d_r) {
+    return (kv == MLA_DT_BF16 || kv == MLA_DT_FP8_E4M3) && d_c == 512 && d_r == 64;
+}
+
+mla_status_t check_cache(const mla_cache_desc_t *c) {
+    if (!c) return fail(MLA_ERR_INVALID_ARG, "cache descriptor is NULL");
+    if (!c->base) return fail(MLA_ERR_INVALID_ARG, "cache base is NULL");
+    if (c->num_blocks < 1) return fail(MLA_ERR_INVALID_ARG, "cache is empty (num_blocks=%lld)", (long long)c->num_blocks);
+    if (c->block_size != kBlock)
+        return fail(MLA_ERR_UNSUPPORTED, "block_size %d unsupported (only %d)", c->block_size, kBlock);
+    if (c->kv_dtype != MLA_DT_F32 && c->kv_dtype != MLA_DT_BF16 && c->kv_dtype != MLA_DT_FP8_E4M3)
+        return fail(MLA_ERR_UNSUPPORTED, "kv dtype %d unsupported", (int)c->kv_dtype);
+    if (c->d_c < 4 || c->d_c > 1024 || c->d_c % 4 || c->d_r < 0 || c->d_r > 256 || c->d_r % 4)
+        return fail(MLA_ERR_UNSUPPORTED, "cache dims d_c=%d d_r=%d unsupported (d_c in [4,1024], d_r in [0,256], multiples of 4)",
+                    c->d_c, c->d_r);
+    if (c->kv_dtype == MLA_DT_FP8_E4M3 && !c->block_scales)
+        return fail(MLA_ERR_INVALID_ARG, "fp8 cache needs block_scales");
+    if (!aligned(c->base, 16)) return fail(MLA_ERR_ALIGN, "cache base not 16-byte aligned");
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_last_error(void) { return g_err; }
+
+const char *mla_version(void) { return "mla-mi355x 0.1.0 (gfx950)"; }
+
+int64_t mla_cache_bytes(const mla_cache_desc_t *cache) {
+    if (!cache || cache->block_size != kBlock || cache->num_blocks < 0) return 0;
+    int64_t bb = block_bytes_of(cache->kv_dtype, cache->d_c, cache->d_r);
+    return bb < 0 ? 0 : bb * cache->num_blocks;
+}
+
+mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_len,
+                             int32_t n_h, int32_t d_c, int32_t d_r, mla_dtype_t kv_dtype,
+                             int32_t num_cus, int32_t *plan_host, int64_t plan_capacity,
+                             mla_plan_t *info) {
+    if (!info) return fail(MLA_ERR_INVALID_ARG, "info is NULL");
+    if (!seq_lens_host) return fail(MLA_ERR_INVALID_ARG, "seq_lens_host is NULL");
+    if (B < 1 || q_len < 1 || n_h < 1 || d_c < 1 || d_r < 0)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d q_len=%d n_h=%d d_c=%d d_r=%d", B, q_len, n_h, d_c, d_r);
+    if (num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "num_cus=%d", num_cus);
+    if (kv_dtype != MLA_DT_F32 && kv_dtype != MLA_DT_BF16 && kv_dtype != MLA_DT_FP8_E4M3)
+        return fail(MLA_ERR_UNSUPPORTED, "kv dtype %d unsupported", (int)kv_dtype);
+    int64_t rows = (int64_t)q_len * n_h;
+    if (rows > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "q_len*n_h too large");
+    int32_t row_chunks = (int32_t)((rows + kRowsPerChunk - 1) / kRowsPerChunk);
+
+    int64_t total_blocks = 0;
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %d < 0", b, seq_lens_host[b]);
+        total_blocks += (seq_lens_host[b] + kBlock - 1) / kBlock;
+    }
+    // Per-item share: spread all (block, row-chunk) work over the compute units.
+    int64_t share = std::max<int64_t>(1, (total_blocks * row_chunks + num_cus - 1) / num_cus);
+
+    int64_t num_items = 0, num_partials = 0;
+    int32_t max_splits = 0;
+    bool any_empty = false;
+    for (int b = 0; b < B; ++b) {
+        int64_t nb = (seq_lens_host[b] + kBlock - 1) / kBlock;
+        if (nb == 0) { any_empty = true; continue; }
+        int64_t splits = (nb + share - 1) / share;
+        num_items += splits;
+        if (splits > 1) num_partials += splits;
+        max_splits = std::max<int32_t>(max_splits, (int32_t)splits);
+    }
+    if (num_items > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "too many work items");
+
+    info->B = B; info->q_len = q_len; info->n_h = n_h; info->d_c = d_c;
+    info->num_items = (int32_t)num_items;
+    info->row_chunks = row_chunks;
+    info->num_partials = (int32_t)num_partials;
+    info->needs_combine = (num_partials > 0 || any_empty) ? 1 : 0;
+    info->max_splits = max_splits;
+    info->blocks_per_item = (int32_t)share;
+    info->plan_ints = 4 + 4 * num_items + 2 * (int64_t)B + 1;
+    int64_t o_bytes = num_partials * rows * d_c * 4;
+    int64_t o_bytes_al = (o_bytes + 255) / 256 * 256;
+    info->workspace_bytes = num_partials ? o_bytes_al + num_partials * rows * 4 : 0;
+
+    if (!plan_host) return ok();
+    if (plan_capacity < info->plan_ints)
+        return fail(MLA_ERR_INVALID_ARG, "plan capacity %lld < %lld", (long long)plan_capacity, (long long)info->plan_ints);
+
+    int32_t *items = plan_host + plan_items_off();
+    int32_t *split_off = plan_host + plan_split_off((int32_t)num_items);
+    int32_t *flags = plan_host + plan_flags_off((int32_t)num_items, B);
+    plan_host[0] = (int32_t)num_items;
+    plan_host[1] = B;
+    plan_host[2] = row_chunks;
+    plan_host[3] = (int32_t)num_partials;
+    int64_t it = 0, slot = 0;
+    for (int b = 0; b < B; ++b) {
+        int64_t nb = (seq_lens_host[b] + kBlock - 1) / kBlock;
+        split_off[b] = (int32_t)slot;
+        if (nb == 0) { flags[b] = 0; continue; }
+        int64_t splits = (nb + share - 1) / share;
+        flags[b] = splits == 1 ? 1 : 0;
+        for (int64_t k = 0; k < splits; ++k) {
+            items[4 * it + 0] = b;
+            items[4 * it + 1] = (int32_t)(k * nb / splits);
+            items[4 * it + 2] = (int32_t)((k + 1) * nb / splits);
+            items[4 * it + 3] = splits == 1 ? -1 : (int32_t)(slot++);
+            ++it;
+        }
+    }
+    split_off[B] = (int32_t)slot;
+    return ok();
+}
+
+mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
+                        const mla_cache_desc_t *cache, const int32_t *block_table,
+                        int32_t bt_stride, const int32_t *seq_lens, int32_t B, int32_t q_len,
+                        int32_t n_h, float scale, const mla_plan_t *plan,
+                        const int32_t *plan_dev, void *workspace, int64_t workspace_bytes,
+                        void *o_lat, float *lse, mla_stream_t stream) {
+    mla_status_t st = check_cache(cache);
+    if (st != MLA_OK) return st;
+    if (!q_lat || !o_lat || !lse || !block_table || !seq_lens)
+        return fail(MLA_ERR_INVALID_ARG, "NULL q_lat/o_lat/lse/block_table/seq_lens");
+    if (cache->d_r > 0 && !q_rope) return fail(MLA_ERR_INVALID_ARG, "q_rope is NULL");
+    if (!plan || !plan_dev) return fail(MLA_ERR_INVALID_ARG, "missing decode plan");
+    if (B < 1 || q_len < 1 || n_h < 1 || bt_stride < 1)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d q_len=%d n_h=%d bt_stride=%d", B, q_len, n_h, bt_stride);
+    if (plan->B != B || plan->q_len != q_len || plan->n_h != n_h || plan->d_c != cache->d_c)
+        return fail(MLA_ERR_INVALID_ARG, "plan was built for other sizes");
+    if (q_dtype != MLA_DT_F32 && q_dtype != MLA_DT_BF16)
+        return fail(MLA_ERR_UNSUPPORTED, "q dtype %d unsupported", (int)q_dtype);
+    if (!aligned(q_lat, 16) || !aligned(o_lat, 16) || (q_rope && !aligned(q_rope, 16)) || !aligned(lse, 4))
+        return fail(MLA_ERR_ALIGN, "q_lat/q_rope/o_lat must be 16-byte aligned");
+    if (workspace_bytes < plan->workspace_bytes)
+        return fail(MLA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)workspace_bytes,
+                    (long long)plan->workspace_bytes);
+    if (plan->workspace_bytes > 0 && (!workspace || !aligned(workspace, 256)))
+        return fail(MLA_ERR_ALIGN, "workspace NULL or not 256-byte aligned");
+    if (!(scale > 0.0f) || scale != scale) return fail(MLA_ERR_INVALID_ARG, "scale must be positive");
+
+    DecodeArgs a{};
+    a.q_lat = q_lat; a.q_rope = q_rope; a.pool = cache->base; a.block_scales = cache->block_scales;
+    a.block_table = block_table; a.seq_lens = seq_lens; a.plan = plan_dev;
+    int64_t rows = (int64_t)q_len * n_h;
+    if (plan->num_partials > 0) {
+        int64_t o_bytes = (int64_t)plan->num_partials * rows * cache->d_c * 4;
+        a.o_part = (float *)workspace;
+        a.lse_part = (float *)((char *)workspace + (o_bytes + 255) / 256 * 256);
+    }
+    a.o_lat = o_lat; a.lse = lse;
+    a.block_bytes = block_bytes_of(cache->kv_dtype, cache->d_c, cache->d_r);
+    a.num_pool_blocks = cache->num_blocks;
+    a.bt_stride = bt_stride; a.B = B; a.q_len = q_len; a.n_h = n_h;
+    a.d_c = cache->d_c; a.d_r = cache->d_r; a.rows = (int32_t)rows;
+    a.num_items = plan->num_items; a.row_chunks = plan->row_chunks;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.q_dtype = q_dtype; a.kv_dtype = cache->kv_dtype;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (plan->num_items > 0) {
+        if (is_fast_shape(cache->kv_dtype, cache->d_c, cache->d_r) && q_dtype == MLA_DT_BF16) {
+            e = cache->kv_dtype == MLA_DT_BF16 ? launch_decode_bf16_mfma(a, s)
+                                               : launch_decode_fp8_mfma(a, s);
+        } else {
+            e = launch_decode_generic(a, s);
+        }
+        if (e != hipSuccess) return hip_status(e, "decode launch");
+    }
+    if (plan->needs_combine) {
+        const int32_t *split_off = plan_dev + plan_split_off(plan->num_items);
+        const int32_t *flags = plan_dev + plan_flags_off(plan->num_items, B);
+        e = launch_combine(a.o_part, a.lse_part, split_off, flags, B, (int32_t)rows, cache->d_c,
+                           o_lat, q_dtype, lse, s);
+        if (e != hipSuccess) return hip_status(e, "combine launch");
+    }
+    return ok();
+}
+
+mla_status_t mla_combine_lse(const float *o_part, const float *lse_part,
+                             const int32_t *split_off, const int32_t *seq_flags, int32_t B,
+                             int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dtype,
+                             float *lse, mla_stream_t stream) {
+    if (!split_off || !o_lat || !lse) return fail(MLA_ERR_INVALID_ARG, "NULL split_off/o_lat/lse");
+    if (B < 1 || rows < 1 || d_c < 1 || d_c > 4096)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d rows=%d d_c=%d", B, rows, d_c);
+    if (out_dtype != MLA_DT_F32 && out_dtype != MLA_DT_BF16)
+        return fail(MLA_ERR_UNSUPPORTED, "out dtype %d unsupported", (int)out_dtype);
+    return hip_status(launch_combine(o_part, lse_part, split_off, seq_flags, B, rows, d_c, o_lat,
+                                     out_dtype, lse, (hipStream_t)stream),
+                      "combine launch");
+}
+
+mla_status_t mla_absorb_q(const void *q_nope, int64_t ld_q, const void *w_uk, void *q_lat,
+                          int32_t T, int32_t n_h, int32_t d_nope, int32_t d_c,
+                          mla_dtype_t dt, mla_stream_t stream) {
+    if (!q_nope || !w_uk || !q_lat) return fail(MLA_ERR_INVALID_ARG, "NULL q_nope/w_uk/q_lat");
+    if (T < 1 || n_h < 1 || d_nope < 1 || d_c < 1 || ld_q < (int64_t)n_h * d_nope)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes T=%d n_h=%d d_nope=%d d_c=%d ld_q=%lld", T, n_h,
+                    d_nope, d_c, (long long)ld_q);
+    if (dt != MLA_DT_F32 && dt != MLA_DT_BF16) return fail(MLA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+    if (!aligned(q_nope, 16) || !aligned(w_uk, 16) || !aligned(q_lat, 16) || (ld_q * elem_bytes(dt)) % 16 ||
+        (d_nope * elem_bytes(dt)) % 16 || (d_c * elem_bytes(dt)) % 16)
+        return fail(MLA_ERR_ALIGN, "absorb_q operands and rows must be 16-byte aligned");
+    return hip_status(launch_absorb_q(q_nope, ld_q, w_uk, q_lat, T, n_h, d_nope, d_c, dt,
+                                      (hipStream_t)stream),
+                      "absorb_q launch");
+}
+
+int64_t mla_absorb_out_workspace(int32_t T, int32_t n_h, int32_t d_v, int32_t d_model,
+                                 mla_dtype_t dt) {
+    if (T < 1 || n_h < 1 || d_v < 1 || d_model < 1) return 0;
+    return absorb_out_workspace(T, n_h, d_v, d_model, dt);
+}
+
+mla_status_t mla_absorb_out(const void *o_lat, const void *w_uv, const void *w_o, void *u_ws,
+                            void *out, void *f32_ws, int64_t f32_ws_bytes, int32_t T,
+                            int32_t n_h, int32_t d_c, int32_t d_v, int32_t d_model,
+                            mla_dtype_t dt, mla_stream_t stream) {
+    if (!o_lat || !w_uv || !w_o || !u_ws || !out)
+        return fail(MLA_ERR_INVALID_ARG, "NULL o_lat/w_uv/w_o/u_ws/out");
+    if (T < 1 || n_h < 1 || d_c < 1 || d_v < 1 || d_model < 1)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes T=%d n_h=%d d_c=%d d_v=%d d_model=%d", T, n_h, d_c, d_v, d_model);
+    if (dt != MLA_DT_F32 && dt != MLA_DT_BF16) return fail(MLA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+    int64_t need = absorb_out_workspace(T, n_h, d_v, d_model, dt);
+    if (f32_ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "absorb_out workspace %lld < %lld", (long long)f32_ws_bytes, (long long)need);
+    if (need > 0 && (!f32_ws || !aligned(f32_ws, 256))) return fail(MLA_ERR_ALIGN, "absorb_out workspace NULL or unaligned");
+    int eb = elem_bytes(dt);
+    if (!aligned(o_lat, 16) || !aligned(w_uv, 16) || !aligned(w_o, 16) || !aligned(u_ws, 16) || !aligned(out, 16) ||
+        (d_c * eb) % 16 || (d_v * eb) % 16 || (d_model * eb) % 16)
+        return fail(MLA_ERR_ALIGN, "absorb_out operands and rows must be 16-byte aligned");
+    return hip_status(launch_absorb_out(o_lat, w_uv, w_o, u_ws, out, (float *)f32_ws, T, n_h, d_c,
+                                        d_v, d_model, dt, (hipStream_t)stream),
+                      "absorb_out launch");
+}
+
+mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *block_table,
+                              int32_t bt_stride, const int32_t *seq_lens, int32_t B,
+                              int32_t max_tokens, void *out, mla_stream_t stream) {
+    mla_status_t st = check_cache(cache);
+    if (st != MLA_OK) return st;
+    if (!block_table || !seq_lens || !out) return fail(MLA_ERR_INVALID_ARG, "NULL block_table/seq_lens/out");
+    if (B < 1 || max_tokens < 1 || bt_stride < 1)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d max_tokens=%d bt_stride=%d", B, max_tokens, bt_stride);
+    if (!aligned(out, 16)) return fail(MLA_ERR_ALIGN, "out not 16-byte aligned");
+    int eb = elem_bytes(cache->kv_dtype);
+    bool split = cache->kv_dtype == MLA_DT_FP8_E4M3;
+    int32_t c_bytes = split ? cache->d_c : (cache->d_c + cache->d_r) * eb;
+    int32_t r_bytes = split ? cache->d_r * 2 : 0;
+    return hip_status(launch_gather((const uint8_t *)cache->base,
+                                    block_bytes_of(cache->kv_dtype, cache->d_c, cache->d_r),
+                                    c_bytes, r_bytes, split, block_table, bt_stride, seq_lens, B,
+                                    max_tokens, (uint8_t *)out, (hipStream_t)stream),
+                      "gather launch");
+}
+
+}  // extern "C"

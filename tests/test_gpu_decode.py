@@ -1,0 +1,151 @@
+"""GPU parity of mla_decode / mla_combine_lse / mla_gather_paged against the
+CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_latent_kv_07_amd import api
+from mla_latent_kv_07_amd import inputs as I
+
+from parity import DEV, FMT, TOL, compare_decode, oracle_decode, run_decode, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def small(kv="bf16", seq=(1, 100, 333), q_len=1, n_h=128, d_c=512, d_r=64, seed=7, heavy=0.0):
+    return I.make_decode_inputs(I.Workload(
+        f"small_{kv}_q{q_len}_h{n_h}", seed, kv, "f32" if kv == "f32" else "bf16", B=len(seq),
+        q_len=q_len, n_h=n_h, d_c=d_c, d_r=d_r, seq_lens=tuple(seq), heavy_frac=heavy))
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8_e4m3"])
+def test_gather_bit_exact(kv):
+    d = small(kv, seq=(3, 64, 129, 0), d_c=512 if kv != "f32" else 64, d_r=64 if kv != "f32" else 16, n_h=8)
+    cache, bt, sl, _, _ = to_device(d)
+    got = api.gather_paged(cache, bt, sl, 130).cpu().numpy()
+    ref = O.gather(d.cache.pool, FMT[kv], d.wl.d_c, d.wl.d_r, d.cache.block_table, d.cache.seq_lens, 130)
+    assert np.array_equal(got, ref)
+
+
+def test_decode_bf16_mfma_ragged():
+    # several tiles and ragged tails; one split per sequence (one "CU")
+    d = small("bf16", seq=(1, 100, 333, 64, 65))
+    o, lse, dec = run_decode(d, cus=1)
+    assert dec.info.num_partials == 0
+    compare_decode(d, o, lse)
+
+
+def test_decode_bf16_mfma_splits_and_combine():
+    # a tiny CU count forces several splits per sequence and the LSE combine
+    d = small("bf16", seq=(1, 700, 1500, 64, 0, 129), seed=8)
+    o, lse, dec = run_decode(d, cus=8)
+    assert dec.info.num_partials > 0 and dec.info.max_splits > 1
+    compare_decode(d, o, lse)
+
+
+def test_decode_bf16_heavy_rows_and_nan_tails():
+    # 5 % of rows scaled x8 (large softmax range, exercises the running-max
+    # raise); NaN tails and spare blocks must not leak
+    d = small("bf16", seq=(2000, 37, 640), seed=9, heavy=0.05)
+    o, lse, _ = run_decode(d, cus=16)
+    compare_decode(d, o, lse)
+
+
+def test_decode_bf16_spec_pair_causal():
+    # q_len = 2: 256 rows per sequence -> two row chunks per work item
+    d = small("bf16", seq=(2, 3, 64, 65, 500), q_len=2, seed=10)
+    o, lse, dec = run_decode(d, cus=16)
+    assert dec.info.row_chunks == 2
+    compare_decode(d, o, lse)
+
+
+def test_decode_bf16_few_heads():
+    # n_h = 16 (e.g. one tensor-parallel shard): rows < one chunk, partly idle waves
+    d = small("bf16", seq=(77, 300), n_h=16, seed=11)
+    o, lse, _ = run_decode(d)
+    compare_decode(d, o, lse)
+
+
+def test_decode_query_longer_than_sequence():
+    d = small("bf16", seq=(1, 0, 2), q_len=2, seed=12)
+    o, lse, _ = run_decode(d)
+    compare_decode(d, o, lse)
+    lse_c = lse.cpu()
+    assert torch.isinf(lse_c[0]).all() and torch.isinf(lse_c[2:4]).all()
+
+
+def test_decode_generic_paths():
+    # f32 cache (tiny dims) and bf16 with f32 queries go through the generic kernel
+    d = small("f32", seq=(1, 70, 200), n_h=8, d_c=64, d_r=16, seed=13)
+    o, lse, _ = run_decode(d, cus=4)
+    compare_decode(d, o, lse)
+
+
+def test_decode_fp8_cache():
+    d = small("fp8_e4m3", seq=(2, 150, 300), q_len=2, seed=14)
+    o, lse, _ = run_decode(d, cus=8)
+    compare_decode(d, o, lse)
+
+
+def test_block_table_permutation_gives_identical_bits():
+    d = small("bf16", seq=(190, 64, 7), seed=15)
+    o1, l1, _ = run_decode(d, cus=8)
+    # same logical rows through another pool permutation
+    g = torch.Generator()
+    g.manual_seed(99)
+    rows = []
+    for b, S in enumerate(d.cache.seq_lens.tolist()):
+        for p in range(S):
+            blk = int(d.cache.block_table[b, p // 64])
+            rows.append(d.cache.pool[blk].view(torch.bfloat16).view(64, -1)[p % 64].float())
+    rows = torch.stack(rows)
+    cache2 = I.page_cache(d.wl, g, d.cache.seq_lens, rows)
+    assert not torch.equal(cache2.block_table, d.cache.block_table)
+    d2 = I.DecodeInputs(d.wl, cache2, d.q_lat, d.q_rope, d.scale)
+    o2, l2, _ = run_decode(d2, cus=8)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_is_deterministic():
+    d = small("bf16", seq=(900, 31), seed=16)
+    cache, bt, sl, ql, qr = to_device(d)
+    dec = api.Decoder(d.cache.seq_lens, 1, 128, 512, 64, "bf16", DEV, cus=8)
+    o1, l1 = dec(ql, qr, cache, bt, sl, d.scale)
+    o2, l2 = dec(ql, qr, cache, bt, sl, d.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_combine_lse_standalone():
+    rng = np.random.default_rng(3)
+    P, rows, d_c = 7, 16, 512
+    o_part = rng.normal(size=(P, rows, d_c))
+    lse_part = rng.normal(size=(P, rows)) * 3
+    lse_part[2, :5] = -np.inf
+    lse_part[3:5, 7] = -np.inf
+    split_off = np.array([0, 3, 3, 7], np.int32)      # sequence 1 has no slots
+    seq_flags = np.array([0, 0, 0], np.int32)
+    o32 = torch.from_numpy(o_part).float()
+    l32 = torch.from_numpy(lse_part).float()
+    o, l = api.combine_lse(o32.to(DEV), l32.to(DEV), torch.from_numpy(split_off).to(DEV), 3, rows,
+                           out_dtype=torch.float32, seq_flags=torch.from_numpy(seq_flags).to(DEV))
+    o, l = o.cpu().numpy().reshape(3, rows, d_c), l.cpu().numpy().reshape(3, rows)
+    for b in range(3):
+        k0, k1 = split_off[b], split_off[b + 1]
+        if k1 == k0:
+            assert not o[b].any() and np.all(np.isneginf(l[b]))
+            continue
+        ro, rl = O.combine(o32.double().numpy()[k0:k1], l32.double().numpy()[k0:k1])
+        assert np.abs(o[b] - ro).max() < 1e-5 and np.abs(l[b] - rl).max() < 1e-5
+
+
+def test_decode_measured_batch_full_size_sampled():
+    """The measured batch (32 x 4096, bf16, 128 heads), in the launch
+    configuration the benchmark times, checked on sampled rows."""
+    d = I.make_decode_inputs(I.C2)
+    o, lse, dec = run_decode(d)
+    assert dec.info.num_items == 256
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(32 * 128, size=96, replace=False))
+    compare_decode(d, o, lse, rows=rows)

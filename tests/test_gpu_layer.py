@@ -1,0 +1,89 @@
+"""GPU parity of the absorption GEMMs and of the whole absorbed layer
+(mla_absorb_q -> mla_decode -> mla_absorb_out) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_latent_kv_07_amd import api
+from mla_latent_kv_07_amd import inputs as I
+
+from parity import DEV, TOL, compare_decode, row_rel_err, run_decode, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dt,T,n_h,d_nope,d_c", [
+    ("f32", 3, 8, 32, 64),
+    ("bf16", 5, 16, 128, 512),
+    ("bf16", 130, 128, 128, 512),
+])
+def test_absorb_q(dt, T, n_h, d_nope, d_c):
+    g = torch.Generator()
+    g.manual_seed(T * 7 + n_h)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q = torch.randn(T, n_h, d_nope, generator=g).to(tdt)
+    w = (torch.randn(n_h, d_c, d_nope, generator=g) / d_c ** 0.5).to(tdt)
+    got = api.absorb_q(q.to(DEV), w.to(DEV)).float().cpu().numpy()
+    ref = O.absorb_q(q.double().numpy(), w.double().numpy())
+    err = row_rel_err(got, ref)
+    say(f"  absorb_q {dt} T={T}: {err:.3e}")
+    assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt,T,n_h,d_c,d_v,d_model", [
+    ("f32", 3, 8, 64, 32, 256),
+    ("bf16", 5, 16, 512, 128, 640),
+    ("bf16", 130, 128, 512, 128, 5120),
+])
+def test_absorb_out(dt, T, n_h, d_c, d_v, d_model):
+    g = torch.Generator()
+    g.manual_seed(T * 11 + d_model)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    o = torch.randn(T, n_h, d_c, generator=g).to(tdt)
+    wv = (torch.randn(n_h, d_c, d_v, generator=g) / d_c ** 0.5).to(tdt)
+    wo = (torch.randn(n_h * d_v, d_model, generator=g) / (n_h * d_v) ** 0.5).to(tdt)
+    u, out = api.absorb_out(o.to(DEV), wv.to(DEV), wo.to(DEV))
+    ref_u, ref_out = O.absorb_out(o.double().numpy(), wv.double().numpy(), wo.double().numpy())
+    eu = row_rel_err(u.float().cpu().numpy(), ref_u)
+    # `out` takes u as the device rounded it (one more bf16 rounding than
+    # the fp64 chain): compare against the oracle applied to the device's u
+    u_dev = u.float().cpu().double().numpy().reshape(T, -1)
+    ref_out_u = u_dev @ wo.double().numpy()
+    eo = row_rel_err(out.float().cpu().numpy(), ref_out_u)
+    eo_chain = row_rel_err(out.float().cpu().numpy(), ref_out)
+    say(f"  absorb_out {dt} T={T}: u {eu:.3e} out {eo:.3e} chain {eo_chain:.3e}")
+    assert eu <= TOL[dt] and eo <= TOL[dt] and eo_chain <= TOL[dt]
+
+
+def test_tiny_fp32_layer_matches_unabsorbed_mha():
+    """The tiny fp32 layer: cache and query rows built from hidden states by
+    the oracle's projections and RoPE (cache append and query production are
+    not on the GPU path); the GPU runs absorb_q -> decode -> absorb_out."""
+    from test_oracle_layer import build_tiny_layer
+    wl, L, w, c, kr, q_nope, q_rope = build_tiny_layer()
+    S = c.shape[0]
+    rows = torch.from_numpy(np.concatenate([c, kr], 1)).to(torch.float32)
+    cache = I.page_cache(wl, L["generator"], L["seq_lens"], rows)
+    qn = torch.from_numpy(q_nope).float()
+    qr = torch.from_numpy(q_rope).float()
+    wuk = torch.from_numpy(w["w_uk"]).float()
+    wuv = torch.from_numpy(w["w_uv"]).float()
+    wo = torch.from_numpy(w["w_o"]).float()
+    q_lat = api.absorb_q(qn.to(DEV), wuk.to(DEV))
+    dcache = api.DeviceCache.from_host(cache, DEV)
+    dec = api.Decoder(cache.seq_lens, 1, wl.n_h, wl.d_c, wl.d_r, "f32", DEV)
+    o_lat, lse = dec(q_lat, qr.to(DEV), dcache, cache.block_table.to(DEV), cache.seq_lens.to(DEV), wl.scale)
+    _, out = api.absorb_out(o_lat, wuv.to(DEV), wo.to(DEV))
+    torch.cuda.synchronize()
+    # reference: brute-force MHA with reconstructed K/V on the fp32-stored
+    # rows and fp32-stored queries/weights
+    o_ref, u_ref, out_ref, lse_ref = O.unabsorbed_mha(
+        rows[:, :wl.d_c].double().numpy(), rows[:, wl.d_c:].double().numpy(),
+        qn.double().numpy(), qr.double().numpy(), wuk.double().numpy(), wuv.double().numpy(),
+        wo.double().numpy(), wl.scale, [S - 1])
+    e_o = row_rel_err(o_lat.cpu().numpy(), o_ref)
+    e_out = row_rel_err(out.cpu().numpy(), out_ref)
+    say(f"  tiny fp32 layer: o_lat {e_o:.3e}, out {e_out:.3e}")
+    assert e_o <= 1e-5 and e_out <= 1e-5
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-5 * max(1.0, np.abs(lse_ref).max())

@@ -1,0 +1,189 @@
+"""libmla host side, on the CPU: the library loads, exports every symbol the
+header declares, the split planner covers every block exactly once, and every
+argument error is reported before any HIP call."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+import torch
+
+from mla_latent_kv_07_amd import _lib as L
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "mla.h"
+
+
+def lib():
+    return L.load()
+
+
+def test_exports_every_declared_symbol():
+    text = HEADER.read_text()
+    declared = set(re.findall(r"^(?:[\w ]+\*?\s*\*?)\b(mla_\w+)\s*\(", text, flags=re.M))
+    assert {"mla_decode", "mla_decode_plan", "mla_combine_lse", "mla_absorb_q", "mla_absorb_out",
+            "mla_gather_paged", "mla_last_error", "mla_version", "mla_cache_bytes",
+            "mla_absorb_out_workspace"} <= declared
+    so = ctypes.CDLL(str(L.LIB_PATH))
+    for name in sorted(declared):
+        assert hasattr(so, name), name
+
+
+def plan(seq, q_len=1, n_h=128, d_c=512, d_r=64, kv=L.DT_BF16, cus=256):
+    sl = torch.tensor(seq, dtype=torch.int32)
+    info = L.Plan()
+    L.check(lib().mla_decode_plan(ctypes.c_void_p(sl.data_ptr()), len(seq), q_len, n_h, d_c, d_r,
+                                  kv, cus, None, 0, ctypes.byref(info)))
+    p = torch.empty(info.plan_ints, dtype=torch.int32)
+    L.check(lib().mla_decode_plan(ctypes.c_void_p(sl.data_ptr()), len(seq), q_len, n_h, d_c, d_r,
+                                  kv, cus, ctypes.c_void_p(p.data_ptr()), p.numel(), ctypes.byref(info)))
+    return info, p
+
+
+def parse(info, p):
+    n = info.num_items
+    items = p[4:4 + 4 * n].view(n, 4).tolist()
+    split_off = p[4 + 4 * n:4 + 4 * n + info.B + 1].tolist()
+    flags = p[4 + 4 * n + info.B + 1:].tolist()
+    return items, split_off, flags
+
+
+@pytest.mark.parametrize("seq,q_len,cus", [
+    ([4096] * 32, 1, 256),                       # the measured batch
+    ([1, 0, 65, 64, 4097, 300], 1, 256),
+    ([100000, 70000, 131072, 65536], 1, 256),
+    ([1024, 8192, 2, 5000] * 16, 2, 256),
+    ([1, 32768, 17, 0, 999], 1, 7),
+    ([0, 0], 1, 256),
+])
+def test_plan_covers_each_block_once(seq, q_len, cus):
+    info, p = plan(seq, q_len=q_len, cus=cus)
+    items, split_off, flags = parse(info, p)
+    assert p[0] == info.num_items and p[1] == len(seq) and p[2] == info.row_chunks
+    assert info.row_chunks == (q_len * 128 + 127) // 128
+    seen = {}
+    slots = set()
+    for b, lo, hi, slot in items:
+        assert 0 <= lo < hi <= (seq[b] + 63) // 64
+        assert hi - lo <= info.blocks_per_item
+        for blk in range(lo, hi):
+            assert (b, blk) not in seen
+            seen[(b, blk)] = slot
+        if slot >= 0:
+            assert split_off[b] <= slot < split_off[b + 1]
+            slots.add(slot)
+    for b, S in enumerate(seq):
+        nb = (S + 63) // 64
+        assert all((b, k) in seen for k in range(nb))
+        n_items = sum(1 for it in items if it[0] == b)
+        if nb == 0:
+            assert flags[b] == 0 and split_off[b + 1] == split_off[b]
+        elif n_items == 1:
+            assert flags[b] == 1 and split_off[b + 1] == split_off[b]
+        else:
+            assert flags[b] == 0 and split_off[b + 1] - split_off[b] == n_items
+    assert slots == set(range(info.num_partials))
+    assert info.needs_combine == int(info.num_partials > 0 or 0 in seq)
+    rows = q_len * 128
+    if info.num_partials:
+        assert info.workspace_bytes >= info.num_partials * rows * (512 + 1) * 4
+    else:
+        assert info.workspace_bytes == 0
+
+
+def test_plan_fills_the_gpu_for_the_measured_batch():
+    info, _ = plan([4096] * 32)
+    assert info.num_items == 256 and info.max_splits == 8 and info.blocks_per_item == 8
+
+
+def test_plan_errors():
+    sl = torch.tensor([10, -1], dtype=torch.int32)
+    info = L.Plan()
+    ptr = ctypes.c_void_p(sl.data_ptr())
+    assert lib().mla_decode_plan(ptr, 2, 1, 128, 512, 64, L.DT_BF16, 256, None, 0, ctypes.byref(info)) == L.MLA_ERR_INVALID_ARG
+    assert b"seq_lens" in lib().mla_last_error()
+    assert lib().mla_decode_plan(ptr, 0, 1, 128, 512, 64, L.DT_BF16, 256, None, 0, ctypes.byref(info)) == L.MLA_ERR_INVALID_ARG
+    assert lib().mla_decode_plan(ptr, 1, 1, 128, 512, 64, L.DT_BF16, 0, None, 0, ctypes.byref(info)) == L.MLA_ERR_INVALID_ARG
+    assert lib().mla_decode_plan(ptr, 1, 1, 128, 512, 64, 7, 256, None, 0, ctypes.byref(info)) == L.MLA_ERR_UNSUPPORTED
+    small = torch.empty(3, dtype=torch.int32)
+    assert lib().mla_decode_plan(ptr, 1, 1, 128, 512, 64, L.DT_BF16, 256,
+                                 ctypes.c_void_p(small.data_ptr()), 3, ctypes.byref(info)) == L.MLA_ERR_INVALID_ARG
+    assert lib().mla_decode_plan(None, 1, 1, 128, 512, 64, L.DT_BF16, 256, None, 0, ctypes.byref(info)) == L.MLA_ERR_INVALID_ARG
+
+
+# Fake, never-dereferenced device addresses: every case below must be rejected
+# by the host checks before the library touches the GPU.
+A = 1 << 20
+
+
+def _desc(**kw):
+    d = dict(base=A, block_scales=None, num_blocks=10, block_size=64, d_c=512, d_r=64, kv_dtype=L.DT_BF16)
+    d.update(kw)
+    return L.CacheDesc(d["base"], d["block_scales"], d["num_blocks"], d["block_size"], d["d_c"],
+                       d["d_r"], d["kv_dtype"])
+
+
+def _decode(desc=None, q=A, qr=A, qdt=L.DT_BF16, bt=A, stride=64, sl=A, B=2, q_len=1, n_h=128,
+            scale=0.07, plan_=None, plan_dev=A, ws=A, ws_bytes=1 << 30, o=A, lse=A):
+    if plan_ is None:
+        plan_, _ = plan([100, 200])
+    desc = desc or _desc()
+    return lib().mla_decode(q, qr, qdt, ctypes.byref(desc), bt, stride, sl, B, q_len, n_h, scale,
+                            ctypes.byref(plan_), plan_dev, ws, ws_bytes, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(desc=_desc(block_size=32)), L.MLA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(num_blocks=0)), L.MLA_ERR_INVALID_ARG),       # empty cache
+    (dict(desc=_desc(base=None)), L.MLA_ERR_INVALID_ARG),
+    (dict(desc=_desc(base=A + 8)), L.MLA_ERR_ALIGN),
+    (dict(desc=_desc(d_c=2048)), L.MLA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(d_r=6)), L.MLA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(kv_dtype=L.DT_FP8_E4M3)), L.MLA_ERR_INVALID_ARG),   # no block scales
+    (dict(q=None), L.MLA_ERR_INVALID_ARG),
+    (dict(qr=None), L.MLA_ERR_INVALID_ARG),
+    (dict(o=None), L.MLA_ERR_INVALID_ARG),
+    (dict(plan_dev=None), L.MLA_ERR_INVALID_ARG),                   # missing plan
+    (dict(B=3), L.MLA_ERR_INVALID_ARG),                             # plan mismatch
+    (dict(n_h=64), L.MLA_ERR_INVALID_ARG),
+    (dict(stride=0), L.MLA_ERR_INVALID_ARG),
+    (dict(qdt=L.DT_FP8_E4M3), L.MLA_ERR_UNSUPPORTED),
+    (dict(q=A + 4), L.MLA_ERR_ALIGN),
+    (dict(o=A + 2), L.MLA_ERR_ALIGN),
+    (dict(ws_bytes=16), L.MLA_ERR_WORKSPACE),
+    (dict(ws=None), L.MLA_ERR_ALIGN),
+    (dict(ws=A + 64), L.MLA_ERR_ALIGN),
+    (dict(scale=0.0), L.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), L.MLA_ERR_INVALID_ARG),
+])
+def test_decode_rejects_bad_arguments_before_launch(kw, status):
+    # plan for [100, 200] at 256 CUs: both sequences fit in one item each, so
+    # force partials with a tiny CU count for the workspace cases
+    if "ws_bytes" in kw or "ws" in kw:
+        kw["plan_"], _ = plan([100, 200], cus=4)
+    assert _decode(**kw) == status
+    assert lib().mla_last_error() != b""
+
+
+def test_other_entry_points_reject_bad_arguments():
+    l = lib()
+    assert l.mla_combine_lse(A, A, None, None, 2, 128, 512, A, L.DT_BF16, A, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_combine_lse(A, A, A, None, 0, 128, 512, A, L.DT_BF16, A, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_combine_lse(A, A, A, None, 2, 128, 512, A, L.DT_FP8_E4M3, A, None) == L.MLA_ERR_UNSUPPORTED
+    assert l.mla_absorb_q(None, 128 * 128, A, A, 4, 128, 128, 512, L.DT_BF16, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_absorb_q(A, 100, A, A, 4, 128, 128, 512, L.DT_BF16, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_absorb_q(A + 2, 128 * 128, A, A, 4, 128, 128, 512, L.DT_BF16, None) == L.MLA_ERR_ALIGN
+    assert l.mla_absorb_q(A, 128 * 128, A, A, 4, 128, 128, 512, L.DT_FP8_E4M3, None) == L.MLA_ERR_UNSUPPORTED
+    assert l.mla_absorb_out(A, A, None, A, A, A, 1 << 30, 4, 128, 512, 128, 5120, L.DT_BF16, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_absorb_out(A, A, A, A, A, A, 1 << 30, 0, 128, 512, 128, 5120, L.DT_BF16, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_absorb_out(A, A, A, A, A + 4, A, 1 << 30, 4, 128, 512, 128, 5120, L.DT_BF16, None) == L.MLA_ERR_ALIGN
+    d = _desc()
+    assert l.mla_gather_paged(ctypes.byref(d), A, 64, A, 0, 10, A, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_gather_paged(ctypes.byref(_desc(block_size=16)), A, 64, A, 2, 10, A, None) == L.MLA_ERR_UNSUPPORTED
+    assert l.mla_gather_paged(ctypes.byref(d), A, 64, A, 2, 10, A + 1, None) == L.MLA_ERR_ALIGN
+
+
+def test_cache_bytes():
+    assert lib().mla_cache_bytes(ctypes.byref(_desc(num_blocks=2048))) == 2048 * 73728
+    assert lib().mla_cache_bytes(ctypes.byref(_desc(num_blocks=3, kv_dtype=L.DT_FP8_E4M3))) == 3 * 40960
+    assert lib().mla_cache_bytes(ctypes.byref(_desc(num_blocks=1, kv_dtype=L.DT_F32, d_c=64, d_r=16))) == 64 * 80 * 4
+    assert lib().mla_cache_bytes(ctypes.byref(_desc(block_size=32))) == 0
