@@ -165,6 +165,28 @@ mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dty
                         void *o_lat, float *lse, mla_stream_t stream);
 
 /*
+ * mla_decode_partial / mla_decode_finish — mla_decode in its two launches.
+ * mla_decode_partial runs the split decode kernel alone: sequences with one
+ * split get their final o_lat / lse, the others leave normalised partials
+ * and their lse in the workspace.  mla_decode_finish then runs the LSE
+ * combine for the plan (nothing if plan->needs_combine is 0), writing the
+ * remaining rows of o_lat (out_dtype = the query dtype) and lse.  Calling
+ * both, in order, on one stream is exactly mla_decode; they exist so that a
+ * caller can place other work or timing events between the two launches.
+ * Arguments and errors are those of mla_decode.
+ */
+mla_status_t mla_decode_partial(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
+                                const mla_cache_desc_t *cache, const int32_t *block_table,
+                                int32_t bt_stride, const int32_t *seq_lens, int32_t B,
+                                int32_t q_len, int32_t n_h, float scale, const mla_plan_t *plan,
+                                const int32_t *plan_dev, void *workspace,
+                                int64_t workspace_bytes, void *o_lat, float *lse,
+                                mla_stream_t stream);
+mla_status_t mla_decode_finish(const mla_plan_t *plan, const int32_t *plan_dev, void *workspace,
+                               int64_t workspace_bytes, mla_dtype_t out_dtype, void *o_lat,
+                               float *lse, mla_stream_t stream);
+
+/*
  * mla_combine_lse — merge per-split partial results (the num_splits
  * reduction named on the vLLM MLA page, "FP8 MLA 지원").  For each sequence b
  * and row r, with slots k in [split_off[b], split_off[b+1]):

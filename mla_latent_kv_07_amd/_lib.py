@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
     L.mla_decode.argtypes = [P, P, c_int32, ctypes.POINTER(CacheDesc), P, c_int32, P, c_int32,
                              c_int32, c_int32, c_float, ctypes.POINTER(Plan), P, P, c_int64, P,
                              P, P]
+    L.mla_decode_partial.argtypes = L.mla_decode.argtypes
+    L.mla_decode_finish.argtypes = [ctypes.POINTER(Plan), P, P, c_int64, c_int32, P, P, P]
     L.mla_combine_lse.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, P, c_int32, P, P]
     L.mla_absorb_q.argtypes = [P, c_int64, P, P, c_int32, c_int32, c_int32, c_int32, c_int32, P]
     L.mla_absorb_out_workspace.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32]
@@ -78,7 +80,8 @@ def load() -> ctypes.CDLL:
     L.mla_cache_bytes.restype = c_int64
     L.mla_last_error.restype = ctypes.c_char_p
     L.mla_version.restype = ctypes.c_char_p
-    for name in ("mla_decode_plan", "mla_decode", "mla_combine_lse", "mla_absorb_q",
+    for name in ("mla_decode_plan", "mla_decode", "mla_decode_partial", "mla_decode_finish",
+                 "mla_combine_lse", "mla_absorb_q",
                  "mla_absorb_out", "mla_gather_paged"):
         getattr(L, name).restype = c_int32
     _lib = L

@@ -85,15 +85,17 @@ class Decoder:
         self.q_len, self.n_h = q_len, n_h
 
     def __call__(self, q_lat, q_rope, cache: DeviceCache, block_table, seq_lens, scale,
-                 o_lat=None, lse=None, stream=None):
+                 o_lat=None, lse=None, stream=None, phase="all"):
         return decode(q_lat, q_rope, cache, block_table, seq_lens, self.q_len, self.n_h, scale,
                       self.info, self.plan_dev, self.workspace, o_lat=o_lat, lse=lse,
-                      stream=stream)
+                      stream=stream, phase=phase)
 
 
 def decode(q_lat, q_rope, cache: DeviceCache, block_table, seq_lens, q_len, n_h, scale, plan,
-           plan_dev, workspace, o_lat=None, lse=None, stream=None):
-    """mla_decode: returns (o_lat [T, n_h, d_c] in q's dtype, lse [T, n_h] fp32)."""
+           plan_dev, workspace, o_lat=None, lse=None, stream=None, phase="all"):
+    """mla_decode: returns (o_lat [T, n_h, d_c] in q's dtype, lse [T, n_h] fp32).
+    phase="partial" / "finish" call mla_decode_partial / mla_decode_finish
+    (the two launches of mla_decode) instead."""
     T = q_lat.shape[0]
     if o_lat is None:
         o_lat = torch.empty((T, n_h, cache.d_c), dtype=q_lat.dtype, device=q_lat.device)
@@ -102,10 +104,15 @@ def decode(q_lat, q_rope, cache: DeviceCache, block_table, seq_lens, q_len, n_h,
     B = block_table.shape[0]
     desc = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    L.check(L.load().mla_decode(_p(q_lat), _p(q_rope), _DT[q_lat.dtype], ctypes.byref(desc),
-                                _p(block_table), block_table.stride(0), _p(seq_lens), B, q_len, n_h,
-                                float(scale), ctypes.byref(plan), _p(plan_dev), _p(workspace),
-                                ws_bytes, _p(o_lat), _p(lse), _stream(stream)))
+    lib = L.load()
+    if phase == "finish":
+        L.check(lib.mla_decode_finish(ctypes.byref(plan), _p(plan_dev), _p(workspace), ws_bytes,
+                                      _DT[q_lat.dtype], _p(o_lat), _p(lse), _stream(stream)))
+        return o_lat, lse
+    fn = {"all": lib.mla_decode, "partial": lib.mla_decode_partial}[phase]
+    L.check(fn(_p(q_lat), _p(q_rope), _DT[q_lat.dtype], ctypes.byref(desc), _p(block_table),
+               block_table.stride(0), _p(seq_lens), B, q_len, n_h, float(scale), ctypes.byref(plan),
+               _p(plan_dev), _p(workspace), ws_bytes, _p(o_lat), _p(lse), _stream(stream)))
     return o_lat, lse
 
 

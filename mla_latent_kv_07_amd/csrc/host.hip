@@ -166,12 +166,15 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     return ok();
 }
 
-mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
-                        const mla_cache_desc_t *cache, const int32_t *block_table,
-                        int32_t bt_stride, const int32_t *seq_lens, int32_t B, int32_t q_len,
-                        int32_t n_h, float scale, const mla_plan_t *plan,
-                        const int32_t *plan_dev, void *workspace, int64_t workspace_bytes,
-                        void *o_lat, float *lse, mla_stream_t stream) {
+namespace {
+
+// Validate mla_decode's arguments and resolve them into kernel arguments.
+mla_status_t prepare_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
+                            const mla_cache_desc_t *cache, const int32_t *block_table,
+                            int32_t bt_stride, const int32_t *seq_lens, int32_t B, int32_t q_len,
+                            int32_t n_h, float scale, const mla_plan_t *plan,
+                            const int32_t *plan_dev, void *workspace, int64_t workspace_bytes,
+                            void *o_lat, float *lse, DecodeArgs *out) {
     mla_status_t st = check_cache(cache);
     if (st != MLA_OK) return st;
     if (!q_lat || !o_lat || !lse || !block_table || !seq_lens)
@@ -196,9 +199,9 @@ mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dty
     DecodeArgs a{};
     a.q_lat = q_lat; a.q_rope = q_rope; a.pool = cache->base; a.block_scales = cache->block_scales;
     a.block_table = block_table; a.seq_lens = seq_lens; a.plan = plan_dev;
-    int64_t rows = (int64_t)q_len * n_h;
+    const int64_t rows = (int64_t)q_len * n_h;
     if (plan->num_partials > 0) {
-        int64_t o_bytes = (int64_t)plan->num_partials * rows * cache->d_c * 4;
+        const int64_t o_bytes = (int64_t)plan->num_partials * rows * cache->d_c * 4;
         a.o_part = (float *)workspace;
         a.lse_part = (float *)((char *)workspace + (o_bytes + 255) / 256 * 256);
     }
@@ -210,26 +213,81 @@ mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dty
     a.num_items = plan->num_items; a.row_chunks = plan->row_chunks;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q_dtype = q_dtype; a.kv_dtype = cache->kv_dtype;
+    *out = a;
+    return MLA_OK;
+}
 
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
+    if (a.num_items == 0) return hipSuccess;
+    if (is_fast_shape(a.kv_dtype, a.d_c, a.d_r) && a.q_dtype == MLA_DT_BF16)
+        return a.kv_dtype == MLA_DT_BF16 ? launch_decode_bf16_mfma(a, s) : launch_decode_fp8_mfma(a, s);
+    return launch_decode_generic(a, s);
+}
+
+mla_status_t finish_decode(const mla_plan_t *plan, const int32_t *plan_dev, void *workspace,
+                           mla_dtype_t out_dtype, void *o_lat, float *lse, hipStream_t s) {
+    if (!plan->needs_combine) return ok();
+    const int64_t rows = (int64_t)plan->q_len * plan->n_h;
+    float *o_part = nullptr, *lse_part = nullptr;
+    if (plan->num_partials > 0) {
+        const int64_t o_bytes = (int64_t)plan->num_partials * rows * plan->d_c * 4;
+        o_part = (float *)workspace;
+        lse_part = (float *)((char *)workspace + (o_bytes + 255) / 256 * 256);
+    }
+    const int32_t *split_off = plan_dev + plan_split_off(plan->num_items);
+    const int32_t *flags = plan_dev + plan_flags_off(plan->num_items, plan->B);
+    return hip_status(launch_combine(o_part, lse_part, split_off, flags, plan->B, (int32_t)rows,
+                                     plan->d_c, o_lat, out_dtype, lse, s),
+                      "combine launch");
+}
+
+}  // namespace
+
+mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
+                        const mla_cache_desc_t *cache, const int32_t *block_table,
+                        int32_t bt_stride, const int32_t *seq_lens, int32_t B, int32_t q_len,
+                        int32_t n_h, float scale, const mla_plan_t *plan,
+                        const int32_t *plan_dev, void *workspace, int64_t workspace_bytes,
+                        void *o_lat, float *lse, mla_stream_t stream) {
+    DecodeArgs a;
+    mla_status_t st = prepare_decode(q_lat, q_rope, q_dtype, cache, block_table, bt_stride, seq_lens,
+                                     B, q_len, n_h, scale, plan, plan_dev, workspace,
+                                     workspace_bytes, o_lat, lse, &a);
+    if (st != MLA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = hipSuccess;
-    if (plan->num_items > 0) {
-        if (is_fast_shape(cache->kv_dtype, cache->d_c, cache->d_r) && q_dtype == MLA_DT_BF16) {
-            e = cache->kv_dtype == MLA_DT_BF16 ? launch_decode_bf16_mfma(a, s)
-                                               : launch_decode_fp8_mfma(a, s);
-        } else {
-            e = launch_decode_generic(a, s);
-        }
-        if (e != hipSuccess) return hip_status(e, "decode launch");
-    }
-    if (plan->needs_combine) {
-        const int32_t *split_off = plan_dev + plan_split_off(plan->num_items);
-        const int32_t *flags = plan_dev + plan_flags_off(plan->num_items, B);
-        e = launch_combine(a.o_part, a.lse_part, split_off, flags, B, (int32_t)rows, cache->d_c,
-                           o_lat, q_dtype, lse, s);
-        if (e != hipSuccess) return hip_status(e, "combine launch");
-    }
-    return ok();
+    hipError_t e = launch_decode(a, s);
+    if (e != hipSuccess) return hip_status(e, "decode launch");
+    return finish_decode(plan, plan_dev, workspace, q_dtype, o_lat, lse, s);
+}
+
+mla_status_t mla_decode_partial(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
+                                const mla_cache_desc_t *cache, const int32_t *block_table,
+                                int32_t bt_stride, const int32_t *seq_lens, int32_t B,
+                                int32_t q_len, int32_t n_h, float scale, const mla_plan_t *plan,
+                                const int32_t *plan_dev, void *workspace,
+                                int64_t workspace_bytes, void *o_lat, float *lse,
+                                mla_stream_t stream) {
+    DecodeArgs a;
+    mla_status_t st = prepare_decode(q_lat, q_rope, q_dtype, cache, block_table, bt_stride, seq_lens,
+                                     B, q_len, n_h, scale, plan, plan_dev, workspace,
+                                     workspace_bytes, o_lat, lse, &a);
+    if (st != MLA_OK) return st;
+    return hip_status(launch_decode(a, (hipStream_t)stream), "decode launch");
+}
+
+mla_status_t mla_decode_finish(const mla_plan_t *plan, const int32_t *plan_dev, void *workspace,
+                               int64_t workspace_bytes, mla_dtype_t out_dtype, void *o_lat,
+                               float *lse, mla_stream_t stream) {
+    if (!plan || !plan_dev || !o_lat || !lse)
+        return fail(MLA_ERR_INVALID_ARG, "NULL plan/plan_dev/o_lat/lse");
+    if (out_dtype != MLA_DT_F32 && out_dtype != MLA_DT_BF16)
+        return fail(MLA_ERR_UNSUPPORTED, "out dtype %d unsupported", (int)out_dtype);
+    if (workspace_bytes < plan->workspace_bytes)
+        return fail(MLA_ERR_WORKSPACE, "workspace %lld < %lld bytes", (long long)workspace_bytes,
+                    (long long)plan->workspace_bytes);
+    if (plan->workspace_bytes > 0 && (!workspace || !aligned(workspace, 256)))
+        return fail(MLA_ERR_ALIGN, "workspace NULL or not 256-byte aligned");
+    return finish_decode(plan, plan_dev, workspace, out_dtype, o_lat, lse, (hipStream_t)stream);
 }
 
 mla_status_t mla_combine_lse(const float *o_part, const float *lse_part,

@@ -20,6 +20,7 @@
  *  [thaki]   thakicloud.com, "transformer-attention-kv-cache-math"
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -30,6 +31,9 @@ enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
 /* Tokens per paged block: the FlashMLA backend accepts only 64
  * ([vllm], "FlashMLABackend: 하드웨어 요구사항"). */
 #define ORACLE_BLOCK 64
+
+/* Threads the OpenMP loops use (reported next to oracle timings). */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------------- */
 /* Number formats, decoded from their definitions.                          */

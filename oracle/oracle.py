@@ -27,7 +27,7 @@ import numpy as np
 
 __all__ = [
     "PIN_STATUS", "FMT_F32", "FMT_BF16", "FMT_FP8_E4M3", "BLOCK",
-    "lib", "build_oracle",
+    "lib", "build_oracle", "threads",
     "kv_bytes_per_token_layer", "kv_cache_bytes", "floats_per_token_all_layers",
     "bf16_bits_to_f64", "e4m3_to_f64", "f64_to_e4m3", "block_bytes",
     "gather", "decode", "combine", "decode_splits",
@@ -106,8 +106,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_decode.restype = i32
         L.oracle_combine.argtypes = [P, P, i32, i64, i32, P, P]
         L.oracle_combine.restype = i32
+        L.oracle_threads.restype = i32
         _lib = L
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(lib().oracle_threads())
 
 
 def _ptr(a):
