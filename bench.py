@@ -10,7 +10,7 @@ Prints one JSON line: latent-cache GB/s over the whole step, plus
   roofline      the decode kernel's algorithmic cache bytes per launch over
                 its average launch time (HIP events on the launch stream),
                 against MI355X's 8 TB/s HBM peak;
-  cpu_baseline  the CPU oracle timed on a quarter of the batch on this host.
+  cpu_baseline  the CPU oracle timed on the same batch on this host's cores.
 Inputs are resident in HBM before timing; 4 replicas of the cache pool are
 rotated so no step finds its pool in the 256 MB last-level (MALL) cache.
 """

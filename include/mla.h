@@ -98,6 +98,9 @@ typedef struct {
     int32_t needs_combine;  /* 1 if mla_decode launches the LSE combine */
     int32_t max_splits;     /* largest split count of any sequence */
     int32_t blocks_per_item;/* target blocks per work item */
+    int32_t partial_dtype;  /* element type of the partial outputs in the workspace:
+                               BF16 for the MFMA shapes (d_c 512, d_r 64, bf16/fp8
+                               cache), F32 otherwise */
     int64_t plan_ints;      /* int32 entries of the device plan */
     int64_t workspace_bytes;/* partial-result workspace mla_decode needs */
 } mla_plan_t;
@@ -194,8 +197,8 @@ mla_status_t mla_decode_finish(const mla_plan_t *plan, const int32_t *plan_dev, 
  *   o = sum_k w_k o_k / sum_k w_k;  lse = M + ln sum_k w_k.
  * Slots with lse = -inf carry no weight; a sequence whose slots are all -inf
  * (or that has none) gets o = 0, lse = -inf.
- * o_part [P][rows][d_c] fp32 (normalised partial outputs), lse_part [P][rows]
- * fp32, split_off [B+1] int32, seq_flags [B] int32 or NULL: sequences with
+ * o_part [P][rows][d_c] fp32 (normalised partial outputs, 16-byte aligned;
+ * d_c a multiple of 4, at most 1024), lse_part [P][rows] fp32, split_off [B+1] int32, seq_flags [B] int32 or NULL: sequences with
  * flag 1 are skipped (their output is already final).  rows = q_len * n_h.
  * o_lat [B*rows][d_c] in out_dtype (F32 or BF16); lse [B*rows] fp32.
  */

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/mla.h"
+#include "mla.h"
 
 namespace mla {
 
@@ -20,7 +20,7 @@ struct DecodeArgs {
     const int32_t *block_table;
     const int32_t *seq_lens;
     const int32_t *plan;       // device plan (header, items, split_off, seq_flags)
-    float *o_part;             // [num_partials][rows][d_c]
+    void *o_part;              // [num_partials][rows][d_c] in partial_dtype
     float *lse_part;           // [num_partials][rows]
     void *o_lat;
     float *lse;
@@ -30,7 +30,7 @@ struct DecodeArgs {
     int32_t rows;              // q_len * n_h
     int32_t num_items, row_chunks;
     float scale_log2;          // scale * log2(e)
-    mla_dtype_t q_dtype, kv_dtype;
+    mla_dtype_t q_dtype, kv_dtype, partial_dtype;
 };
 
 // Plan layout offsets (int32 entries).
@@ -43,9 +43,10 @@ __host__ __device__ inline int64_t plan_flags_off(int32_t num_items, int32_t B) 
 hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16_mfma(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_fp8_mfma(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_combine(const float *o_part, const float *lse_part, const int32_t *split_off,
-                          const int32_t *seq_flags, int32_t B, int32_t rows, int32_t d_c,
-                          void *o_lat, mla_dtype_t out_dt, float *lse, hipStream_t s);
+hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *lse_part,
+                          const int32_t *split_off, const int32_t *seq_flags, int32_t B,
+                          int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dt, float *lse,
+                          hipStream_t s);
 hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int32_t c_bytes,
                          int32_t r_bytes, bool split_rows, const int32_t *bt, int32_t bt_stride,
                          const int32_t *seq_lens, int32_t B, int32_t max_tokens, uint8_t *out,

@@ -3,23 +3,25 @@
 //
 // Workgroup = 4 waves = 128 query rows (heads x query tokens) of one
 // sequence; wave w owns rows 32w..32w+31 for the whole work item and keeps
-//   - its queries as MFMA B fragments in VGPRs (32 rows x 576, 144 VGPRs),
+//   - the latent part of its queries as MFMA B fragments in VGPRs
+//     (32 rows x 512, 128 VGPRs); the rotary part sits in LDS (16 KB),
 //   - O^T, the fp32 latent output sum (512 x 32 rows, 256 accumulators).
-// The cached tokens stream through LDS one 64-token paged block at a time
-// (the block is the tile), double-buffered with asynchronous direct-to-LDS
-// loads; every tile is read from HBM once per workgroup and from LDS by all
-// four waves:
-//   score  S^T[64 tok x 32 rows] = K_tile[64 x 576] . Q^T        (MFMA 32x32x16)
-//   p      = exp2(S*scale*log2e - m) with a lazily raised running max m
-//   value  O^T[512 x 32] += V_tile^T[512 x 64] . P^T[64 x 32]    (MFMA 32x32x16)
-// where V_tile is the c part of the same LDS rows, read transposed with
-// ds_read_b64_tr_b16.  The score accumulator layout already is the value
-// contraction's B operand, up to a fixed permutation of the 16 tokens of a
-// k-step that both operands share, so P never moves between lanes.
+// Cached tokens stream through LDS in 32-token stages (half a paged block),
+// four stage buffers deep, filled by asynchronous direct-to-LDS loads that
+// run up to three stages ahead of the compute.  Every cached byte is read
+// from HBM once per workgroup and from LDS by all four waves:
+//   score  S^T[32 tok x 32 rows] = K[32 x 576] . Q^T           (MFMA 32x32x16)
+//   p      = exp2(S*scale*log2e - m) with a lazily raised reference max m
+//   value  O^T[512 x 32] += V^T[512 x 32] . P^T[32 x 32]       (MFMA 32x32x16)
+// V is the latent part of the same LDS rows, read transposed with
+// ds_read_b64_tr_b16; the score accumulator layout is already the value
+// MFMA's B operand, up to a fixed permutation of the 16 tokens of a k-step
+// that both operands share, so P never moves between lanes.
 //
-// Score content + RoPE decomposition: huny.dev "DeepSeek MLA 해부" §2-3;
-// W^UK absorption (the q_lat operand): §3-1; latent value sum: §3-2;
-// MQA form over one latent head: vLLM MLA page, "MLA의 MQA 디코딩 경로".
+// Score = content + rotary part: huny.dev "DeepSeek MLA 해부" §2-3
+// decomposition; absorbed query against the cached latent: §3-1; latent
+// value sum: §3-2; one shared latent "head" (MQA form): vLLM MLA page,
+// "MLA의 MQA 디코딩 경로".
 #include "common.hpp"
 
 namespace mla {
@@ -30,106 +32,142 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int DC = 512, DR = 64, D = DC + DR;
-constexpr int ROW_BYTES = D * 2;                 // 1152
-constexpr int TILE_BYTES = kBlock * ROW_BYTES;   // 73728
-constexpr int KSTEPS = D / 16;                   // 36 score k-steps
-constexpr int MBLOCKS = DC / 32;                 // 16 value M-blocks
+constexpr int DC = 512, DR = 64;
+constexpr int ROW_BYTES = (DC + DR) * 2;        // 1152 bytes per cached token in HBM
+constexpr int CB = DC * 2;                      // 1024: latent bytes of a token
+constexpr int RB = DR * 2;                      // 128: rotary bytes of a token
+constexpr int HALF = 32;                        // tokens per pipeline stage
+constexpr int STAGE_BYTES = HALF * (CB + RB);   // 36864
+constexpr int NSTAGE = 4;
+constexpr int KC = DC / 16;                     // 32 latent score k-steps
+constexpr int MBLOCKS = DC / 32;                // 16 value M-blocks
+constexpr int O_PITCH = CB + 16;                // epilogue staging row pitch (bytes)
 
-// 16-byte chunk swizzle inside each 128-byte group of a row: chunk c of token
-// t is stored at chunk c ^ sigma(t).  sigma is a bijection on any 8 aligned
-// consecutive tokens (conflict-free score reads: 8 lanes = 8 tokens, same
-// chunk) and sigma>>1 is a bijection on any 4 aligned consecutive tokens
-// (conflict-free transposed reads: 4 tokens x 2 chunks per 16 lanes).
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// LDS layout of a stage: latent rows [32][1024 B] then rotary rows [32][128 B].
+// 16-byte chunk c of latent row t is stored at chunk c ^ sc(t) (the XOR stays
+// inside the 16-chunk / 256-byte group), rotary chunk c of row t at c ^ sr(t).
+// With 64 four-byte banks (256 B per cycle):
+//  - score reads (16 lanes = 16 consecutive tokens, one chunk) need sc to be
+//    a bijection on t mod 16;
+//  - transposed value reads (32 lanes = 4 consecutive tokens x 4 chunks of a
+//    4-chunk group) need sc >> 2 to be a bijection on t mod 4;
+//  - rotary reads (16 tokens, one chunk, 128-byte rows) need (t & 1, sr(t))
+//    distinct over 16 tokens.
+__device__ __forceinline__ int sc(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+__device__ __forceinline__ int sr(int t) { return (t >> 1) & 7; }
 
-// Per-lane source offsets of the asynchronous tile copy.  Wave w copies LDS
-// bytes [w*18K, (w+1)*18K) in 1 KiB steps; the lane whose LDS slot is
-// (token t, stored chunk pc) reads global chunk pc ^ sigma(t) of token t.
-// 9 KiB is exactly 8 rows, so steps k and k+9 differ by 9216 bytes and only
-// nine offsets per lane are distinct.
-struct TileLoadOffsets {
-    int off[9];
-};
-
-__device__ __forceinline__ TileLoadOffsets tile_load_offsets(int wave, int lane) {
-    TileLoadOffsets o;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-        const int p = (wave * 18 + k) * 1024 + lane * 16;
-        const int t = p / ROW_BYTES;
-        const int pc = (p - t * ROW_BYTES) >> 4;
-        o.off[k] = t * ROW_BYTES + ((pc ^ swz(t)) << 4);
-    }
-    return o;
+// One asynchronous 1 KiB copy: global_load_lds_dwordx4 writes lane i's 16
+// bytes to LDS at M0 + 16 i.  Issued as inline asm so that the compiler's
+// wait-count pass does not see an LDS writer in flight (it would otherwise
+// drain every LDS read with lgkmcnt(0)); completion is awaited explicitly
+// (vmcnt + barrier) before a stage is read.  VMEM loads complete in order, so
+// the compiler's own vmcnt waits stay correct: unseen extra loads can only
+// make them over-wait.
+__device__ __forceinline__ void dma16(lds_u8 *lds_dst, uint32_t voff, const uint8_t *src) {
+    const uint32_t lds = (uint32_t)(uintptr_t)lds_dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(src)
+                 : "memory", "m0");
 }
 
-// Issue the asynchronous copy of one 64-token block into an LDS tile.
-__device__ __forceinline__ void issue_tile_load(const uint8_t *blk_base, lds_u8 *tile, int wave,
-                                                const TileLoadOffsets &o) {
+constexpr int DMA_PER_STAGE = 9;   // per wave: 8 latent rows + 1 KiB of rotary rows
+
+// Copy one stage (32 tokens starting at token tok0 of the block at blk_base).
+// Wave w copies latent rows 8w..8w+7 (one instruction each) and the rotary
+// rows of the same 8 tokens (one instruction).
+__device__ __forceinline__ void issue_stage(const uint8_t *blk_base, int tok0, lds_u8 *stage,
+                                            int wave, int lane) {
 #pragma unroll
-    for (int k = 0; k < 18; ++k) {
-        const int region = (wave * 18 + k) * 1024;
-        __builtin_amdgcn_global_load_lds((const void *)(blk_base + o.off[k % 9] + (k / 9) * 9216),
-                                         (__attribute__((address_space(3))) void *)(tile + region),
-                                         16, 0, 0);
+    for (int k = 0; k < 8; ++k) {
+        const int t = wave * 8 + k;
+        dma16(stage + t * CB, (uint32_t)((tok0 + t) * ROW_BYTES + ((lane ^ sc(t)) << 4)), blk_base);
     }
+    const int t = wave * 8 + (lane >> 3);
+    dma16(stage + HALF * CB + wave * 8 * RB,
+          (uint32_t)((tok0 + t) * ROW_BYTES + CB + (((lane & 7) ^ sr(t)) << 4)), blk_base);
 }
 
-__device__ __forceinline__ float max_across_halves(float v) {
-    return fmaxf(v, __shfl_xor(v, 32, 64));
+// Wait until at most `ahead` later stages of this wave's copies are in flight.
+__device__ __forceinline__ void wait_stage(int ahead) {
+    static_assert(DMA_PER_STAGE == 9, "vmcnt immediates below assume 9 copies per stage");
+    if (ahead >= 2)
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (ahead == 1)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Loads of wave-uniform values (plan, block table, lengths) through the
+// constant address space become scalar loads, which never wait on the
+// vector-memory counter of the asynchronous stage copies.
+__device__ __forceinline__ int32_t sload(const int32_t *p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
 }
 
 __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
-    const int64_t num_blocks = a.num_pool_blocks;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TILE_BYTES];
-    lds_u8 *tiles = (lds_u8 *)smem;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_[NSTAGE * STAGE_BYTES];
+    // rotary part of the queries, [128 rows][128 B], chunk c of row r stored
+    // at chunk c ^ sr(r)
+    __shared__ __attribute__((aligned(1024))) uint8_t qrope_[kRowsPerChunk * RB];
+    lds_u8 *smem = (lds_u8 *)smem_;
+    lds_u8 *qrope = (lds_u8 *)qrope_;
 
     // workgroup -> (item, row chunk); the row chunks of one item sit 8 apart so
-    // that they land on the same XCD and share the tile through its L2.
+    // that they land on the same XCD and share the stream through its L2.
     const int rc = a.row_chunks;
     const int grp = blockIdx.x / (8 * rc), within = blockIdx.x % (8 * rc);
     const int chunk = within / 8;
     const int item = grp * 8 + within % 8;
     if (item >= a.num_items) return;
-    const int32_t *it = a.plan + plan_items_off() + 4 * item;
-    const int b = it[0], blk0 = it[1], blk1 = it[2], slot = it[3];
-    const int ntiles = blk1 - blk0;
+    const int64_t io = plan_items_off() + 4 * item;
+    const int b = sload(a.plan, io), blk0 = sload(a.plan, io + 1), blk1 = sload(a.plan, io + 2),
+              slot = sload(a.plan, io + 3);
+    const int S = sload(a.seq_lens, b);
+    const int nst = 2 * (blk1 - blk0);   // 32-token stages in this item
+    // a stage holds tokens only if its first position is < S (the plan covers
+    // ceil(S/64) blocks, so the second half of the last block may be empty)
+    const int p_first = blk0 * kBlock;
+    const int nst_live = min(nst, (S - p_first + HALF - 1) / HALF);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5;           // lane half
     const int ln = lane & 31;
-    const int row = chunk * kRowsPerChunk + wave * 32 + ln;   // query row in the sequence
+    const int wrow = wave * 32 + ln;   // row inside the chunk
+    const int row = chunk * kRowsPerChunk + wrow;
     const bool row_ok = row < a.rows;
-    const int S = a.seq_lens[b];
     const int lim = row_ok ? S - a.q_len + row / a.n_h + 1 : 0;   // visible positions < lim
     const int64_t grow = (int64_t)b * a.rows + row;
 
     const uint8_t *pool = (const uint8_t *)a.pool;
-    const int32_t *bt = a.block_table + (int64_t)b * a.bt_stride;
-    auto block_ptr = [&](int blk) {
-        int64_t id = bt[blk];
+    const int64_t bt_row = (int64_t)b * a.bt_stride;
+    const int64_t num_blocks = a.num_pool_blocks;
+    auto stage_src = [&](int st) {
+        int64_t id = sload(a.block_table, bt_row + blk0 + (st >> 1));
         id = id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
-        return pool + id * (int64_t)TILE_BYTES;
+        return pool + id * (int64_t)(kBlock * ROW_BYTES);
     };
+    auto stage_buf = [&](int st) { return smem + (st & (NSTAGE - 1)) * STAGE_BYTES; };
 
-    const TileLoadOffsets tlo = tile_load_offsets(wave, lane);
-    // first tile in flight before the query loads
-    issue_tile_load(block_ptr(blk0), tiles, wave, tlo);
+    // stage 0 in flight, then the queries, then stages 1 and 2
+    issue_stage(stage_src(0), 0, stage_buf(0), wave, lane);
 
-    // queries as B fragments: lane (row ln, half g) holds features 16ks+8g..+7
-    bf16x8 qf[KSTEPS];
+    bf16x8 qf[KC];
     {
         // rows past the end load row 0's queries; their scores are all masked
         const int64_t qrow = row_ok ? grow : (int64_t)b * a.rows;
         const bf16x8 *ql = (const bf16x8 *)((const uint16_t *)a.q_lat + qrow * DC);
         const bf16x8 *qr = (const bf16x8 *)((const uint16_t *)a.q_rope + qrow * DR);
 #pragma unroll
-        for (int ks = 0; ks < DC / 16; ++ks) qf[ks] = ql[2 * ks + g];
+        for (int ks = 0; ks < KC; ++ks) qf[ks] = ql[2 * ks + g];
 #pragma unroll
-        for (int ks = 0; ks < DR / 16; ++ks) qf[DC / 16 + ks] = qr[2 * ks + g];
+        for (int ks = 0; ks < DR / 16; ++ks)
+            *(bf16x8 *)(qrope + wrow * RB + (((2 * ks + g) ^ sr(wrow)) << 4)) = qr[2 * ks + g];
     }
+    for (int st = 1; st < 3 && st < nst_live; ++st)
+        issue_stage(stage_src(st), (st & 1) * HALF, stage_buf(st), wave, lane);
 
     f32x16 oacc[MBLOCKS];
 #pragma unroll
@@ -137,140 +175,172 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     float m_run = -INFINITY;   // reference max (log2 units), lazily raised
     float l_lane = 0.f;        // this lane's share of the softmax denominator
 
-    // Per-lane LDS read bases; every read below is base + a compile-time
-    // offset.  Score reads: token ln (+32h), chunk 2ks+g, stored at chunk
-    // (2ks+g) ^ sigma(ln); the XOR only touches the low 3 bits, so the bases
-    // depend on ks & 3 and ks >> 2 adds 128 bytes.
-    int kbase[4];
+    // Per-lane LDS read bases; every read is base + stage offset + a
+    // compile-time immediate.
+    // Score, latent chunk 2ks+g of token ln: (2ks+g) ^ sc(ln) = 2ks ^ x with
+    // x = g ^ sc(ln), so the base depends on ks & 7 and ks >> 3 adds 256 B.
+    const int x = g ^ sc(ln);
+    int kbase[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kbase[j] = ln * ROW_BYTES + (((2 * j + g) ^ swz(ln)) << 4);
+    for (int j = 0; j < 8; ++j) kbase[j] = ln * CB + (((2 * j) ^ x) << 4);
+    int rbase[DR / 16];
+#pragma unroll
+    for (int j = 0; j < DR / 16; ++j) rbase[j] = HALF * CB + ln * RB + (((2 * j + g) ^ sr(ln)) << 4);
+    int qrbase[DR / 16];
+#pragma unroll
+    for (int j = 0; j < DR / 16; ++j) qrbase[j] = wrow * RB + (((2 * j + g) ^ sr(wrow)) << 4);
     // Transposed value reads (ds_read_b64_tr_b16: lane i of each 16-lane group
     // receives element i%4 of the 8 bytes read by lanes 4s + i/4, s = 0..3):
-    // lane (group G, index w) reads token 4(G/2) + w/4 of the k-step and the
-    // 4 features 32mb + 16(G%2) + 4(w%4), i.e. chunk 4mb + 2(G%2) + (w%4)/2,
-    // byte 8(w%2); both operands then agree on the token order of a k-step.
+    // lane (group G, index w) reads token 4(G/2) + w/4 (+8 for the upper half)
+    // of the k-step and features 32mb + 16(G%2) + 4(w%4): chunk
+    // 4mb + 2(G%2) + (w%4)/2, byte 8(w%2).  Bases depend on mb & 3 (the XOR
+    // touches the low 4 chunk bits); mb >> 2 adds 256 B, a k-step 16 KiB.
     const int grp16 = lane >> 4, w16 = lane & 15;
     const int tr_tok = 4 * (grp16 >> 1) + (w16 >> 2);
     const int tr_chunk = 2 * (grp16 & 1) + ((w16 & 3) >> 1);
-    int vbase[2];
+    int vbase[2][4];
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-        vbase[e] = tr_tok * ROW_BYTES + (((4 * e + tr_chunk) ^ swz(tr_tok)) << 4) + (w16 & 1) * 8;
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            vbase[hi][e] = (tr_tok + 8 * hi) * CB + (((4 * e + tr_chunk) ^ sc(tr_tok + 8 * hi)) << 4) +
+                           (w16 & 1) * 8;
 
-    for (int ti = 0; ti < ntiles; ++ti) {
-        lds_u8 *tile = tiles + (ti & 1) * TILE_BYTES;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies landed
-        __syncthreads();                      // ... and everyone's; other buffer free
-        const int p0 = (blk0 + ti) * kBlock;
-        const int valid = S - p0;             // rows of this block holding tokens
-        if (valid < kBlock) {
-            // zero the tail rows so that P = 0 never meets NaN/garbage values
-            for (int off = valid * ROW_BYTES + threadIdx.x * 16; off < TILE_BYTES; off += 256 * 16)
-                *(uint4 *)(tile + off) = make_uint4(0, 0, 0, 0);
+    for (int st = 0; st < nst_live; ++st) {
+        // stage st landed (later stages may still be in flight) ...
+        wait_stage(min(2, nst_live - 1 - st));
+        __syncthreads();   // ... for every wave; stage st-1's buffer is free
+        lds_u8 *stg = stage_buf(st);
+        const int p0 = p_first + st * HALF;
+        const int valid = S - p0;   // >= 1 for a live stage
+        if (valid < HALF) {
+            // zero the rows past the sequence end so that P = 0 never meets
+            // NaN or stale data in the value MFMA
+            for (int off = valid * CB + threadIdx.x * 16; off < HALF * CB; off += 256 * 16)
+                *(uint4 *)(stg + off) = make_uint4(0, 0, 0, 0);
+            for (int off = HALF * CB + valid * RB + threadIdx.x * 16; off < STAGE_BYTES; off += 256 * 16)
+                *(uint4 *)(stg + off) = make_uint4(0, 0, 0, 0);
             __syncthreads();
         }
-        if (ti + 1 < ntiles)
-            issue_tile_load(block_ptr(blk0 + ti + 1), tiles + ((ti + 1) & 1) * TILE_BYTES, wave, tlo);
+        if (st + 3 < nst_live)
+            issue_stage(stage_src(st + 3), ((st + 3) & 1) * HALF, stage_buf(st + 3), wave, lane);
 
+        // ---- score: S^T[32 tokens x 32 rows]; K fragments two k-steps ahead
+        f32x16 sacc = {};
+        auto kld = [&](int ks) {
+            return ks < KC ? *(const bf16x8 *)(stg + kbase[ks & 7] + 256 * (ks >> 3))
+                           : *(const bf16x8 *)(stg + rbase[(ks - KC) & 3]);
+        };
+        auto qget = [&](int ks) {
+            return ks < KC ? qf[ks < KC ? ks : 0] : *(const bf16x8 *)(qrope + qrbase[(ks - KC) & 3]);
+        };
+        constexpr int KS = KC + DR / 16;   // 36
+        bf16x8 kb0 = kld(0), kb1 = kld(1), kb2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            // ---- score: S^T[32 tokens x 32 rows] for tokens 32h..32h+31
-            f32x16 sacc = {};
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 2 < KS) kb2 = kld(ks + 2);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb0, qget(ks), sacc, 0, 0, 0);
+            kb0 = kb1;
+            kb1 = kb2;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+
+        // ---- online softmax; lane holds row ln, tokens 8(r/4)+4g+r%4
+        float mx = -INFINITY;
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 kf = *(const bf16x8 *)(tile + kbase[ks & 3] + 128 * (ks >> 2) + h * 32 * ROW_BYTES);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+            const int p = p0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const float s = p < lim ? sacc[r] * a.scale_log2 : -INFINITY;
+            sacc[r] = s;
+            mx = fmaxf(mx, s);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // raise the reference max only when a score exceeds it by 2^8
+        const bool raise = mx > m_run + 8.0f;
+        const float m_new = raise ? mx : m_run;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        if (__ballot(raise && m_run != -INFINITY)) {
+            // rare: keep the accumulators in AGPRs and rescale them block by
+            // block (a plain multiply makes the compiler move all 256 into VGPRs)
+#pragma unroll
+            for (int mb = 0; mb < MBLOCKS; ++mb) {
+                asm volatile("" : "+a"(oacc[mb]));
+                oacc[mb] *= alpha;
+                asm volatile("" : "+a"(oacc[mb]));
             }
-            // ---- online softmax; lane holds row ln, tokens 8(r/4)+4g+r%4
-            float mx = -INFINITY;
+        }
+        l_lane *= alpha;
+        m_run = m_new;
+        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+        bf16x8 pf[2];
+        float psum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int p = p0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
-                const float s = p < lim ? sacc[r] * a.scale_log2 : -INFINITY;
-                sacc[r] = s;
-                mx = fmaxf(mx, s);
-            }
-            mx = max_across_halves(mx);
-            // raise the reference max only when a score exceeds it by 2^8
-            const bool raise = mx > m_run + 8.0f;
-            const float m_new = raise ? mx : m_run;
-            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-            if (__ballot(raise && m_run != -INFINITY)) {
-                // rare: keep the accumulators in AGPRs and rescale them one
-                // block at a time (a plain multiply makes the compiler move
-                // all 256 of them into VGPRs)
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(sacc[r] - m_ref);
+            psum += pv;
+            pf[r >> 3][r & 7] = (__bf16)pv;
+        }
+        l_lane += psum;
+
+        // ---- value: O^T[512 x 32] += V^T[512 x 16 tok] . P^T[16 tok x 32],
+        // two k-steps; transposed V fragments two MFMAs ahead
+        auto vld = [&](int i) {
+            const int s2 = i / MBLOCKS, mb = i % MBLOCKS;
+            lds_u8 *lo = stg + vbase[0][mb & 3] + s2 * 16 * CB + 256 * (mb >> 2);
+            lds_u8 *hi = stg + vbase[1][mb & 3] + s2 * 16 * CB + 256 * (mb >> 2);
+            bf16x8 vf;
+            vf.lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo));
+            vf.hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi));
+            return vf;
+        };
+        bf16x8 vb0 = vld(0), vb1 = vld(1), vb2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-                for (int mb = 0; mb < MBLOCKS; ++mb) {
-                    asm volatile("" : "+a"(oacc[mb]));
-                    oacc[mb] *= alpha;
-                    asm volatile("" : "+a"(oacc[mb]));
-                }
-            }
-            l_lane *= alpha;
-            m_run = m_new;
-            const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-            bf16x8 pf[2];
-            float psum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(sacc[r] - m_ref);
-                psum += pv;
-                pf[r >> 3][r & 7] = (__bf16)pv;
-            }
-            l_lane += psum;
-            // ---- value: O^T[512 x 32] += V^T[512 x 16 tok] . P^T[16 tok x 32]
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int tok_off = (32 * h + 16 * s2) * ROW_BYTES;
-#pragma unroll
-                for (int mb = 0; mb < MBLOCKS; ++mb) {
-                    lds_u8 *vp = tile + vbase[mb & 1] + tok_off + 128 * (mb >> 1);
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4 *)vp);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4 *)(vp + 8 * ROW_BYTES));
-                    bf16x8 vf;
-                    vf.lo = __builtin_bit_cast(bf16x4, lo);
-                    vf.hi = __builtin_bit_cast(bf16x4, hi);
-                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], oacc[mb], 0, 0, 0);
-                }
-            }
+        for (int i = 0; i < 2 * MBLOCKS; ++i) {
+            if (i + 2 < 2 * MBLOCKS) vb2 = vld(i + 2);
+            oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb0, pf[i / MBLOCKS],
+                                                                        oacc[i % MBLOCKS], 0, 0, 0);
+            vb0 = vb1;
+            vb1 = vb2;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i + 2 < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
     }
 
-    // ---- epilogue: lane (row ln, half g) holds features 32mb + 8(r/4) + 4g + (r%4)
+    // ---- epilogue: O / l as bf16 rows staged through LDS, then 1 KiB
+    // coalesced row stores (final o_lat, or this split's bf16 partial).
     const float l_tot = l_lane + __shfl_xor(l_lane, 32, 64);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-    if (!row_ok) return;
-    if (slot < 0) {
-        uint16_t *dst = (uint16_t *)a.o_lat + grow * DC;
+    __syncthreads();   // every wave is done with the stage buffers
+    lds_u8 *orow = smem + wrow * O_PITCH;
 #pragma unroll
-        for (int mb = 0; mb < MBLOCKS; ++mb) {
+    for (int mb = 0; mb < MBLOCKS; ++mb) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int f = 32 * mb + 8 * q + 4 * g;
-                bf16x4 v;
-                v[0] = (__bf16)(oacc[mb][4 * q + 0] * inv);
-                v[1] = (__bf16)(oacc[mb][4 * q + 1] * inv);
-                v[2] = (__bf16)(oacc[mb][4 * q + 2] * inv);
-                v[3] = (__bf16)(oacc[mb][4 * q + 3] * inv);
-                *(bf16x4 *)(dst + f) = v;
-            }
+        for (int q = 0; q < 4; ++q) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[mb][4 * q + e] * inv);
+            *(bf16x4 *)(orow + (32 * mb + 8 * q + 4 * g) * 2) = v;
         }
-        if (g == 0) a.lse[grow] = lse_v;
-    } else {
-        float *dst = a.o_part + ((int64_t)slot * a.rows + row) * DC;
-#pragma unroll
-        for (int mb = 0; mb < MBLOCKS; ++mb) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int f = 32 * mb + 8 * q + 4 * g;
-                *(float4 *)(dst + f) = make_float4(oacc[mb][4 * q] * inv, oacc[mb][4 * q + 1] * inv,
-                                                   oacc[mb][4 * q + 2] * inv, oacc[mb][4 * q + 3] * inv);
-            }
-        }
-        if (g == 0) a.lse_part[(int64_t)slot * a.rows + row] = lse_v;
+    }
+    // each wave stores its own 32 rows (no cross-wave dependency)
+    uint8_t *dst_base = slot < 0 ? (uint8_t *)a.o_lat + ((int64_t)b * a.rows) * CB
+                                 : (uint8_t *)a.o_part + ((int64_t)slot * a.rows) * CB;
+    const int row0 = chunk * kRowsPerChunk + wave * 32;
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+        if (row0 + r >= a.rows) break;
+        const uint4 v = *(const uint4 *)(smem + (wave * 32 + r) * O_PITCH + lane * 16);
+        *(uint4 *)(dst_base + (int64_t)(row0 + r) * CB + lane * 16) = v;
+    }
+    if (row_ok && g == 0) {
+        if (slot < 0)
+            a.lse[grow] = lse_v;
+        else
+            a.lse_part[(int64_t)slot * a.rows + row] = lse_v;
     }
 }
 
@@ -284,7 +354,7 @@ hipError_t launch_decode_bf16_mfma(const DecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_fp8_mfma(const DecodeArgs &a, hipStream_t s) {
-    // fp8 MFMA path not instantiated yet: fall back to the generic kernel
+    // fp8 MFMA path not instantiated yet: the generic kernel serves fp8 caches
     return launch_decode_generic(a, s);
 }
 

@@ -133,8 +133,16 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
                 }
             }
             if (lane == 0) a.lse[grow] = lse_v;
+        } else if (a.partial_dtype == MLA_DT_BF16) {
+            uint16_t *dst = (uint16_t *)a.o_part + ((int64_t)slot * a.rows + r) * a.d_c;
+#pragma unroll
+            for (int j = 0; j < kMaxC; ++j) {
+                const int f = lane + 64 * j;
+                if (f < a.d_c) dst[f] = f32_to_bf16(o[j] * inv);
+            }
+            if (lane == 0) a.lse_part[(int64_t)slot * a.rows + r] = lse_v;
         } else {
-            float *dst = a.o_part + ((int64_t)slot * a.rows + r) * a.d_c;
+            float *dst = (float *)a.o_part + ((int64_t)slot * a.rows + r) * a.d_c;
 #pragma unroll
             for (int j = 0; j < kMaxC; ++j) {
                 const int f = lane + 64 * j;

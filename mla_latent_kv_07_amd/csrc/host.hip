@@ -131,8 +131,9 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     info->needs_combine = (num_partials > 0 || any_empty) ? 1 : 0;
     info->max_splits = max_splits;
     info->blocks_per_item = (int32_t)share;
+    info->partial_dtype = is_fast_shape(kv_dtype, d_c, d_r) ? MLA_DT_BF16 : MLA_DT_F32;
     info->plan_ints = 4 + 4 * num_items + 2 * (int64_t)B + 1;
-    int64_t o_bytes = num_partials * rows * d_c * 4;
+    int64_t o_bytes = num_partials * rows * d_c * elem_bytes((mla_dtype_t)info->partial_dtype);
     int64_t o_bytes_al = (o_bytes + 255) / 256 * 256;
     info->workspace_bytes = num_partials ? o_bytes_al + num_partials * rows * 4 : 0;
 
@@ -200,9 +201,12 @@ mla_status_t prepare_decode(const void *q_lat, const void *q_rope, mla_dtype_t q
     a.q_lat = q_lat; a.q_rope = q_rope; a.pool = cache->base; a.block_scales = cache->block_scales;
     a.block_table = block_table; a.seq_lens = seq_lens; a.plan = plan_dev;
     const int64_t rows = (int64_t)q_len * n_h;
+    if (plan->partial_dtype != MLA_DT_F32 && plan->partial_dtype != MLA_DT_BF16)
+        return fail(MLA_ERR_INVALID_ARG, "plan has a bad partial dtype");
     if (plan->num_partials > 0) {
-        const int64_t o_bytes = (int64_t)plan->num_partials * rows * cache->d_c * 4;
-        a.o_part = (float *)workspace;
+        const int64_t o_bytes = (int64_t)plan->num_partials * rows * cache->d_c *
+                                elem_bytes((mla_dtype_t)plan->partial_dtype);
+        a.o_part = workspace;
         a.lse_part = (float *)((char *)workspace + (o_bytes + 255) / 256 * 256);
     }
     a.o_lat = o_lat; a.lse = lse;
@@ -213,6 +217,7 @@ mla_status_t prepare_decode(const void *q_lat, const void *q_rope, mla_dtype_t q
     a.num_items = plan->num_items; a.row_chunks = plan->row_chunks;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q_dtype = q_dtype; a.kv_dtype = cache->kv_dtype;
+    a.partial_dtype = (mla_dtype_t)plan->partial_dtype;
     *out = a;
     return MLA_OK;
 }
@@ -228,16 +233,18 @@ mla_status_t finish_decode(const mla_plan_t *plan, const int32_t *plan_dev, void
                            mla_dtype_t out_dtype, void *o_lat, float *lse, hipStream_t s) {
     if (!plan->needs_combine) return ok();
     const int64_t rows = (int64_t)plan->q_len * plan->n_h;
-    float *o_part = nullptr, *lse_part = nullptr;
+    const mla_dtype_t pdt = (mla_dtype_t)plan->partial_dtype;
+    void *o_part = nullptr;
+    float *lse_part = nullptr;
     if (plan->num_partials > 0) {
-        const int64_t o_bytes = (int64_t)plan->num_partials * rows * plan->d_c * 4;
-        o_part = (float *)workspace;
+        const int64_t o_bytes = (int64_t)plan->num_partials * rows * plan->d_c * elem_bytes(pdt);
+        o_part = workspace;
         lse_part = (float *)((char *)workspace + (o_bytes + 255) / 256 * 256);
     }
     const int32_t *split_off = plan_dev + plan_split_off(plan->num_items);
     const int32_t *flags = plan_dev + plan_flags_off(plan->num_items, plan->B);
-    return hip_status(launch_combine(o_part, lse_part, split_off, flags, plan->B, (int32_t)rows,
-                                     plan->d_c, o_lat, out_dtype, lse, s),
+    return hip_status(launch_combine(o_part, pdt, lse_part, split_off, flags, plan->B,
+                                     (int32_t)rows, plan->d_c, o_lat, out_dtype, lse, s),
                       "combine launch");
 }
 
@@ -295,12 +302,14 @@ mla_status_t mla_combine_lse(const float *o_part, const float *lse_part,
                              int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dtype,
                              float *lse, mla_stream_t stream) {
     if (!split_off || !o_lat || !lse) return fail(MLA_ERR_INVALID_ARG, "NULL split_off/o_lat/lse");
-    if (B < 1 || rows < 1 || d_c < 1 || d_c > 4096)
-        return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d rows=%d d_c=%d", B, rows, d_c);
+    if (B < 1 || rows < 1 || d_c < 4 || d_c > 1024 || d_c % 4)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d rows=%d d_c=%d (d_c in [4,1024], multiple of 4)", B, rows, d_c);
+    if (!o_part || !lse_part) return fail(MLA_ERR_INVALID_ARG, "NULL o_part/lse_part");
+    if (!aligned(o_part, 16)) return fail(MLA_ERR_ALIGN, "o_part not 16-byte aligned");
     if (out_dtype != MLA_DT_F32 && out_dtype != MLA_DT_BF16)
         return fail(MLA_ERR_UNSUPPORTED, "out dtype %d unsupported", (int)out_dtype);
-    return hip_status(launch_combine(o_part, lse_part, split_off, seq_flags, B, rows, d_c, o_lat,
-                                     out_dtype, lse, (hipStream_t)stream),
+    return hip_status(launch_combine(o_part, MLA_DT_F32, lse_part, split_off, seq_flags, B, rows,
+                                     d_c, o_lat, out_dtype, lse, (hipStream_t)stream),
                       "combine launch");
 }
 

@@ -35,47 +35,108 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__
     }
 }
 
-// One workgroup per (sequence, 2 rows); 128 threads per row stride over d_c.
-template <typename OutT>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ o_part,
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// One wave per output row (sequence b, row r); 4 rows per workgroup.  The
+// split weights w_k = exp(lse_k - max) are computed once per row (lane k
+// holds split k), then each lane accumulates 4 consecutive features per
+// 256-feature stripe with 16-byte loads.  Requires d_c % 4 == 0, d_c <= 1024.
+template <typename PartT>
+__device__ __forceinline__ void load4(const PartT *p, float &a, float &b, float &c, float &d) {
+    if constexpr (sizeof(PartT) == 2) {
+        const uint2 v = *(const uint2 *)p;
+        a = __uint_as_float(v.x << 16);
+        b = __uint_as_float(v.x & 0xffff0000u);
+        c = __uint_as_float(v.y << 16);
+        d = __uint_as_float(v.y & 0xffff0000u);
+    } else {
+        const float4 v = *(const float4 *)p;
+        a = v.x; b = v.y; c = v.z; d = v.w;
+    }
+}
+
+template <typename PartT, typename OutT>
+__global__ __launch_bounds__(256) void combine_kernel(const PartT *__restrict__ o_part,
                                                       const float *__restrict__ lse_part,
                                                       const int32_t *__restrict__ split_off,
                                                       const int32_t *__restrict__ seq_flags,
                                                       int32_t rows, int32_t d_c,
                                                       OutT *__restrict__ o_lat,
                                                       float *__restrict__ lse) {
+    const int lane = threadIdx.x & 63;
     const int b = blockIdx.y;
-    const int r = blockIdx.x * 2 + (threadIdx.x >> 7);
-    const int tid = threadIdx.x & 127;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
     if (seq_flags && seq_flags[b] == 1) return;
-    const int k0 = split_off[b], k1 = split_off[b + 1];
+    const int k0 = split_off[b], n = split_off[b + 1] - k0;
     const int64_t out_row = (int64_t)b * rows + r;
+    // running max over all splits (in chunks of 64 lanes)
     float m = -INFINITY;
-    for (int k = k0; k < k1; ++k) m = fmaxf(m, lse_part[(int64_t)k * rows + r]);
+    for (int c = 0; c < n; c += 64)
+        if (c + lane < n) m = fmaxf(m, lse_part[(int64_t)(k0 + c + lane) * rows + r]);
+    m = wave_max(m);
     OutT *dst = o_lat + out_row * d_c;
     if (m == -INFINITY) {
-        for (int f = tid; f < d_c; f += 128) dst[f] = OutT(0);
-        if (tid == 0) lse[out_row] = -INFINITY;
+        for (int f = lane * 4; f < d_c; f += 256)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[f + j] = OutT(0);
+        if (lane == 0) lse[out_row] = -INFINITY;
         return;
     }
     float wsum = 0.f;
-    for (int k = k0; k < k1; ++k) wsum += expf(lse_part[(int64_t)k * rows + r] - m);
-    const float inv = 1.0f / wsum;
-    for (int f = tid; f < d_c; f += 128) {
-        float acc = 0.f;
-        for (int k = k0; k < k1; ++k) {
-            const float lk = lse_part[(int64_t)k * rows + r];
-            if (lk == -INFINITY) continue;
-            acc += expf(lk - m) * o_part[((int64_t)k * rows + r) * d_c + f];
+    float acc[16];   // d_c <= 1024: up to 4 stripes of 256 features, 4 per lane
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+    const int stripes = (d_c + 255) / 256;
+    for (int c = 0; c < n; c += 64) {
+        const float lk = c + lane < n ? lse_part[(int64_t)(k0 + c + lane) * rows + r] : -INFINITY;
+        const float wk = lk == -INFINITY ? 0.f : expf(lk - m);
+        wsum += wave_sum(wk);
+        const int cn = min(64, n - c);
+        for (int k = 0; k < cn; ++k) {
+            const float w = __shfl(wk, k, 64);
+            if (w == 0.f) continue;
+            const PartT *src = o_part + ((int64_t)(k0 + c + k) * rows + r) * d_c;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j >= stripes) break;
+                const int f = j * 256 + lane * 4;
+                if (f < d_c) {
+                    float v0, v1, v2, v3;
+                    load4(src + f, v0, v1, v2, v3);
+                    acc[4 * j + 0] += w * v0;
+                    acc[4 * j + 1] += w * v1;
+                    acc[4 * j + 2] += w * v2;
+                    acc[4 * j + 3] += w * v3;
+                }
+            }
         }
-        acc *= inv;
-        if constexpr (sizeof(OutT) == 2)
-            dst[f] = f32_to_bf16(acc);
-        else
-            dst[f] = acc;
     }
-    if (tid == 0) lse[out_row] = m + logf(wsum);
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int f = j * 256 + lane * 4;
+        if (j < stripes && f < d_c) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (sizeof(OutT) == 2)
+                    dst[f + e] = f32_to_bf16(acc[4 * j + e] * inv);
+                else
+                    dst[f + e] = acc[4 * j + e] * inv;
+            }
+        }
+    }
+    if (lane == 0) lse[out_row] = m + logf(wsum);
 }
 
 }  // namespace
@@ -90,16 +151,30 @@ hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int32_t c_byt
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const float *o_part, const float *lse_part, const int32_t *split_off,
-                          const int32_t *seq_flags, int32_t B, int32_t rows, int32_t d_c,
-                          void *o_lat, mla_dtype_t out_dt, float *lse, hipStream_t s) {
-    dim3 grid((rows + 1) / 2, B);
-    if (out_dt == MLA_DT_BF16)
-        hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, o_part, lse_part,
-                           split_off, seq_flags, rows, d_c, (uint16_t *)o_lat, lse);
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, o_part, lse_part,
-                           split_off, seq_flags, rows, d_c, (float *)o_lat, lse);
+hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *lse_part,
+                          const int32_t *split_off, const int32_t *seq_flags, int32_t B,
+                          int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dt, float *lse,
+                          hipStream_t s) {
+    dim3 grid((rows + 3) / 4, B);
+    if (part_dt == MLA_DT_BF16) {
+        if (out_dt == MLA_DT_BF16)
+            hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s,
+                               (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, d_c,
+                               (uint16_t *)o_lat, lse);
+        else
+            hipLaunchKernelGGL((combine_kernel<uint16_t, float>), grid, dim3(256), 0, s,
+                               (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, d_c,
+                               (float *)o_lat, lse);
+    } else {
+        if (out_dt == MLA_DT_BF16)
+            hipLaunchKernelGGL((combine_kernel<float, uint16_t>), grid, dim3(256), 0, s,
+                               (const float *)o_part, lse_part, split_off, seq_flags, rows, d_c,
+                               (uint16_t *)o_lat, lse);
+        else
+            hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(256), 0, s,
+                               (const float *)o_part, lse_part, split_off, seq_flags, rows, d_c,
+                               (float *)o_lat, lse);
+    }
     return hipGetLastError();
 }
 

@@ -84,8 +84,9 @@ def test_plan_covers_each_block_once(seq, q_len, cus):
     assert slots == set(range(info.num_partials))
     assert info.needs_combine == int(info.num_partials > 0 or 0 in seq)
     rows = q_len * 128
+    assert info.partial_dtype == L.DT_BF16          # MFMA shape: bf16 partials
     if info.num_partials:
-        assert info.workspace_bytes >= info.num_partials * rows * (512 + 1) * 4
+        assert info.workspace_bytes >= info.num_partials * rows * (512 * 2 + 4)
     else:
         assert info.workspace_bytes == 0
 
