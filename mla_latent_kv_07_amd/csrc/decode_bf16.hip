@@ -8,7 +8,7 @@
 //   - O^T, the fp32 latent output sum (512 x 32 rows, 256 accumulators).
 // Cached tokens stream through LDS in 32-token stages (half a paged block),
 // four stage buffers deep, filled by asynchronous direct-to-LDS loads that
-// run up to three stages ahead of the compute.  Every cached byte is read
+// run two stages ahead of the compute.  Every cached byte is read
 // from HBM once per workgroup and from LDS by all four waves:
 //   score  S^T[32 tok x 32 rows] = K[32 x 576] . Q^T           (MFMA 32x32x16)
 //   p      = exp2(S*scale*log2e - m) with a lazily raised reference max m
@@ -22,6 +22,8 @@
 // decomposition; absorbed query against the cached latent: §3-1; latent
 // value sum: §3-2; one shared latent "head" (MQA form): vLLM MLA page,
 // "MLA의 MQA 디코딩 경로".
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace mla {
@@ -89,17 +91,6 @@ __device__ __forceinline__ void issue_stage(const uint8_t *blk_base, int tok0, l
           (uint32_t)((tok0 + t) * ROW_BYTES + CB + (((lane & 7) ^ sr(t)) << 4)), blk_base);
 }
 
-// Wait until at most `ahead` later stages of this wave's copies are in flight.
-__device__ __forceinline__ void wait_stage(int ahead) {
-    static_assert(DMA_PER_STAGE == 9, "vmcnt immediates below assume 9 copies per stage");
-    if (ahead >= 2)
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if (ahead == 1)
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Loads of wave-uniform values (plan, block table, lengths) through the
 // constant address space become scalar loads, which never wait on the
 // vector-memory counter of the asynchronous stage copies.
@@ -151,7 +142,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     };
     auto stage_buf = [&](int st) { return smem + (st & (NSTAGE - 1)) * STAGE_BYTES; };
 
-    // stage 0 in flight, then the queries, then stages 1 and 2
+    // stage 0 in flight, then the queries, then stage 1
     issue_stage(stage_src(0), 0, stage_buf(0), wave, lane);
 
     bf16x8 qf[KC];
@@ -166,8 +157,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
         for (int ks = 0; ks < DR / 16; ++ks)
             *(bf16x8 *)(qrope + wrow * RB + (((2 * ks + g) ^ sr(wrow)) << 4)) = qr[2 * ks + g];
     }
-    for (int st = 1; st < 3 && st < nst_live; ++st)
-        issue_stage(stage_src(st), (st & 1) * HALF, stage_buf(st), wave, lane);
+    if (nst_live > 1) issue_stage(stage_src(1), HALF, stage_buf(1), wave, lane);
 
     f32x16 oacc[MBLOCKS];
 #pragma unroll
@@ -183,33 +173,64 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     int kbase[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) kbase[j] = ln * CB + (((2 * j) ^ x) << 4);
-    int rbase[DR / 16];
-#pragma unroll
-    for (int j = 0; j < DR / 16; ++j) rbase[j] = HALF * CB + ln * RB + (((2 * j + g) ^ sr(ln)) << 4);
-    int qrbase[DR / 16];
-#pragma unroll
-    for (int j = 0; j < DR / 16; ++j) qrbase[j] = wrow * RB + (((2 * j + g) ^ sr(wrow)) << 4);
+    const int rrow = HALF * CB + ln * RB, rx = g ^ sr(ln);        // rotary chunk 2j+g of token ln
+    const int qrrow = wrow * RB, qrx = g ^ sr(wrow);             // rotary query chunk 2j+g
     // Transposed value reads (ds_read_b64_tr_b16: lane i of each 16-lane group
-    // receives element i%4 of the 8 bytes read by lanes 4s + i/4, s = 0..3):
-    // lane (group G, index w) reads token 4(G/2) + w/4 (+8 for the upper half)
-    // of the k-step and features 32mb + 16(G%2) + 4(w%4): chunk
-    // 4mb + 2(G%2) + (w%4)/2, byte 8(w%2).  Bases depend on mb & 3 (the XOR
-    // touches the low 4 chunk bits); mb >> 2 adds 256 B, a k-step 16 KiB.
+    // receives element i%4 of the 8 bytes read by lanes 4s + i/4, s = 0..3).
+    // Value k-step s2 takes the tokens {8 s2 + 4g + (0..3)} and the same +16
+    // (score accumulator entries r = 4 s2 + (0..3) and 8 + 4 s2 + (0..3));
+    // lane (group G, index w) reads token 8 s2 + 4(G/2) + w/4 (+16 for the
+    // upper half) and features 32mb + 16(G%2) + 4(w%4): chunk
+    // 4mb + 2(G%2) + (w%4)/2, byte 8(w%2).  sc() repeats every 16 tokens, so
+    // the upper half is the lower address + 16 KiB.  Bases depend on mb & 3
+    // (the XOR touches the low 4 chunk bits); mb >> 2 adds 256 B.
     const int grp16 = lane >> 4, w16 = lane & 15;
     const int tr_tok = 4 * (grp16 >> 1) + (w16 >> 2);
     const int tr_chunk = 2 * (grp16 & 1) + ((w16 & 3) >> 1);
-    int vbase[2][4];
+    int vbase[2][4];   // [k-step][mb & 3]
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi)
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            vbase[hi][e] = (tr_tok + 8 * hi) * CB + (((4 * e + tr_chunk) ^ sc(tr_tok + 8 * hi)) << 4) +
+            vbase[s2][e] = (8 * s2 + tr_tok) * CB + (((4 * e + tr_chunk) ^ sc(8 * s2 + tr_tok)) << 4) +
                            (w16 & 1) * 8;
 
-    for (int st = 0; st < nst_live; ++st) {
-        // stage st landed (later stages may still be in flight) ...
-        wait_stage(min(2, nst_live - 1 - st));
-        __syncthreads();   // ... for every wave; stage st-1's buffer is free
+    // value MFMAs of one stage: O^T[512 x 32] += V^T[512 x 32 tok] . P^T[32 tok x 32]
+    // as two 16-token k-steps; transposed V fragments two MFMAs ahead.
+    auto value_stage = [&](lds_u8 *vst, const bf16x8 (&pv)[2], auto vpat_tag) {
+        constexpr int vpat = decltype(vpat_tag)::value;
+        auto vld = [&](int i) {
+            const int s2 = i / MBLOCKS, mb = i % MBLOCKS;
+            lds_u8 *lo = vst + vbase[s2][mb & 3] + 256 * (mb >> 2);
+            lds_u8 *hi = lo + 16 * CB;
+            bf16x8 vf;
+            vf.lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo));
+            vf.hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi));
+            return vf;
+        };
+        bf16x8 vb0 = vld(0), vb1 = vld(1), vb2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, vpat);
+#pragma unroll
+        for (int i = 0; i < 2 * MBLOCKS; ++i) {
+            if (i + 2 < 2 * MBLOCKS) vb2 = vld(i + 2);
+            oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb0, pv[i / MBLOCKS],
+                                                                        oacc[i % MBLOCKS], 0, 0, 0);
+            vb0 = vb1;
+            vb1 = vb2;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, vpat);
+            if (i + 2 < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, vpat);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, vpat);   // softmax VALU in the shadow
+        }
+    };
+
+    // One stage: wait for its copy, score it, softmax, value MFMAs.
+    auto stage = [&](int st) {
+        // stage st landed (stage st+1 may still be in flight) ...
+        if (st + 1 < nst_live)
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();   // ... for every wave; stage st-2's buffer is free
         lds_u8 *stg = stage_buf(st);
         const int p0 = p_first + st * HALF;
         const int valid = S - p0;   // >= 1 for a live stage
@@ -222,48 +243,75 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
                 *(uint4 *)(stg + off) = make_uint4(0, 0, 0, 0);
             __syncthreads();
         }
-        if (st + 3 < nst_live)
-            issue_stage(stage_src(st + 3), ((st + 3) & 1) * HALF, stage_buf(st + 3), wave, lane);
+        if (st + 2 < nst_live)
+            issue_stage(stage_src(st + 2), ((st + 2) & 1) * HALF, stage_buf(st + 2), wave, lane);
 
-        // ---- score: S^T[32 tokens x 32 rows]; K fragments two k-steps ahead
-        f32x16 sacc = {};
+        // ---- score: S^T[32 tokens x 32 rows]; K fragments two k-steps ahead.
+        // The score MFMAs are written as inline asm with VGPR operands: the
+        // compiler gives every MFMA builtin an AGPR accumulator, and the 256
+        // AGPRs are all taken by O^T.  Hazards the compiler cannot see are
+        // covered by hand: the chain accumulates back to back into the same
+        // registers (no wait states needed); s_nop 1 before each MFMA covers
+        // a VALU write of an operand; s_nop 15 after the last one covers the
+        // MFMA-result -> VALU-read latency (>= 12 wait states for 8 passes).
+        f32x16 sacc;
         auto kld = [&](int ks) {
             return ks < KC ? *(const bf16x8 *)(stg + kbase[ks & 7] + 256 * (ks >> 3))
-                           : *(const bf16x8 *)(stg + rbase[(ks - KC) & 3]);
+                           : *(const bf16x8 *)(stg + rrow + (((2 * ((ks - KC) & 3)) ^ rx) << 4));
         };
         auto qget = [&](int ks) {
-            return ks < KC ? qf[ks < KC ? ks : 0] : *(const bf16x8 *)(qrope + qrbase[(ks - KC) & 3]);
+            return ks < KC ? qf[ks < KC ? ks : 0]
+                           : *(const bf16x8 *)(qrope + qrrow + (((2 * ((ks - KC) & 3)) ^ qrx) << 4));
         };
         constexpr int KS = KC + DR / 16;   // 36
         bf16x8 kb0 = kld(0), kb1 = kld(1), kb2;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 2 < KS) kb2 = kld(ks + 2);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb0, qget(ks), sacc, 0, 0, 0);
+            const bf16x8 qv = qget(ks);
+            if (ks == 0)
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                             : "=v"(sacc) : "v"(kb0), "v"(qv));
+            else
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+v"(sacc) : "v"(kb0), "v"(qv));
             kb0 = kb1;
             kb1 = kb2;
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        asm volatile("s_nop 15" : "+v"(sacc));
 
-        // ---- online softmax; lane holds row ln, tokens 8(r/4)+4g+r%4
+        // ---- online softmax (lane holds row ln, tokens 8(r/4)+4g+r%4)
+        const int lim_rel = lim - p0 - 4 * g;   // token offset t is visible iff t < lim_rel
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int p = p0 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const float s = p < lim ? sacc[r] * a.scale_log2 : -INFINITY;
-            sacc[r] = s;
-            mx = fmaxf(mx, s);
+            const float sv = (8 * (r >> 2) + (r & 3)) < lim_rel ? sacc[r] : -INFINITY;
+            sacc[r] = sv;
+            mx = fmaxf(mx, sv);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx),
+                                                             false, false);
+            mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));   // max over lanes l, l^32
+        }
+        mx *= a.scale_log2;
         // raise the reference max only when a score exceeds it by 2^8
         const bool raise = mx > m_run + 8.0f;
         const float m_new = raise ? mx : m_run;
         const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        bf16x8 pcur[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, -m_ref));
+            psum += pv;
+            pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3)] = (__bf16)pv;
+        }
         if (__ballot(raise && m_run != -INFINITY)) {
-            // rare: keep the accumulators in AGPRs and rescale them block by
-            // block (a plain multiply makes the compiler move all 256 into VGPRs)
+            // rare: the value sum so far (through stage st-1) moves to the new
+            // reference; accumulators stay in AGPRs and are rescaled block by
+            // block (a plain multiply makes the compiler move all 256 to VGPRs)
 #pragma unroll
             for (int mb = 0; mb < MBLOCKS; ++mb) {
                 asm volatile("" : "+a"(oacc[mb]));
@@ -271,47 +319,21 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
                 asm volatile("" : "+a"(oacc[mb]));
             }
         }
-        l_lane *= alpha;
+        l_lane = l_lane * alpha + psum;
         m_run = m_new;
-        const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-        bf16x8 pf[2];
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(sacc[r] - m_ref);
-            psum += pv;
-            pf[r >> 3][r & 7] = (__bf16)pv;
-        }
-        l_lane += psum;
+        value_stage(stg, pcur, std::integral_constant<int, 1>{});
+    };
 
-        // ---- value: O^T[512 x 32] += V^T[512 x 16 tok] . P^T[16 tok x 32],
-        // two k-steps; transposed V fragments two MFMAs ahead
-        auto vld = [&](int i) {
-            const int s2 = i / MBLOCKS, mb = i % MBLOCKS;
-            lds_u8 *lo = stg + vbase[0][mb & 3] + s2 * 16 * CB + 256 * (mb >> 2);
-            lds_u8 *hi = stg + vbase[1][mb & 3] + s2 * 16 * CB + 256 * (mb >> 2);
-            bf16x8 vf;
-            vf.lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo));
-            vf.hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi));
-            return vf;
-        };
-        bf16x8 vb0 = vld(0), vb1 = vld(1), vb2;
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * MBLOCKS; ++i) {
-            if (i + 2 < 2 * MBLOCKS) vb2 = vld(i + 2);
-            oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb0, pf[i / MBLOCKS],
-                                                                        oacc[i % MBLOCKS], 0, 0, 0);
-            vb0 = vb1;
-            vb1 = vb2;
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i + 2 < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-    }
+    for (int st = 0; st < nst_live; ++st) stage(st);
 
     // ---- epilogue: O / l as bf16 rows staged through LDS, then 1 KiB
     // coalesced row stores (final o_lat, or this split's bf16 partial).
-    const float l_tot = l_lane + __shfl_xor(l_lane, 32, 64);
+    float l_tot;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(l_lane), __float_as_int(l_lane),
+                                                         false, false);
+        l_tot = __int_as_float(sw[0]) + __int_as_float(sw[1]);   // sum over lanes l, l^32
+    }
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
     __syncthreads();   // every wave is done with the stage buffers
