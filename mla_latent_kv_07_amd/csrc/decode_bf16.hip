@@ -46,6 +46,7 @@ constexpr int NSTAGE = 4;
 constexpr int KC = DC / 16;                     // 32 latent score k-steps
 constexpr int MBLOCKS = DC / 32;                // 16 value M-blocks
 constexpr int O_PITCH = CB + 16;                // epilogue staging row pitch (bytes)
+constexpr int PF = 4;                           // LDS fragment prefetch depth (MFMAs)
 
 // LDS layout of a stage: latent rows [32][1024 B] then rotary rows [32][128 B].
 // 16-byte chunk c of latent row t is stored at chunk c ^ sc(t) (the XOR stays
@@ -100,18 +101,17 @@ __device__ __forceinline__ int32_t sload(const int32_t *p, int64_t i) {
 
 __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_[NSTAGE * STAGE_BYTES];
-    // rotary part of the queries, [128 rows][128 B], chunk c of row r stored
-    // at chunk c ^ sr(r)
-    __shared__ __attribute__((aligned(1024))) uint8_t qrope_[kRowsPerChunk * RB];
     lds_u8 *smem = (lds_u8 *)smem_;
-    lds_u8 *qrope = (lds_u8 *)qrope_;
 
-    // workgroup -> (item, row chunk); the row chunks of one item sit 8 apart so
-    // that they land on the same XCD and share the stream through its L2.
+    // workgroup -> (item, row chunk).  Workgroups are dealt to the 8 XCDs
+    // round robin (XCD = blockIdx % 8); XCD x takes the contiguous run
+    // x*G .. x*G+G-1 of the (item, chunk) units, so the splits of a sequence
+    // and the row chunks of an item share one L2: the queries of a sequence
+    // and each streamed block are fetched from HBM once.
     const int rc = a.row_chunks;
-    const int grp = blockIdx.x / (8 * rc), within = blockIdx.x % (8 * rc);
-    const int chunk = within / 8;
-    const int item = grp * 8 + within % 8;
+    const int G = gridDim.x / 8;
+    const int unit = (blockIdx.x & 7) * G + (blockIdx.x >> 3);
+    const int item = unit / rc, chunk = unit % rc;
     if (item >= a.num_items) return;
     const int64_t io = plan_items_off() + 4 * item;
     const int b = sload(a.plan, io), blk0 = sload(a.plan, io + 1), blk1 = sload(a.plan, io + 2),
@@ -145,7 +145,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     // stage 0 in flight, then the queries, then stage 1
     issue_stage(stage_src(0), 0, stage_buf(0), wave, lane);
 
-    bf16x8 qf[KC];
+    constexpr int KS = KC + DR / 16;   // 36 score k-steps: 32 latent + 4 rotary
+    bf16x8 qf[KS];
     {
         // rows past the end load row 0's queries; their scores are all masked
         const int64_t qrow = row_ok ? grow : (int64_t)b * a.rows;
@@ -154,8 +155,13 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KC; ++ks) qf[ks] = ql[2 * ks + g];
 #pragma unroll
-        for (int ks = 0; ks < DR / 16; ++ks)
-            *(bf16x8 *)(qrope + wrow * RB + (((2 * ks + g) ^ sr(wrow)) << 4)) = qr[2 * ks + g];
+        for (int ks = 0; ks < DR / 16; ++ks) qf[KC + ks] = qr[2 * ks + g];
+        // Consume the query registers here so that the compiler completes
+        // these loads now (alongside stage 0's copy); otherwise it places
+        // vmcnt waits on them inside the stage loop, where the count would
+        // also drain the stage copies it does not know about.
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
     }
     if (nst_live > 1) issue_stage(stage_src(1), HALF, stage_buf(1), wave, lane);
 
@@ -174,7 +180,6 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) kbase[j] = ln * CB + (((2 * j) ^ x) << 4);
     const int rrow = HALF * CB + ln * RB, rx = g ^ sr(ln);        // rotary chunk 2j+g of token ln
-    const int qrrow = wrow * RB, qrx = g ^ sr(wrow);             // rotary query chunk 2j+g
     // Transposed value reads (ds_read_b64_tr_b16: lane i of each 16-lane group
     // receives element i%4 of the 8 bytes read by lanes 4s + i/4, s = 0..3).
     // Value k-step s2 takes the tokens {8 s2 + 4g + (0..3)} and the same +16
@@ -196,7 +201,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
                            (w16 & 1) * 8;
 
     // value MFMAs of one stage: O^T[512 x 32] += V^T[512 x 32 tok] . P^T[32 tok x 32]
-    // as two 16-token k-steps; transposed V fragments two MFMAs ahead.
+    // as two 16-token k-steps; transposed V fragments PF MFMAs ahead (LDS
+    // latency under load is ~4 MFMA issue slots).
     auto value_stage = [&](lds_u8 *vst, const bf16x8 (&pv)[2], auto vpat_tag) {
         constexpr int vpat = decltype(vpat_tag)::value;
         auto vld = [&](int i) {
@@ -208,18 +214,17 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
             vf.hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi));
             return vf;
         };
-        bf16x8 vb0 = vld(0), vb1 = vld(1), vb2;
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, vpat);
+        bf16x8 vb[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) vb[j] = vld(j);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, vpat);
 #pragma unroll
         for (int i = 0; i < 2 * MBLOCKS; ++i) {
-            if (i + 2 < 2 * MBLOCKS) vb2 = vld(i + 2);
-            oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb0, pv[i / MBLOCKS],
+            oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % PF], pv[i / MBLOCKS],
                                                                         oacc[i % MBLOCKS], 0, 0, 0);
-            vb0 = vb1;
-            vb1 = vb2;
+            if (i + PF < 2 * MBLOCKS) vb[i % PF] = vld(i + PF);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, vpat);
-            if (i + 2 < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, vpat);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, vpat);   // softmax VALU in the shadow
+            if (i + PF < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, vpat);
         }
     };
 
@@ -259,24 +264,20 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
             return ks < KC ? *(const bf16x8 *)(stg + kbase[ks & 7] + 256 * (ks >> 3))
                            : *(const bf16x8 *)(stg + rrow + (((2 * ((ks - KC) & 3)) ^ rx) << 4));
         };
-        auto qget = [&](int ks) {
-            return ks < KC ? qf[ks < KC ? ks : 0]
-                           : *(const bf16x8 *)(qrope + qrrow + (((2 * ((ks - KC) & 3)) ^ qrx) << 4));
-        };
-        constexpr int KS = KC + DR / 16;   // 36
-        bf16x8 kb0 = kld(0), kb1 = kld(1), kb2;
+        bf16x8 kb[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) kb[j] = kld(j);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 2 < KS) kb2 = kld(ks + 2);
-            const bf16x8 qv = qget(ks);
+            // the first MFMA writes the accumulator while reading its operands:
+            // early clobber keeps them apart
             if (ks == 0)
                 asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                             : "=v"(sacc) : "v"(kb0), "v"(qv));
+                             : "=&v"(sacc) : "v"(kb[0]), "v"(qf[0]));
             else
                 asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                             : "+v"(sacc) : "v"(kb0), "v"(qv));
-            kb0 = kb1;
-            kb1 = kb2;
+                             : "+v"(sacc) : "v"(kb[ks % PF]), "v"(qf[ks]));
+            if (ks + PF < KS) kb[ks % PF] = kld(ks + PF);
         }
         asm volatile("s_nop 15" : "+v"(sacc));
 
@@ -369,8 +370,9 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_bf16_mfma(const DecodeArgs &a, hipStream_t s) {
-    const int groups = (a.num_items + 7) / 8;
-    dim3 grid((unsigned)groups * 8 * a.row_chunks);
+    // a multiple of 8 workgroups, one per (item, row chunk) plus padding
+    const int units = a.num_items * a.row_chunks;
+    dim3 grid((unsigned)((units + 7) / 8) * 8);
     hipLaunchKernelGGL(decode_bf16_kernel, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }

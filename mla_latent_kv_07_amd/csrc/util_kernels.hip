@@ -139,6 +139,85 @@ __global__ __launch_bounds__(256) void combine_kernel(const PartT *__restrict__ 
     if (lane == 0) lse[out_row] = m + logf(wsum);
 }
 
+// Fast path for bf16 partials of 512 latent features (the MFMA decode's
+// split output): one wave per output row, lane owns features 8l..8l+7 (one
+// 16-byte load per split).  The partial rows of up to 8 splits are requested
+// before the split weights are known, so a row costs one memory round trip
+// per 8 splits instead of one per split.
+template <typename OutT>
+__global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restrict__ o_part,
+                                                         const float *__restrict__ lse_part,
+                                                         const int32_t *__restrict__ split_off,
+                                                         const int32_t *__restrict__ seq_flags,
+                                                         int32_t rows, OutT *__restrict__ o_lat,
+                                                         float *__restrict__ lse) {
+    constexpr int U = 8;
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.y;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    if (seq_flags && seq_flags[b] == 1) return;
+    const int k0 = split_off[b], n = split_off[b + 1] - k0;
+    const int64_t out_row = (int64_t)b * rows + r;
+    const uint16_t *src0 = o_part + ((int64_t)k0 * rows + r) * 512 + lane * 8;
+    const int64_t split_stride = (int64_t)rows * 512;
+
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        v[u] = u < n ? *(const uint4 *)(src0 + u * split_stride) : make_uint4(0, 0, 0, 0);
+    float m = -INFINITY;
+    for (int c = 0; c < n; c += 64)
+        if (c + lane < n) m = fmaxf(m, lse_part[(int64_t)(k0 + c + lane) * rows + r]);
+    m = wave_max(m);
+    uint4 *dst = (uint4 *)(o_lat + out_row * 512 + lane * 8);
+    if (m == -INFINITY) {
+        *dst = make_uint4(0, 0, 0, 0);
+        if constexpr (sizeof(OutT) == 4) dst[1] = make_uint4(0, 0, 0, 0);
+        if (lane == 0) lse[out_row] = -INFINITY;
+        return;
+    }
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float wsum = 0.f;
+    for (int c = 0; c < n; c += U) {
+        if (c > 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = c + u < n ? *(const uint4 *)(src0 + (c + u) * split_stride) : make_uint4(0, 0, 0, 0);
+        }
+        // lane u of the wave holds the weight of split c + u
+        const float lk = lane < U && c + lane < n ? lse_part[(int64_t)(k0 + c + lane) * rows + r] : -INFINITY;
+        const float wk = lk == -INFINITY ? 0.f : __expf(lk - m);
+        wsum += wave_sum(wk);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), u));
+            if (w == 0.f) continue;   // split without visible tokens (or past n)
+            const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += w * __uint_as_float(x[e] << 16);
+                acc[2 * e + 1] += w * __uint_as_float(x[e] & 0xffff0000u);
+            }
+        }
+    }
+    const float inv = 1.0f / wsum;
+    if constexpr (sizeof(OutT) == 2) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pk[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+        *dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+        float4 *d4 = (float4 *)dst;
+        d4[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        d4[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    }
+    if (lane == 0) lse[out_row] = m + __logf(wsum);
+}
+
 }  // namespace
 
 hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int32_t c_bytes,
@@ -156,7 +235,16 @@ hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *
                           int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dt, float *lse,
                           hipStream_t s) {
     dim3 grid((rows + 3) / 4, B);
-    if (part_dt == MLA_DT_BF16) {
+    if (part_dt == MLA_DT_BF16 && d_c == 512) {
+        if (out_dt == MLA_DT_BF16)
+            hipLaunchKernelGGL(combine512_kernel<uint16_t>, grid, dim3(256), 0, s,
+                               (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows,
+                               (uint16_t *)o_lat, lse);
+        else
+            hipLaunchKernelGGL(combine512_kernel<float>, grid, dim3(256), 0, s,
+                               (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows,
+                               (float *)o_lat, lse);
+    } else if (part_dt == MLA_DT_BF16) {
         if (out_dt == MLA_DT_BF16)
             hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s,
                                (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, d_c,
