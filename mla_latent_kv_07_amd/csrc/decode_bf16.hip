@@ -3,8 +3,7 @@
 //
 // Workgroup = 4 waves = 128 query rows (heads x query tokens) of one
 // sequence; wave w owns rows 32w..32w+31 for the whole work item and keeps
-//   - the latent part of its queries as MFMA B fragments in VGPRs
-//     (32 rows x 512, 128 VGPRs); the rotary part sits in LDS (16 KB),
+//   - its queries as MFMA B fragments in VGPRs (32 rows x 576, 144 VGPRs),
 //   - O^T, the fp32 latent output sum (512 x 32 rows, 256 accumulators).
 // Cached tokens stream through LDS in 32-token stages (half a paged block),
 // four stage buffers deep, filled by asynchronous direct-to-LDS loads that
@@ -15,8 +14,10 @@
 //   value  O^T[512 x 32] += V^T[512 x 32] . P^T[32 x 32]       (MFMA 32x32x16)
 // V is the latent part of the same LDS rows, read transposed with
 // ds_read_b64_tr_b16; the score accumulator layout is already the value
-// MFMA's B operand, up to a fixed permutation of the 16 tokens of a k-step
-// that both operands share, so P never moves between lanes.
+// MFMA's B operand, so P never moves between lanes.
+// The stage loop is software pipelined: while the matrix pipe runs the score
+// MFMAs of stage i+1, the same wave turns stage i's scores into
+// probabilities, one slice of the softmax after each MFMA.
 //
 // Score = content + rotary part: huny.dev "DeepSeek MLA 해부" §2-3
 // decomposition; absorbed query against the cached latent: §3-1; latent
@@ -41,25 +42,33 @@ constexpr int ROW_BYTES = (DC + DR) * 2;        // 1152 bytes per cached token i
 constexpr int CB = DC * 2;                      // 1024: latent bytes of a token
 constexpr int RB = DR * 2;                      // 128: rotary bytes of a token
 constexpr int HALF = 32;                        // tokens per pipeline stage
-constexpr int STAGE_BYTES = HALF * (CB + RB);   // 36864
+constexpr int LPITCH = CB + 16;                 // 1040: LDS pitch of a latent row
+constexpr int LAT_BYTES = HALF * LPITCH;        // 33280
+constexpr int STAGE_BYTES = LAT_BYTES + HALF * RB;   // 37376
 constexpr int NSTAGE = 4;
 constexpr int KC = DC / 16;                     // 32 latent score k-steps
+constexpr int KS = KC + DR / 16;                // 36 score k-steps
 constexpr int MBLOCKS = DC / 32;                // 16 value M-blocks
 constexpr int O_PITCH = CB + 16;                // epilogue staging row pitch (bytes)
-constexpr int PF = 4;                           // LDS fragment prefetch depth (MFMAs)
+constexpr int PF = 8;                           // value-fragment prefetch depth (MFMAs)
+constexpr int PFK = 3;                          // score-fragment prefetch depth (MFMAs)
+static_assert(NSTAGE * STAGE_BYTES <= 160 * 1024, "stage buffers exceed LDS");
+static_assert(4 * 32 * O_PITCH <= NSTAGE * STAGE_BYTES, "epilogue staging exceeds the stage buffers");
 
-// LDS layout of a stage: latent rows [32][1024 B] then rotary rows [32][128 B].
-// 16-byte chunk c of latent row t is stored at chunk c ^ sc(t) (the XOR stays
-// inside the 16-chunk / 256-byte group), rotary chunk c of row t at c ^ sr(t).
-// With 64 four-byte banks (256 B per cycle):
-//  - score reads (16 lanes = 16 consecutive tokens, one chunk) need sc to be
-//    a bijection on t mod 16;
-//  - transposed value reads (32 lanes = 4 consecutive tokens x 4 chunks of a
-//    4-chunk group) need sc >> 2 to be a bijection on t mod 4;
-//  - rotary reads (16 tokens, one chunk, 128-byte rows) need (t & 1, sr(t))
-//    distinct over 16 tokens.
-__device__ __forceinline__ int sc(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
-__device__ __forceinline__ int sr(int t) { return (t >> 1) & 7; }
+// LDS layout of a stage (slot t = token t of the stage):
+//   latent rows  [32][1040 B]: bytes 0..1023 of slot t = c of token t;
+//   rotary part  [4][8 chunks][8 tokens][16 B]: chunk c of token t at
+//                LAT_BYTES + (t >> 3) * 1024 + c * 128 + (t & 7) * 16.
+// Row i of the score MFMA (A-operand lane i) reads slot tok_of(i), where
+// i = 8a + 4h + e  ->  16 (a >> 1) + 4 e + 2 (a & 1) + h.
+// With 64 four-byte banks (256 B per cycle), the 16-byte pitch step makes
+// the 16 slots of a score read land in 16 distinct 16-byte bank groups, and
+// a transposed value read (32 lanes = 4 slots x 64 B) gets 4 slots spaced 4
+// apart, i.e. 64 B apart in bank space: every bank exactly once.  Every LDS
+// read is then a per-lane base plus a compile-time offset.
+__device__ __forceinline__ constexpr int tok_of(int i) {
+    return 16 * (i >> 4) + 4 * (i & 3) + 2 * ((i >> 3) & 1) + ((i >> 2) & 1);
+}
 
 // One asynchronous 1 KiB copy: global_load_lds_dwordx4 writes lane i's 16
 // bytes to LDS at M0 + 16 i.  Issued as inline asm so that the compiler's
@@ -68,28 +77,27 @@ __device__ __forceinline__ int sr(int t) { return (t >> 1) & 7; }
 // (vmcnt + barrier) before a stage is read.  VMEM loads complete in order, so
 // the compiler's own vmcnt waits stay correct: unseen extra loads can only
 // make them over-wait.
-__device__ __forceinline__ void dma16(lds_u8 *lds_dst, uint32_t voff, const uint8_t *src) {
-    const uint32_t lds = (uint32_t)(uintptr_t)lds_dst;
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const uint8_t *src) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(src)
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(src)
                  : "memory", "m0");
 }
 
-constexpr int DMA_PER_STAGE = 9;   // per wave: 8 latent rows + 1 KiB of rotary rows
+constexpr int DMA_PER_STAGE = 9;   // per wave: 8 latent rows + 1 KiB of rotary parts
 
-// Copy one stage (32 tokens starting at token tok0 of the block at blk_base).
-// Wave w copies latent rows 8w..8w+7 (one instruction each) and the rotary
-// rows of the same 8 tokens (one instruction).
-__device__ __forceinline__ void issue_stage(const uint8_t *blk_base, int tok0, lds_u8 *stage,
-                                            int wave, int lane) {
+// Copy one stage whose first token is at src0 (token row pointer in HBM).
+// Wave w copies latent rows 8w..8w+7 (one 1 KiB instruction each; lane i
+// reads bytes 16i..16i+15, voff = l16 = 16 i) and the rotary parts of the same
+// 8 tokens (one instruction; lane i = 8c + u reads chunk c of token 8w + u,
+// voff = rot_off).
+__device__ __forceinline__ void issue_stage(const uint8_t *src0, uint32_t stage_lds, int wave,
+                                            uint32_t l16, uint32_t rot_off) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int t = wave * 8 + k;
-        dma16(stage + t * CB, (uint32_t)((tok0 + t) * ROW_BYTES + ((lane ^ sc(t)) << 4)), blk_base);
+        dma16(stage_lds + t * LPITCH, l16, src0 + t * ROW_BYTES);
     }
-    const int t = wave * 8 + (lane >> 3);
-    dma16(stage + HALF * CB + wave * 8 * RB,
-          (uint32_t)((tok0 + t) * ROW_BYTES + CB + (((lane & 7) ^ sr(t)) << 4)), blk_base);
+    dma16(stage_lds + LAT_BYTES + wave * 1024, rot_off, src0);
 }
 
 // Loads of wave-uniform values (plan, block table, lengths) through the
@@ -99,9 +107,11 @@ __device__ __forceinline__ int32_t sload(const int32_t *p, int64_t i) {
     return ((const __attribute__((address_space(4))) int32_t *)p)[i];
 }
 
+
 __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_[NSTAGE * STAGE_BYTES];
     lds_u8 *smem = (lds_u8 *)smem_;
+    const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
     // workgroup -> (item, row chunk).  Workgroups are dealt to the 8 XCDs
     // round robin (XCD = blockIdx % 8); XCD x takes the contiguous run
@@ -123,7 +133,9 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     const int p_first = blk0 * kBlock;
     const int nst_live = min(nst, (S - p_first + HALF - 1) / HALF);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave index as a wave-uniform (scalar) value: the stage copies use it in
+    // their scalar source pointers and LDS destinations
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 5;           // lane half
     const int ln = lane & 31;
     const int wrow = wave * 32 + ln;   // row inside the chunk
@@ -135,35 +147,55 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     const uint8_t *pool = (const uint8_t *)a.pool;
     const int64_t bt_row = (int64_t)b * a.bt_stride;
     const int64_t num_blocks = a.num_pool_blocks;
-    auto stage_src = [&](int st) {
+    auto stage_src = [&](int st) {   // HBM row of the stage's first token
         int64_t id = sload(a.block_table, bt_row + blk0 + (st >> 1));
         id = id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
-        return pool + id * (int64_t)(kBlock * ROW_BYTES);
+        return pool + id * (int64_t)(kBlock * ROW_BYTES) + (st & 1) * HALF * ROW_BYTES;
     };
-    auto stage_buf = [&](int st) { return smem + (st & (NSTAGE - 1)) * STAGE_BYTES; };
+    auto stage_off = [&](int st) { return (uint32_t)((st & (NSTAGE - 1)) * STAGE_BYTES); };
+    const uint32_t l16 = lane << 4;
+    const uint32_t rot_off = (uint32_t)((wave * 8 + (lane & 7)) * ROW_BYTES + CB + 16 * (lane >> 3));
+    auto issue = [&](int st) { issue_stage(stage_src(st), smem_addr + stage_off(st), wave, l16, rot_off); };
 
-    // stage 0 in flight, then the queries, then stage 1
-    issue_stage(stage_src(0), 0, stage_buf(0), wave, lane);
-
-    constexpr int KS = KC + DR / 16;   // 36 score k-steps: 32 latent + 4 rotary
+    // ---- queries -> VGPRs (MFMA B fragments: lane (ln, g) holds, for k-step
+    // ks, bytes 32 ks + 16 g .. +15 of row ln's 1152).  Each wave copies its 32
+    // rows into its own 36 KiB region of the not yet used stage buffers with
+    // coalesced 1 KiB copies: latent row r with its 16-byte chunks XOR-swizzled
+    // by r & 15 (lane i fetches chunk i ^ (r & 15)), so that 16 rows reading
+    // one chunk hit 16 distinct bank groups; the rotary parts as
+    // [r >> 3][chunk][r & 7].  Rows past the end of the sequence's rows read
+    // its last row (their scores are masked).
     bf16x8 qf[KS];
     {
-        // rows past the end load row 0's queries; their scores are all masked
-        const int64_t qrow = row_ok ? grow : (int64_t)b * a.rows;
-        const bf16x8 *ql = (const bf16x8 *)((const uint16_t *)a.q_lat + qrow * DC);
-        const bf16x8 *qr = (const bf16x8 *)((const uint16_t *)a.q_rope + qrow * DR);
+        const uint32_t qreg = smem_addr + wave * 36864;
+        const int row_base = chunk * kRowsPerChunk + wave * 32;   // first row of this wave
+        const int64_t seq_row0 = (int64_t)b * a.rows;
+        const uint8_t *qlat = (const uint8_t *)a.q_lat + seq_row0 * CB;
+        const uint8_t *qrope = (const uint8_t *)a.q_rope + seq_row0 * RB;
 #pragma unroll
-        for (int ks = 0; ks < KC; ++ks) qf[ks] = ql[2 * ks + g];
+        for (int r = 0; r < 32; ++r) {
+            const int rr = min(row_base + r, a.rows - 1);
+            dma16(qreg + r * CB, l16 ^ (uint32_t)((r & 15) << 4), qlat + (int64_t)rr * CB);
+        }
 #pragma unroll
-        for (int ks = 0; ks < DR / 16; ++ks) qf[KC + ks] = qr[2 * ks + g];
-        // Consume the query registers here so that the compiler completes
-        // these loads now (alongside stage 0's copy); otherwise it places
-        // vmcnt waits on them inside the stage loop, where the count would
-        // also drain the stage copies it does not know about.
+        for (int q = 0; q < 4; ++q) {
+            // lane i = 8 c + u: chunk c of row 8 q + u
+            const int rr = min(row_base + 8 * q + (lane & 7), a.rows - 1);
+            dma16(qreg + 32 * CB + q * 1024, (uint32_t)(rr * RB + 16 * (lane >> 3)), qrope);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies are in LDS
+        lds_u8 *qw = smem + wave * 36864;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+        for (int ks = 0; ks < KC; ++ks)
+            qf[ks] = *(const bf16x8 *)(qw + ln * CB + (((2 * ks + g) ^ (ln & 15)) << 4));
+#pragma unroll
+        for (int j = 0; j < DR / 16; ++j)
+            qf[KC + j] = *(const bf16x8 *)(qw + 32 * CB + (ln >> 3) * 1024 + (2 * j + g) * 128 + (ln & 7) * 16);
     }
-    if (nst_live > 1) issue_stage(stage_src(1), HALF, stage_buf(1), wave, lane);
+    __syncthreads();   // every wave holds its queries: the stage buffers are free
+    issue(0);
+    if (nst_live > 1) issue(1);
+    if (nst_live > 2) issue(2);
 
     f32x16 oacc[MBLOCKS];
 #pragma unroll
@@ -171,144 +203,176 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     float m_run = -INFINITY;   // reference max (log2 units), lazily raised
     float l_lane = 0.f;        // this lane's share of the softmax denominator
 
-    // Per-lane LDS read bases; every read is base + stage offset + a
-    // compile-time immediate.
-    // Score, latent chunk 2ks+g of token ln: (2ks+g) ^ sc(ln) = 2ks ^ x with
-    // x = g ^ sc(ln), so the base depends on ks & 7 and ks >> 3 adds 256 B.
-    const int x = g ^ sc(ln);
-    int kbase[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) kbase[j] = ln * CB + (((2 * j) ^ x) << 4);
-    const int rrow = HALF * CB + ln * RB, rx = g ^ sr(ln);        // rotary chunk 2j+g of token ln
-    // Transposed value reads (ds_read_b64_tr_b16: lane i of each 16-lane group
-    // receives element i%4 of the 8 bytes read by lanes 4s + i/4, s = 0..3).
-    // Value k-step s2 takes the tokens {8 s2 + 4g + (0..3)} and the same +16
-    // (score accumulator entries r = 4 s2 + (0..3) and 8 + 4 s2 + (0..3));
-    // lane (group G, index w) reads token 8 s2 + 4(G/2) + w/4 (+16 for the
-    // upper half) and features 32mb + 16(G%2) + 4(w%4): chunk
-    // 4mb + 2(G%2) + (w%4)/2, byte 8(w%2).  sc() repeats every 16 tokens, so
-    // the upper half is the lower address + 16 KiB.  Bases depend on mb & 3
-    // (the XOR touches the low 4 chunk bits); mb >> 2 adds 256 B.
+    // Per-lane LDS read bases (a stage offset is added once per stage; every
+    // read adds a compile-time offset).
+    //  score, latent k-step ks: slot tok_of(ln), chunk 2 ks + g -> kb0 + 32 ks
+    //  score, rotary k-step KC + j: chunk 2 j + g of slot tok_of(ln) -> rb0 + 256 j
+    //  value (ds_read_b64_tr_b16: lane i of each 16-lane group receives element
+    //  i % 4 of the 8 bytes read by lane 4s + i/4, s = 0..3): k-step s2 needs,
+    //  for lane half g, the tokens tok_of(8 s2 + 4 g + e) = 4 e + 2 s2 + g and,
+    //  for the upper 8 k, 16 + the same; lane (group G, index w) reads slot
+    //  4 (w >> 2) + 2 s2 + (G >> 1) (+16), features 32 mb + 16 (G & 1) + 4 (w & 3)
+    //  -> vb0 + 2 LPITCH s2 + 64 mb (+ 16 LPITCH).
+    const int tq = tok_of(ln);
+    const uint32_t kb0 = tq * LPITCH + 16 * g;
+    const uint32_t rb0 = LAT_BYTES + (tq >> 3) * 1024 + 128 * g + (tq & 7) * 16;
     const int grp16 = lane >> 4, w16 = lane & 15;
-    const int tr_tok = 4 * (grp16 >> 1) + (w16 >> 2);
-    const int tr_chunk = 2 * (grp16 & 1) + ((w16 & 3) >> 1);
-    int vbase[2][4];   // [k-step][mb & 3]
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            vbase[s2][e] = (8 * s2 + tr_tok) * CB + (((4 * e + tr_chunk) ^ sc(8 * s2 + tr_tok)) << 4) +
-                           (w16 & 1) * 8;
+    const uint32_t vb0 = (4 * (w16 >> 2) + (grp16 >> 1)) * LPITCH + 32 * (grp16 & 1) + 8 * (w16 & 3);
 
-    // value MFMAs of one stage: O^T[512 x 32] += V^T[512 x 32 tok] . P^T[32 tok x 32]
-    // as two 16-token k-steps; transposed V fragments PF MFMAs ahead (LDS
-    // latency under load is ~4 MFMA issue slots).
-    auto value_stage = [&](lds_u8 *vst, const bf16x8 (&pv)[2], auto vpat_tag) {
-        constexpr int vpat = decltype(vpat_tag)::value;
-        auto vld = [&](int i) {
-            const int s2 = i / MBLOCKS, mb = i % MBLOCKS;
-            lds_u8 *lo = vst + vbase[s2][mb & 3] + 256 * (mb >> 2);
-            lds_u8 *hi = lo + 16 * CB;
-            bf16x8 vf;
-            vf.lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo));
-            vf.hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi));
-            return vf;
-        };
-        bf16x8 vb[PF];
-#pragma unroll
-        for (int j = 0; j < PF; ++j) vb[j] = vld(j);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, vpat);
-#pragma unroll
-        for (int i = 0; i < 2 * MBLOCKS; ++i) {
-            oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % PF], pv[i / MBLOCKS],
-                                                                        oacc[i % MBLOCKS], 0, 0, 0);
-            if (i + PF < 2 * MBLOCKS) vb[i % PF] = vld(i + PF);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, vpat);
-            if (i + PF < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, vpat);
+    auto kld = [&](uint32_t kbs, uint32_t rbs, int ks) {
+        return ks < KC ? *(const bf16x8 *)(smem + kbs + 32 * ks)
+                       : *(const bf16x8 *)(smem + rbs + 256 * (ks - KC));
+    };
+    auto vld = [&](uint32_t vbs, int i) {
+        const int s2 = i / MBLOCKS, mb = i % MBLOCKS;
+        lds_u8 *lo = smem + vbs + 2 * LPITCH * s2 + 64 * mb;
+        bf16x8 vf;
+        vf.lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo));
+        vf.hi = __builtin_bit_cast(bf16x4,
+                                   __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lo + 16 * LPITCH)));
+        return vf;
+    };
+
+    // ---- score MFMAs: S^T[32 tokens x 32 rows] += K[32 x 16] . Q^T[16 x 32].
+    // Written as inline asm with VGPR operands: the compiler gives every MFMA
+    // builtin an AGPR accumulator, and the 256 AGPRs are all taken by O^T.
+    // Hazards the compiler cannot see are covered by hand: the chain
+    // accumulates back to back into the same registers (no wait states
+    // needed); s_nop 1 before each MFMA covers a VALU write of an operand; an
+    // s_nop 15 after the chain covers the MFMA-result -> VALU-read latency
+    // (>= 10 wait states for an 8-pass MFMA).
+    auto score_mfma = [&](f32x16 &acc, const bf16x8 &kf, int ks) {
+        // the first MFMA writes the accumulator while reading its operands:
+        // early clobber keeps them apart
+        if (ks == 0)
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                         : "=&v"(acc) : "v"(kf), "v"(qf[0]));
+        else
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+v"(acc) : "v"(kf), "v"(qf[ks]));
+    };
+
+    // Rows past the sequence end in a partial stage are zeroed in LDS so that
+    // P = 0 never meets NaN or stale data in the value MFMA (their scores are
+    // masked to -inf, so the score MFMA may read either).
+    auto zero_tail = [&](int st) {
+        const int valid = S - (p_first + st * HALF);   // >= 1 for a live stage
+        if (valid < HALF) {
+            lds_u8 *stg = smem + stage_off(st);
+            for (int idx = threadIdx.x; idx < (HALF - valid) * 64; idx += 256)
+                *(uint4 *)(stg + (valid + (idx >> 6)) * LPITCH + (idx & 63) * 16) = make_uint4(0, 0, 0, 0);
+            for (int idx = threadIdx.x; idx < (HALF - valid) * 8; idx += 256) {
+                const int t = valid + (idx >> 3), c = idx & 7;
+                *(uint4 *)(stg + LAT_BYTES + (t >> 3) * 1024 + c * 128 + (t & 7) * 16) = make_uint4(0, 0, 0, 0);
+            }
         }
     };
 
-    // One stage: wait for its copy, score it, softmax, value MFMAs.
-    auto stage = [&](int st) {
-        // stage st landed (stage st+1 may still be in flight) ...
-        if (st + 1 < nst_live)
-            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();   // ... for every wave; stage st-2's buffer is free
-        lds_u8 *stg = stage_buf(st);
-        const int p0 = p_first + st * HALF;
-        const int valid = S - p0;   // >= 1 for a live stage
-        if (valid < HALF) {
-            // zero the rows past the sequence end so that P = 0 never meets
-            // NaN or stale data in the value MFMA
-            for (int off = valid * CB + threadIdx.x * 16; off < HALF * CB; off += 256 * 16)
-                *(uint4 *)(stg + off) = make_uint4(0, 0, 0, 0);
-            for (int off = HALF * CB + valid * RB + threadIdx.x * 16; off < STAGE_BYTES; off += 256 * 16)
-                *(uint4 *)(stg + off) = make_uint4(0, 0, 0, 0);
-            __syncthreads();
-        }
-        if (st + 2 < nst_live)
-            issue_stage(stage_src(st + 2), ((st + 2) & 1) * HALF, stage_buf(st + 2), wave, lane);
-
-        // ---- score: S^T[32 tokens x 32 rows]; K fragments two k-steps ahead.
-        // The score MFMAs are written as inline asm with VGPR operands: the
-        // compiler gives every MFMA builtin an AGPR accumulator, and the 256
-        // AGPRs are all taken by O^T.  Hazards the compiler cannot see are
-        // covered by hand: the chain accumulates back to back into the same
-        // registers (no wait states needed); s_nop 1 before each MFMA covers
-        // a VALU write of an operand; s_nop 15 after the last one covers the
-        // MFMA-result -> VALU-read latency (>= 12 wait states for 8 passes).
-        f32x16 sacc;
-        auto kld = [&](int ks) {
-            return ks < KC ? *(const bf16x8 *)(stg + kbase[ks & 7] + 256 * (ks >> 3))
-                           : *(const bf16x8 *)(stg + rrow + (((2 * ((ks - KC) & 3)) ^ rx) << 4));
-        };
-        bf16x8 kb[PF];
+    // ---- prologue: score of stage 0 (wait for this wave's copy of stage 0;
+    // the barrier makes every wave's copies visible)
+    if (nst_live > 2)
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (nst_live > 1)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    zero_tail(0);
+    f32x16 sA, sB;
+    {
+        const uint32_t kbs = kb0 + stage_off(0), rbs = rb0 + stage_off(0);
+        bf16x8 kb[PFK];
 #pragma unroll
-        for (int j = 0; j < PF; ++j) kb[j] = kld(j);
+        for (int j = 0; j < PFK; ++j) kb[j] = kld(kbs, rbs, j);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            // the first MFMA writes the accumulator while reading its operands:
-            // early clobber keeps them apart
-            if (ks == 0)
-                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                             : "=&v"(sacc) : "v"(kb[0]), "v"(qf[0]));
-            else
-                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                             : "+v"(sacc) : "v"(kb[ks % PF]), "v"(qf[ks]));
-            if (ks + PF < KS) kb[ks % PF] = kld(ks + PF);
+            score_mfma(sA, kb[ks % PFK], ks);
+            if (ks + PFK < KS) kb[ks % PFK] = kld(kbs, rbs, ks + PFK);
         }
-        asm volatile("s_nop 15" : "+v"(sacc));
+        asm volatile("s_nop 15" : "+v"(sA));
+    }
 
-        // ---- online softmax (lane holds row ln, tokens 8(r/4)+4g+r%4)
-        const int lim_rel = lim - p0 - 4 * g;   // token offset t is visible iff t < lim_rel
-        float mx = -INFINITY;
+    // ---- one pipelined iteration: scores of stage st (cur, complete) become
+    // probabilities while stage st+1's score MFMAs fill nxt; then stage st's
+    // value MFMAs.
+    auto iteration = [&](int st, f32x16 &cur, f32x16 &nxt) {
+        const bool has_next = st + 1 < nst_live;
+        if (has_next) {
+            // stage st+1 landed for this wave (stage st+2 may be in flight)
+            if (st + 2 < nst_live)
+                asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        // every wave's copy of stage st+1 is visible, and every wave has
+        // finished iteration st-1, so stage st-1's buffer may be refilled
+        __syncthreads();
+        if (st + 3 < nst_live) issue(st + 3);
+        if (has_next) zero_tail(st + 1);
+        const uint32_t kbs = kb0 + stage_off(st + 1), rbs = rb0 + stage_off(st + 1);
+        bf16x8 kb[PFK];
+        if (has_next) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float sv = (8 * (r >> 2) + (r & 3)) < lim_rel ? sacc[r] : -INFINITY;
-            sacc[r] = sv;
-            mx = fmaxf(mx, sv);
+            for (int j = 0; j < PFK; ++j) kb[j] = kld(kbs, rbs, j);
         }
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx),
-                                                             false, false);
-            mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));   // max over lanes l, l^32
+
+        // mask: entry r of lane half g is token tok_of(8 (r >> 2) + 4 g + (r & 3))
+        // = 16 (r >> 3) + 4 (r & 3) + 2 ((r >> 2) & 1) + g of the stage, visible
+        // iff < lim - p0 (only the last stage of a sequence, causal query pairs
+        // and rows past the end need it)
+        const int lim_rel = lim - (p_first + st * HALF) - g;
+        if (__ballot(lim_rel < HALF - 1)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                cur[r] = (16 * (r >> 3) + 4 * (r & 3) + 2 * ((r >> 2) & 1)) < lim_rel ? cur[r] : -INFINITY;
         }
-        mx *= a.scale_log2;
-        // raise the reference max only when a score exceeds it by 2^8
-        const bool raise = mx > m_run + 8.0f;
-        const float m_new = raise ? mx : m_run;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+
+        float mx = -INFINITY, m_new = m_run, m_ref = 0.f, alpha = 1.f, psum = 0.f;
+        bool raise = false;
         bf16x8 pcur[2];
-        float psum = 0.f;
+        bf16x8 vb[PF];
+        // Slice k of the softmax of stage st.  Each slice holds at most three
+        // independent VALU ops; the exp2 pipeline is skewed (fma of entry r,
+        // exp2 of r-1 and the sum of r-2 in one slice) so no slice waits on
+        // its own results.
+        auto softmax_slice = [&](int k) {
+            if (k < 8) {
+                mx = __builtin_fmaxf(mx, __builtin_fmaxf(cur[2 * k], cur[2 * k + 1]));
+            } else if (k == 8) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx),
+                                                                 false, false);
+                mx = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1])) * a.scale_log2;
+                // raise the reference max only when a score exceeds it by 2^8
+                raise = mx > m_run + 8.0f;
+                m_new = raise ? mx : m_run;
+                m_ref = m_new == -INFINITY ? 0.f : m_new;
+            } else if (k < 28) {
+                if (k == 9) alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+                const int r = k - 10;
+                if (r >= 2 && r < 18) psum += cur[r - 2];
+                if (r >= 1 && r < 17) cur[r - 1] = __builtin_amdgcn_exp2f(cur[r - 1]);
+                if (r >= 0 && r < 16) cur[r] = __builtin_fmaf(cur[r], a.scale_log2, -m_ref);
+            } else {
+                const int r = 2 * (k - 28);   // entries r, r+1 -> one packed pair of P
+                pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3)] = (__bf16)cur[r];
+                pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3) + 1] = (__bf16)cur[r + 1];
+            }
+        };
+
+        if (has_next) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, -m_ref));
-            psum += pv;
-            pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3)] = (__bf16)pv;
+            for (int ks = 0; ks < KS; ++ks) {
+                score_mfma(nxt, kb[ks % PFK], ks);
+                if (ks + PFK < KS) kb[ks % PFK] = kld(kbs, rbs, ks + PFK);
+                softmax_slice(ks);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            asm volatile("s_nop 15" : "+v"(nxt));
+        } else {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) softmax_slice(k);
         }
+
         if (__ballot(raise && m_run != -INFINITY)) {
             // rare: the value sum so far (through stage st-1) moves to the new
             // reference; accumulators stay in AGPRs and are rescaled block by
@@ -322,10 +386,29 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
         }
         l_lane = l_lane * alpha + psum;
         m_run = m_new;
-        value_stage(stg, pcur, std::integral_constant<int, 1>{});
+
+        // value MFMAs: O^T[512 x 32] += V^T[512 x 32 tok] . P^T[32 tok x 32]
+        // as two 16-token k-steps, V fragments PF MFMAs ahead
+        const uint32_t vbs = vb0 + stage_off(st);
+#pragma unroll
+        for (int j = 0; j < PF; ++j) vb[j] = vld(vbs, j);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);   // the prefetch reads first
+#pragma unroll
+        for (int i = 0; i < 2 * MBLOCKS; ++i) {
+            oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % PF], pcur[i / MBLOCKS],
+                                                                        oacc[i % MBLOCKS], 0, 0, 0);
+            if (i + PF < 2 * MBLOCKS) vb[i % PF] = vld(vbs, i + PF);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i + PF < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
     };
 
-    for (int st = 0; st < nst_live; ++st) stage(st);
+    // two iterations per trip so that the score accumulators swap roles
+    // without register copies
+    for (int st = 0; st < nst_live; st += 2) {
+        iteration(st, sA, sB);
+        if (st + 1 < nst_live) iteration(st + 1, sB, sA);
+    }
 
     // ---- epilogue: O / l as bf16 rows staged through LDS, then 1 KiB
     // coalesced row stores (final o_lat, or this split's bf16 partial).
