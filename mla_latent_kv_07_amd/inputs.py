@@ -146,8 +146,48 @@ def draw_seq_lens(wl: Workload, g: torch.Generator) -> torch.Tensor:
     return torch.tensor(wl.seq_lens, dtype=torch.int32)
 
 
+# Draws of more than this many values come from NumPy PCG64 streams seeded
+# with one 63-bit integer drawn from the workload's torch generator (one draw
+# of the generator per tensor, as for small tensors).  The values are filled
+# in fixed chunks of _CHUNK, chunk i from the seeded stream jumped i times,
+# on a thread pool: the result does not depend on the thread count, and the
+# multi-gigabyte caches of the long-context and full-layer workloads take
+# seconds instead of minutes.
+_BIG_DRAW = 1 << 20
+_CHUNK = 1 << 24
+
+
 def _normal(shape, g, std=1.0):
-    return torch.randn(shape, generator=g, dtype=torch.float32) * std
+    n = math.prod(shape)
+    if n <= _BIG_DRAW:
+        return torch.randn(shape, generator=g, dtype=torch.float32) * std
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    seed = int(torch.randint(0, 2 ** 63 - 1, (1,), generator=g, dtype=torch.int64))
+    out = np.empty(n, dtype=np.float32)
+    base = np.random.PCG64(seed)
+
+    def fill(i):
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        np.random.Generator(base.jumped(i)).standard_normal(out=out[lo:hi], dtype=np.float32)
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range((n + _CHUNK - 1) // _CHUNK)))
+    t = torch.from_numpy(out).view(shape)
+    return t * std if std != 1.0 else t
+
+
+def _normal(shape, g, std=1.0):
+    n = math.prod(shape)
+    if n <= _BIG_DRAW:
+        return torch.randn(shape, generator=g, dtype=torch.float32) * std
+    import numpy as np
+    seed = int(torch.randint(0, 2 ** 63 - 1, (1,), generator=g, dtype=torch.int64))
+    x = np.random.Generator(np.random.PCG64(seed)).standard_normal(n, dtype=np.float32)
+    t = torch.from_numpy(x).view(shape)
+    return t * std if std != 1.0 else t
 
 
 def draw_layer_weights(wl: Workload, g: torch.Generator) -> dict:
@@ -203,8 +243,11 @@ def page_cache(wl: Workload, g: torch.Generator, seq_lens: torch.Tensor,
     max_blocks = max(1, int(nblk.max()) if len(nblk) else 1)
     perm = torch.randperm(num_blocks, generator=g)
 
-    # logical [total][64][d_c + d_r] fp32, NaN past each sequence's end
-    logical = torch.full((total, BLOCK, d_c + d_r), float("nan"), dtype=torch.float32)
+    # logical [total][64][d_c + d_r], NaN past each sequence's end; staged in
+    # the storage dtype for f32/bf16 (rounding each value once, as a cast of
+    # the whole block would), in fp32 for fp8 (the block scale needs it)
+    stage_dt = _TORCH_DT.get(wl.kv_dtype, torch.float32)
+    logical = torch.full((total, BLOCK, d_c + d_r), float("nan"), dtype=stage_dt)
     flat = logical.view(total * BLOCK, d_c + d_r)
     src = 0
     dst_blk = 0
@@ -220,9 +263,9 @@ def page_cache(wl: Workload, g: torch.Generator, seq_lens: torch.Tensor,
     bt[:] = int(spare_ids[0])  # unused entries point at a NaN-filled spare block
     k = 0
     for b in range(wl.B):
-        for j in range(int(nblk[b])):
-            bt[b, j] = int(perm[k])
-            k += 1
+        n = int(nblk[b])
+        bt[b, :n] = perm[k:k + n].to(torch.int32)
+        k += n
 
     bb = block_bytes(wl.kv_dtype, d_c, d_r)
     pool = torch.empty((num_blocks, bb), dtype=torch.uint8)
@@ -231,7 +274,7 @@ def page_cache(wl: Workload, g: torch.Generator, seq_lens: torch.Tensor,
         dt = _TORCH_DT[wl.kv_dtype]
         typed = pool.view(dt).view(num_blocks, BLOCK, d_c + d_r)
         typed[:] = float("nan")
-        typed[perm[:total]] = logical.to(dt)
+        typed[perm[:total]] = logical
     else:
         # fp8: one scale per block = absmax of its valid latent values / 448
         # (448 = largest finite e4m3); an all-zero block takes scale 1.

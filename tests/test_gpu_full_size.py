@@ -1,0 +1,110 @@
+"""GPU parity of the decode path at the full sizes of the long-context, fp8
+speculative and full-layer workloads, in the launch configuration of the
+benchmark (all compute units of the device), checked on sampled outputs that
+the oracle computes one by one.  The small-size parity cases in
+test_gpu_decode.py and test_gpu_layer.py check every output element."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_latent_kv_07_amd import api
+from mla_latent_kv_07_amd import inputs as I
+
+from parity import DEV, TOL, compare_decode, oracle_decode, row_rel_err, run_decode, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(n_rows: int, k: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(n_rows, size=min(k, n_rows), replace=False))
+
+
+def test_long_context_full_size_sampled():
+    """4 sequences of 64K-128K tokens, 1 % of cached rows scaled by 8: many
+    splits per sequence and a combine over them."""
+    t0 = time.time()
+    d = I.make_decode_inputs(I.C3)
+    say(f"  inputs {time.time() - t0:.1f} s, seq_lens {d.cache.seq_lens.tolist()}")
+    o, lse, dec = run_decode(d)
+    assert dec.info.max_splits > 1 and dec.info.needs_combine
+    rows = _sample_rows(d.wl.B * d.wl.n_h, 64, 3)
+    compare_decode(d, o, lse, rows=rows)
+
+
+def test_fp8_spec_pair_full_size_sampled():
+    """64 sequences of 1K-8K tokens, e4m3 latent with one scale per block,
+    bf16 rotary keys, two causal query tokens per sequence."""
+    t0 = time.time()
+    d = I.make_decode_inputs(I.C4)
+    say(f"  inputs {time.time() - t0:.1f} s")
+    o, lse, _ = run_decode(d)
+    rows = _sample_rows(d.wl.B * d.wl.q_len * d.wl.n_h, 128, 4)
+    compare_decode(d, o, lse, rows=rows)
+
+
+def test_full_layer_full_size_sampled():
+    """128 sequences of 1-32K tokens through the whole absorbed layer:
+    mla_absorb_q -> mla_decode -> mla_absorb_out, d_model 5120.  Query
+    production (h -> q^C, q^R) is not on the GPU path: the oracle's fp64
+    low-rank projection and RoPE make the bf16 queries.  Each GPU stage is
+    checked against the oracle applied to the device's own input to that
+    stage, and the end-to-end output against the fp64 chain, on sampled
+    sequences."""
+    wl = I.C5
+    t0 = time.time()
+    L = I.make_layer_inputs(wl)
+    cache = I.page_cache(wl, L["generator"], L["seq_lens"], L["cache_rows"])
+    del L["cache_rows"]
+    w = L["weights"]
+    sl = L["seq_lens"]
+    say(f"  inputs {time.time() - t0:.1f} s, {int(sl.sum())} cached tokens")
+    pos = (sl.to(torch.int64) - 1).numpy()          # each query sits at S_b - 1
+    q_nope, q_rope = O.project_queries_lowrank(L["hidden"].double().numpy(), w["w_dq"].double().numpy(),
+                                               w["w_uq"].double().numpy(), w["w_qr"].double().numpy(),
+                                               wl.n_h, wl.d_nope, wl.d_r, pos)
+    bf = torch.bfloat16
+    qn = torch.from_numpy(q_nope).to(bf)
+    qr = torch.from_numpy(q_rope).to(bf)
+    wuk, wuv, wo = w["w_uk"].to(bf), w["w_uv"].to(bf), w["w_o"].to(bf)
+
+    # GPU: the three stages, in the benchmark's launch configuration
+    q_lat = api.absorb_q(qn.to(DEV), wuk.to(DEV))
+    dcache = api.DeviceCache.from_host(cache, DEV)
+    dec = api.Decoder(sl, 1, wl.n_h, wl.d_c, wl.d_r, "bf16", DEV)
+    o_lat, lse = dec(q_lat, qr.to(DEV), dcache, cache.block_table.to(DEV), sl.to(DEV), wl.scale)
+    u, out = api.absorb_out(o_lat, wuv.to(DEV), wo.to(DEV))
+    torch.cuda.synchronize()
+    del dcache
+    say(f"  gpu done {time.time() - t0:.1f} s")
+
+    # stage 1: absorb_q on every row
+    q_lat_h = q_lat.cpu()
+    e1 = row_rel_err(q_lat_h.float().numpy(), O.absorb_q(qn.double().numpy(), wuk.double().numpy()))
+    # stage 2: decode on sampled sequences, from the device's q_lat
+    seqs = _sample_rows(wl.B, 6, 5)
+    rows = (seqs[:, None] * wl.n_h + np.arange(wl.n_h)[None, :]).reshape(-1)
+    d = I.DecodeInputs(wl=wl, cache=cache, q_lat=q_lat_h, q_rope=qr, scale=wl.scale)
+    e2 = compare_decode(d, o_lat, lse, rows=rows)
+    # stage 3: absorb_out on every token, from the device's o_lat (u) and u (out)
+    o_h = o_lat.cpu().double().numpy()
+    ref_u, _ = O.absorb_out(o_h, wuv.double().numpy(), wo.double().numpy())
+    e3u = row_rel_err(u.float().cpu().numpy(), ref_u)
+    u_h = u.float().cpu().double().numpy().reshape(wl.B, -1)
+    e3 = row_rel_err(out.float().cpu().numpy(), u_h @ wo.double().numpy())
+    # end to end on the sampled sequences: the fp64 chain from the bf16 inputs
+    # (sampled sequences take the oracle's fp64 q_lat; the oracle only reads
+    # the rows it is asked for)
+    ref_q_lat = O.absorb_q(qn.double().numpy()[seqs], wuk.double().numpy())
+    q_full = q_lat_h.double().clone()
+    q_full[seqs] = torch.from_numpy(ref_q_lat)
+    dref = I.DecodeInputs(wl=wl, cache=cache, q_lat=q_full, q_rope=qr, scale=wl.scale)
+    ref_o, _ = oracle_decode(dref, rows=rows)
+    _, ref_out = O.absorb_out(ref_o.reshape(len(seqs), wl.n_h, wl.d_c), wuv.double().numpy(), wo.double().numpy())
+    e_chain = row_rel_err(out.float().cpu().numpy()[seqs], ref_out)
+    say(f"  absorb_q {e1:.3e}  decode {e2:.3e}  absorb_out u {e3u:.3e} out {e3:.3e}  chain {e_chain:.3e}"
+        f"  ({time.time() - t0:.1f} s)")
+    assert max(e1, e3u, e3, e_chain) <= TOL["bf16"]
