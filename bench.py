@@ -17,6 +17,10 @@ Prints one JSON line: latent-cache GB/s over the whole step, plus
 Inputs are resident in HBM before timing; 4 replicas of the cache pool are
 rotated so no step finds its pool in the 256 MB last-level (MALL) cache.
 
+  --workload NAME     another workload of the same path: the long-context
+                      batch, the fp8 cache with speculative query pairs, or
+                      the whole absorbed layer (absorb_q -> decode ->
+                      absorb_out); one JSON line of the same form;
   --copy-calibration  also runs a plain 256 MiB device copy (for scaling the
                       HBM byte counters of a profiler run of this command);
   --summarize-counters FETCH_CSV WRITE_CSV
@@ -36,6 +40,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak
 COPY_BYTES = 256 << 20          # calibration copy size
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_bf16_traffic.json")
 DECODE_KERNEL = "decode_bf16_kernel"
@@ -47,7 +52,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="cache pool replicas rotated per call (default: enough for >= 512 MB)")
+    ap.add_argument("--workload", default="v2_decode_b32_s4096_bf16",
+                    choices=["v2_decode_b32_s4096_bf16", "long_ctx_b4_s64k_128k_bf16",
+                             "fp8_cache_spec2_b64", "full_layer_b128_bf16"],
+                    help="the measured batch (default) or one of the other parity workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -103,24 +113,40 @@ def summarize_counters(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(out))
 
 
-def cpu_baseline(d, cache_bytes):
-    """The oracle, as it stands, on the whole batch (all 32 sequences x 128
-    heads x 4096 tokens, ~1-3 s on the host's cores), in latent-cache bytes
-    per second."""
+def cpu_baseline(d, cache_bytes, max_rows=4096):
+    """The oracle, as it stands, on a bounded sample of the workload's query
+    rows (all of them for the measured batch: 32 sequences x 128 heads x 4096
+    tokens, ~1-3 s on the host's cores), scaled to latent-cache bytes per
+    second of the whole batch."""
     import numpy as np
     import oracle as O
 
-    B, n_h = d.wl.B, d.wl.n_h
-    rows = np.arange(B * n_h, dtype=np.int64)
-    O.decode(d.cache.pool, O.FMT_BF16, d.cache.block_table, d.cache.seq_lens, d.q_lat.double(),
-             d.q_rope.double(), d.scale, rows=rows[:n_h // 8])   # warm up (load, page in)
+    wl = d.wl
+    fmt = {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "fp8_e4m3": O.FMT_FP8_E4M3}[wl.kv_dtype]
+    n_rows = wl.B * wl.q_len * wl.n_h
+    rows = np.arange(n_rows, dtype=np.int64)
+    if n_rows > max_rows:
+        rows = np.sort(np.random.default_rng(0).choice(n_rows, size=max_rows, replace=False))
+
+    def run(r):
+        O.decode(d.cache.pool, fmt, d.cache.block_table, d.cache.seq_lens, d.q_lat.double(),
+                 d.q_rope.double(), d.scale, q_len=wl.q_len, block_scales=d.cache.block_scales, rows=r)
+
+    run(rows[:max(1, wl.n_h // 8)])   # warm up (load, page in)
     t0 = time.perf_counter()
-    O.decode(d.cache.pool, O.FMT_BF16, d.cache.block_table, d.cache.seq_lens, d.q_lat.double(),
-             d.q_rope.double(), d.scale, rows=rows)
+    run(rows)
     dt = time.perf_counter() - t0
-    return {"value": round(cache_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": O.threads(),
+    full = dt * n_rows / rows.size
+    return {"value": round(cache_bytes / full / 1e9, 4), "unit": "GB/s", "cores": O.threads(),
             "kind": "oracle",
-            "sample": f"{B} of {B} sequences (all {n_h} heads x 4096 tokens), {dt:.2f} s"}
+            "sample": f"{rows.size} of {n_rows} query rows ({dt:.2f} s), scaled to the whole batch"}
+
+
+def visible_flops(seq_lens, q_len, n_h, d_c, d_r) -> float:
+    """Algorithmic decode FLOPs: 2 (d_c + d_R + d_c) per (query row, visible token)."""
+    vis = sum(int(S) - q_len + t + 1 for S in seq_lens.tolist() for t in range(q_len)
+              if int(S) - q_len + t + 1 > 0)
+    return 2.0 * n_h * vis * (d_c + d_r + d_c)
 
 
 def main():
@@ -134,25 +160,152 @@ def main():
         sys.exit(2)
 
     import torch
+    from mla_latent_kv_07_amd import inputs as I
+
+    torch.cuda.set_device(torch.device("cuda:0"))
+    wl = I.WORKLOADS[args.workload]
+    if wl.d_model:
+        out = run_layer(args, wl)
+    else:
+        out = run_decode(args, wl)
+    print(json.dumps(out), flush=True)
+
+
+class Timer:
+    """HIP events on the launch stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def legs(self, fn, argsets, n, check):
+        """Average time of n back-to-back launches (ms)."""
+        a, b = self.ev(), self.ev()
+        a.record(self.stream)
+        st = 0
+        for i in range(n):
+            st |= fn(*argsets[i % len(argsets)])
+        b.record(self.stream)
+        self.torch.cuda.synchronize()
+        check(st)
+        return a.elapsed_time(b) / n
+
+    def steps(self, step, K, check):
+        """K steps between two synchronizations: (wall ms, event ms) per step."""
+        e0, e1 = self.ev(), self.ev()
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(self.stream)
+        st = 0
+        for i in range(K):
+            st |= step(i)
+        e1.record(self.stream)
+        self.torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        check(st)
+        return wall * 1e3 / K, e0.elapsed_time(e1) / K
+
+    def per_call(self, step, n, check):
+        pairs = [(self.ev(), self.ev()) for _ in range(n)]
+        st = 0
+        for i, (a, b) in enumerate(pairs):
+            a.record(self.stream)
+            st |= step(i)
+            b.record(self.stream)
+        self.torch.cuda.synchronize()
+        check(st)
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+        pct = lambda q: round(us[min(len(us) - 1, int(q * len(us)))], 2)
+        return {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9)}
+
+
+def replicas_for(args, pool_bytes) -> int:
+    """Enough rotated pool replicas that >= 512 MB separate two uses of one
+    (so no call finds its cache in the 256 MB MALL)."""
+    if args.replicas:
+        return args.replicas
+    return max(2, -(-(512 << 20) // pool_bytes))
+
+
+def copy_calibration(torch, timer, dev):
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = timer.ev(), timer.ev()
+    a.record(timer.stream)
+    for _ in range(5):
+        dst.copy_(src)
+    b.record(timer.stream)
+    torch.cuda.synchronize()
+    return round(2 * COPY_BYTES / (a.elapsed_time(b) / 5 * 1e-3) / 1e9, 1)
+
+
+def decode_kernel_name(wl) -> str:
+    """The decode kernel libmla launches for this shape."""
+    if wl.kv_dtype == "bf16" and wl.q_dtype == "bf16" and wl.d_c == 512 and wl.d_r == 64:
+        return DECODE_KERNEL
+    return "decode_generic_kernel"
+
+
+def roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic):
+    """Roofline of the decode kernel.  Bound: HBM when the workload's FLOP per
+    cache byte is below the ridge of the kernel's contraction (bf16 MFMA 2.5
+    PFLOP/s, or fp32 vector ALU 157.3 TFLOP/s for the generic kernel, against
+    8 TB/s), else the compute unit."""
+    gbs = cache_bytes / (dec_ms * 1e-3) / 1e9
+    tfl = flops / (dec_ms * 1e-3) / 1e12
+    if kernel == DECODE_KERNEL:
+        cpeak, cbound = BF16_MFMA_PEAK_TFLOPS, "mfma"
+    else:
+        cpeak, cbound = FP32_VALU_PEAK_TFLOPS, "alu"
+    intensity = flops / cache_bytes
+    ridge = cpeak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        r = {"bound": cbound, "achieved": round(tfl, 1), "peak": cpeak, "unit": "TFLOP/s",
+             "frac": round(tfl / cpeak, 4)}
+    r.update({"traffic": traffic, "kernel": kernel, "algorithmic_bytes": cache_bytes,
+              "algorithmic_flops": flops, "flop_per_byte": round(intensity, 1),
+              "hbm_gbs": round(gbs, 1), "tflops": round(tfl, 1),
+              "compute_frac": round(tfl / cpeak, 4)})
+    return r
+
+
+def traffic_for(kernel, workload):
+    """Measured HBM bytes per launch, if the counter summary was taken for this
+    kernel source on this workload."""
+    if kernel != DECODE_KERNEL or not os.path.exists(TRAFFIC_JSON):
+        return None
+    t = json.load(open(TRAFFIC_JSON))
+    ok = t.get("kernel_source_sha") == kernel_sha() and t.get("workload") == workload
+    return round(t["bytes_per_launch"]) if ok else None
+
+
+def run_decode(args, wl):
+    import torch
     from mla_latent_kv_07_amd import _lib as L
     from mla_latent_kv_07_amd import api
     from mla_latent_kv_07_amd import inputs as I
 
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    wl = I.C2
     d = I.make_decode_inputs(wl)
-    cache_bytes = d.cache.cache_bytes                      # 150,994,944 B of valid rows
-    S = int(d.cache.seq_lens[0])
-    flops = 2 * wl.B * wl.n_h * S * (wl.d_c + wl.d_r + wl.d_c)   # score (576) + value (512) MACs
+    cache_bytes = d.cache.cache_bytes                      # valid rows only
+    flops = visible_flops(d.cache.seq_lens, wl.q_len, wl.n_h, wl.d_c, wl.d_r)
+    R = replicas_for(args, d.cache.pool.numel())
 
-    pools = [api.DeviceCache.from_host(d.cache, dev) for _ in range(args.replicas)]
+    pools = [api.DeviceCache.from_host(d.cache, dev) for _ in range(R)]
     bt = d.cache.block_table.to(dev)
     sl = d.cache.seq_lens.to(dev)
     ql, qr = d.q_lat.to(dev), d.q_rope.to(dev)
     dec = api.Decoder(d.cache.seq_lens, wl.q_len, wl.n_h, wl.d_c, wl.d_r, wl.kv_dtype, dev)
-    o_lat = torch.empty((wl.B, wl.n_h, wl.d_c), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((wl.B, wl.n_h), dtype=torch.float32, device=dev)
+    T = wl.B * wl.q_len
+    qdt = ql.dtype
+    o_lat = torch.empty((T, wl.n_h, wl.d_c), dtype=qdt, device=dev)
+    lse = torch.empty((T, wl.n_h), dtype=torch.float32, device=dev)
 
     # pre-marshalled arguments: the host must stay ahead of the GPU
     lib = L.load()
@@ -161,93 +314,144 @@ def main():
     P = ctypes.c_void_p
     descs = [p.desc() for p in pools]
     ws_bytes = dec.workspace.numel()
-    call_args = [(P(ql.data_ptr()), P(qr.data_ptr()), L.DT_BF16, ctypes.byref(descs[r]),
+    qdt_c = L.DT_BF16 if qdt == torch.bfloat16 else L.DT_F32
+    call_args = [(P(ql.data_ptr()), P(qr.data_ptr()), qdt_c, ctypes.byref(descs[r]),
                   P(bt.data_ptr()), bt.stride(0), P(sl.data_ptr()), wl.B, wl.q_len, wl.n_h,
                   ctypes.c_float(d.scale), ctypes.byref(dec.info), P(dec.plan_dev.data_ptr()),
                   P(dec.workspace.data_ptr()), ws_bytes, P(o_lat.data_ptr()), P(lse.data_ptr()), sp)
-                 for r in range(args.replicas)]
+                 for r in range(R)]
     fin_args = (ctypes.byref(dec.info), P(dec.plan_dev.data_ptr()), P(dec.workspace.data_ptr()),
-                ws_bytes, L.DT_BF16, P(o_lat.data_ptr()), P(lse.data_ptr()), sp)
+                ws_bytes, qdt_c, P(o_lat.data_ptr()), P(lse.data_ptr()), sp)
     full, part, fin = lib.mla_decode, lib.mla_decode_partial, lib.mla_decode_finish
-    R = args.replicas
+    timer = Timer(torch, stream)
 
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
+    def step(i):
+        return full(*call_args[i % R])
 
     for i in range(args.warmup):
-        L.check(full(*call_args[i % R]))
+        L.check(step(i))
     torch.cuda.synchronize()
-
-    # ---- timed steps: K whole decode calls, bracketed by synchronizations
     K = args.steps
-    e0, e1 = ev(), ev()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    bad = 0
-    for i in range(K):
-        bad |= full(*call_args[i % R])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    L.check(bad)
-    ms_per_step = wall * 1e3 / K
-    gpu_ms = e0.elapsed_time(e1) / K
-
-    # ---- per-kernel launch durations: back-to-back launches of each phase
-    def timed(fn, argsets, n):
-        a, b = ev(), ev()
-        a.record(stream)
-        st = 0
-        for i in range(n):
-            st |= fn(*argsets[i % len(argsets)])
-        b.record(stream)
-        torch.cuda.synchronize()
-        L.check(st)
-        return a.elapsed_time(b) / n
-
+    ms_per_step, gpu_ms = timer.steps(step, K, L.check)
     n_leg = max(K, 50)
-    dec_ms = timed(part, call_args, n_leg)
-    comb_ms = timed(fin, [fin_args], n_leg)
+    dec_ms = timer.legs(part, call_args, n_leg, L.check)
+    comb_ms = timer.legs(fin, [fin_args], n_leg, L.check) if dec.info.needs_combine else 0.0
+    call_us = timer.per_call(step, n_leg, L.check)
+    copy_gbs = copy_calibration(torch, timer, dev) if args.copy_calibration else None
 
-    # ---- per-call distribution of the whole call (events around each call)
-    pairs = [(ev(), ev()) for _ in range(n_leg)]
-    st = 0
-    for i, (a, b) in enumerate(pairs):
-        a.record(stream)
-        st |= full(*call_args[i % R])
-        b.record(stream)
-    torch.cuda.synchronize()
-    L.check(st)
-    call_us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
-    pct = lambda q: round(call_us[min(len(call_us) - 1, int(q * len(call_us)))], 2)
-
-    copy_gbs = None
-    if args.copy_calibration:
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        a, b = ev(), ev()
-        a.record(stream)
-        for _ in range(5):
-            dst.copy_(src)
-        b.record(stream)
-        torch.cuda.synchronize()
-        copy_gbs = round(2 * COPY_BYTES / (a.elapsed_time(b) / 5 * 1e-3) / 1e9, 1)
-        del src, dst
-
-    value = cache_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = cache_bytes / (dec_ms * 1e-3) / 1e9
-
-    traffic = None
-    if os.path.exists(TRAFFIC_JSON):
-        t = json.load(open(TRAFFIC_JSON))
-        if t.get("kernel_source_sha") == kernel_sha():
-            traffic = round(t["bytes_per_launch"])
-
+    kernel = decode_kernel_name(wl)
+    S = d.cache.seq_lens.tolist()
+    headline = wl.name == "v2_decode_b32_s4096_bf16"
     out = {
-        "metric": "MLA decode latent-cache GB/s + TFLOP/s, B=32 S=4096 bf16, % of roofline",
-        "value": round(value, 2),
+        "metric": ("MLA decode latent-cache GB/s + TFLOP/s, B=32 S=4096 bf16, % of roofline" if headline
+                   else f"MLA decode latent-cache GB/s + TFLOP/s, {wl.name}, % of roofline"),
+        "value": round(cache_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.kv_dtype == "bf16" else ("fp8_e4m3+bf16" if wl.kv_dtype == "fp8_e4m3" else "f32"),
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "seq_len": S[0] if len(set(S)) == 1 else [min(S), max(S)],
+                   "q_len": wl.q_len, "n_h": wl.n_h, "d_c": wl.d_c, "d_r": wl.d_r,
+                   "kv_dtype": wl.kv_dtype, "block_size": 64, "cache_bytes": cache_bytes,
+                   "pool_replicas": R, "work_items": dec.info.num_items,
+                   "splits_per_seq": dec.info.max_splits},
+        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "call_us": call_us,
+        "decode_kernel_us": round(dec_ms * 1e3, 2),
+        "combine_kernel_us": round(comb_ms * 1e3, 2),
+        "roofline": roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic_for(kernel, wl.name)),
+        "cpu_baseline": None,
+    }
+    if copy_gbs is not None:
+        out["copy_calibration_gbs"] = copy_gbs
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, cache_bytes)
+    return out
+
+
+def run_layer(args, wl):
+    """The whole absorbed layer at decode: absorb_q -> split decode + combine
+    -> absorb_out.  Query production (h -> q^C, q^R) is not on the path: q^C
+    and q^R are drawn N(0, 1) from the workload's generator after its cache."""
+    import torch
+    from mla_latent_kv_07_amd import _lib as L
+    from mla_latent_kv_07_amd import api
+    from mla_latent_kv_07_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    Lw = I.make_layer_inputs(wl)
+    cache = I.page_cache(wl, Lw["generator"], Lw["seq_lens"], Lw["cache_rows"])
+    del Lw["cache_rows"]
+    g = Lw["generator"]
+    bf = torch.bfloat16
+    T = wl.B * wl.q_len
+    qn = torch.randn((T, wl.n_h, wl.d_nope), generator=g).to(bf).to(dev)
+    qr = torch.randn((T, wl.n_h, wl.d_r), generator=g).to(bf).to(dev)
+    w = {k: v.to(bf).to(dev) for k, v in Lw["weights"].items() if k in ("w_uk", "w_uv", "w_o")}
+    sl_h = Lw["seq_lens"]
+    cache_bytes = cache.cache_bytes
+    weight_bytes = sum(v.numel() * 2 for v in w.values())
+    flops_dec = visible_flops(sl_h, wl.q_len, wl.n_h, wl.d_c, wl.d_r)
+    flops_q = 2.0 * T * wl.n_h * wl.d_nope * wl.d_c
+    flops_o = 2.0 * T * wl.n_h * wl.d_c * wl.d_v + 2.0 * T * wl.n_h * wl.d_v * wl.d_model
+    R = replicas_for(args, cache.pool.numel())
+    pools = [api.DeviceCache.from_host(cache, dev) for _ in range(R)]
+    bt, sl = cache.block_table.to(dev), sl_h.to(dev)
+    dec = api.Decoder(sl_h, wl.q_len, wl.n_h, wl.d_c, wl.d_r, "bf16", dev)
+    q_lat = torch.empty((T, wl.n_h, wl.d_c), dtype=bf, device=dev)
+    o_lat = torch.empty((T, wl.n_h, wl.d_c), dtype=bf, device=dev)
+    lse = torch.empty((T, wl.n_h), dtype=torch.float32, device=dev)
+    u = torch.empty((T, wl.n_h, wl.d_v), dtype=bf, device=dev)
+    out_t = torch.empty((T, wl.d_model), dtype=bf, device=dev)
+    ws_o_bytes = api.absorb_out_workspace_bytes(T, wl.n_h, wl.d_v, wl.d_model, bf)
+    ws_o = torch.empty(max(ws_o_bytes, 256), dtype=torch.uint8, device=dev)
+
+    lib = L.load()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    descs = [p.desc() for p in pools]
+    aq = (P(qn.data_ptr()), qn.stride(0), P(w["w_uk"].data_ptr()), P(q_lat.data_ptr()), T, wl.n_h,
+          wl.d_nope, wl.d_c, L.DT_BF16, sp)
+    dargs = [(P(q_lat.data_ptr()), P(qr.data_ptr()), L.DT_BF16, ctypes.byref(descs[r]), P(bt.data_ptr()),
+              bt.stride(0), P(sl.data_ptr()), wl.B, wl.q_len, wl.n_h, ctypes.c_float(wl.scale),
+              ctypes.byref(dec.info), P(dec.plan_dev.data_ptr()), P(dec.workspace.data_ptr()),
+              dec.workspace.numel(), P(o_lat.data_ptr()), P(lse.data_ptr()), sp) for r in range(R)]
+    ao = (P(o_lat.data_ptr()), P(w["w_uv"].data_ptr()), P(w["w_o"].data_ptr()), P(u.data_ptr()),
+          P(out_t.data_ptr()), P(ws_o.data_ptr()), ws_o_bytes, T, wl.n_h, wl.d_c, wl.d_v, wl.d_model,
+          L.DT_BF16, sp)
+    timer = Timer(torch, stream)
+
+    def step(i):
+        return lib.mla_absorb_q(*aq) | lib.mla_decode(*dargs[i % R]) | lib.mla_absorb_out(*ao)
+
+    for i in range(args.warmup):
+        L.check(step(i))
+    torch.cuda.synchronize()
+    K = args.steps
+    ms_per_step, gpu_ms = timer.steps(step, K, L.check)
+    n_leg = max(K, 20)
+    q_ms = timer.legs(lib.mla_absorb_q, [aq], n_leg, L.check)
+    dec_ms = timer.legs(lib.mla_decode_partial, dargs, n_leg, L.check)
+    fin = (ctypes.byref(dec.info), P(dec.plan_dev.data_ptr()), P(dec.workspace.data_ptr()),
+           dec.workspace.numel(), L.DT_BF16, P(o_lat.data_ptr()), P(lse.data_ptr()), sp)
+    comb_ms = timer.legs(lib.mla_decode_finish, [fin], n_leg, L.check)
+    o_ms = timer.legs(lib.mla_absorb_out, [ao], n_leg, L.check)
+    call_us = timer.per_call(step, n_leg, L.check)
+
+    kernel = decode_kernel_name(wl)
+    layer_bytes = cache_bytes + weight_bytes
+    S = sl_h.tolist()
+    out = {
+        "metric": f"MLA absorbed layer (absorb_q, decode, absorb_out) cache+weight GB/s, {wl.name}",
+        "value": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
@@ -258,29 +462,28 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "seq_len": S, "q_len": wl.q_len, "n_h": wl.n_h,
-                   "d_c": wl.d_c, "d_r": wl.d_r, "kv_dtype": wl.kv_dtype, "block_size": 64,
-                   "cache_bytes": cache_bytes, "pool_replicas": R,
-                   "work_items": dec.info.num_items, "splits_per_seq": dec.info.max_splits},
-        "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "config": {"workload": wl.name, "B": wl.B, "seq_len": [min(S), max(S)], "q_len": wl.q_len,
+                   "n_h": wl.n_h, "d_c": wl.d_c, "d_r": wl.d_r, "d_nope": wl.d_nope, "d_v": wl.d_v,
+                   "d_model": wl.d_model, "cache_bytes": cache_bytes, "weight_bytes": weight_bytes,
+                   "pool_replicas": R, "work_items": dec.info.num_items},
+        "tflops": round((flops_dec + flops_q + flops_o) / (ms_per_step * 1e-3) / 1e12, 2),
         "gpu_ms_per_step": round(gpu_ms, 5),
-        "call_us": {"p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9)},
+        "call_us": call_us,
+        "absorb_q_us": round(q_ms * 1e3, 2),
         "decode_kernel_us": round(dec_ms * 1e3, 2),
         "combine_kernel_us": round(comb_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": DECODE_KERNEL,
-                     "algorithmic_bytes": cache_bytes,
-                     "mfma_tflops": round(flops / (dec_ms * 1e-3) / 1e12, 1),
-                     "mfma_frac": round(flops / (dec_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "absorb_out_us": round(o_ms * 1e3, 2),
+        "absorb_gemm_gbs": {
+            "absorb_q": round((w["w_uk"].numel() * 2 + qn.numel() * 2 + q_lat.numel() * 2) / (q_ms * 1e-3) / 1e9, 1),
+            "absorb_out": round((w["w_uv"].numel() * 2 + w["w_o"].numel() * 2 + o_lat.numel() * 2
+                                 + out_t.numel() * 2) / (o_ms * 1e-3) / 1e9, 1)},
+        "roofline": roofline(wl, kernel, dec_ms, cache_bytes, flops_dec, traffic_for(kernel, wl.name)),
         "cpu_baseline": None,
     }
-    if copy_gbs is not None:
-        out["copy_calibration_gbs"] = copy_gbs
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(d, cache_bytes)
-    print(json.dumps(out), flush=True)
+        d = I.DecodeInputs(wl=wl, cache=cache, q_lat=q_lat.cpu(), q_rope=qr.cpu(), scale=wl.scale)
+        out["cpu_baseline"] = cpu_baseline(d, cache_bytes, max_rows=1024)
+    return out
 
 
 if __name__ == "__main__":
