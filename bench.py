@@ -26,7 +26,7 @@ rotated so no step finds its pool in the 256 MB last-level (MALL) cache.
   --summarize-counters FETCH_CSV WRITE_CSV
                       turns the counter CSVs of two `rocprofv3 --pmc` runs of
                       this command (FETCH_SIZE, then WRITE_SIZE) into
-                      profiles/decode_bf16_traffic.json and exits.
+                      profiles/decode_mfma_bf16_traffic.json and exits.
 """
 from __future__ import annotations
 
@@ -42,8 +42,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak
 COPY_BYTES = 256 << 20          # calibration copy size
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_bf16_traffic.json")
-DECODE_KERNEL = "decode_bf16_kernel"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_mfma_bf16_traffic.json")
+DECODE_KERNEL = "decode_mfma_kernel<false>"      # bf16 cache
+DECODE_KERNEL_FP8 = "decode_mfma_kernel<true>"   # fp8 cache, converted to bf16 in LDS
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -66,7 +67,7 @@ def parse():
 
 def kernel_sha() -> str:
     import hashlib
-    src = os.path.join(ROOT, "mla_latent_kv_07_amd", "csrc", "decode_bf16.hip")
+    src = os.path.join(ROOT, "mla_latent_kv_07_amd", "csrc", "decode_mfma.hip")
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
@@ -244,8 +245,11 @@ def copy_calibration(torch, timer, dev):
 
 def decode_kernel_name(wl) -> str:
     """The decode kernel libmla launches for this shape."""
-    if wl.kv_dtype == "bf16" and wl.q_dtype == "bf16" and wl.d_c == 512 and wl.d_r == 64:
-        return DECODE_KERNEL
+    if wl.q_dtype == "bf16" and wl.d_c == 512 and wl.d_r == 64:
+        if wl.kv_dtype == "bf16":
+            return DECODE_KERNEL
+        if wl.kv_dtype == "fp8_e4m3":
+            return DECODE_KERNEL_FP8
     return "decode_generic_kernel"
 
 
@@ -256,7 +260,7 @@ def roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic):
     8 TB/s), else the compute unit."""
     gbs = cache_bytes / (dec_ms * 1e-3) / 1e9
     tfl = flops / (dec_ms * 1e-3) / 1e12
-    if kernel == DECODE_KERNEL:
+    if kernel in (DECODE_KERNEL, DECODE_KERNEL_FP8):
         cpeak, cbound = BF16_MFMA_PEAK_TFLOPS, "mfma"
     else:
         cpeak, cbound = FP32_VALU_PEAK_TFLOPS, "alu"

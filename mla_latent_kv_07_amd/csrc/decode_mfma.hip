@@ -1,5 +1,7 @@
-// Absorbed MLA decode on MFMA for the DeepSeek-V2 shape: bf16 cache rows of
-// [c (512) | k^R (64)], bf16 queries, fp32 accumulation.
+// Absorbed MLA decode on MFMA for the DeepSeek-V2 shape (latent 512, rotary
+// 64, bf16 queries, fp32 accumulation) over a paged cache of bf16 rows
+// [c (512) | k^R (64)], or of e4m3 latents with one scale per 64-token block
+// plus bf16 rotary keys (decode_mfma_kernel<true>, see below).
 //
 // Workgroup = 4 waves = 128 query rows (heads x query tokens) of one
 // sequence; wave w owns rows 32w..32w+31 for the whole work item and keeps
@@ -52,8 +54,18 @@ constexpr int MBLOCKS = DC / 32;                // 16 value M-blocks
 constexpr int O_PITCH = CB + 16;                // epilogue staging row pitch (bytes)
 constexpr int PF = 8;                           // value-fragment prefetch depth (MFMAs)
 constexpr int PFK = 3;                          // score-fragment prefetch depth (MFMAs)
-static_assert(NSTAGE * STAGE_BYTES <= 160 * 1024, "stage buffers exceed LDS");
-static_assert(4 * 32 * O_PITCH <= NSTAGE * STAGE_BYTES, "epilogue staging exceeds the stage buffers");
+// fp8 caches: each stage's e4m3 latent (32 x 512 B) and bf16 rotary rows
+// (32 x 128 B) land in one of two staging buffers, and are converted once per
+// workgroup into a bf16 stage buffer of the layout above (three of them).
+constexpr int FP8_LAT = HALF * DC;              // 16384
+constexpr int FP8_STAGE = FP8_LAT + HALF * RB;  // 20480
+constexpr int NSTAGE8 = 3;
+template <bool FP8>
+constexpr int lds_bytes() { return FP8 ? NSTAGE8 * STAGE_BYTES + 2 * FP8_STAGE : NSTAGE * STAGE_BYTES; }
+static_assert(lds_bytes<false>() <= 160 * 1024 && lds_bytes<true>() <= 160 * 1024, "stage buffers exceed LDS");
+static_assert(4 * 36864 <= lds_bytes<true>() && 4 * 36864 <= lds_bytes<false>(), "query staging exceeds LDS");
+static_assert(4 * 32 * O_PITCH <= lds_bytes<true>() && 4 * 32 * O_PITCH <= lds_bytes<false>(),
+              "epilogue staging exceeds the LDS allocation");
 
 // LDS layout of a stage (slot t = token t of the stage):
 //   latent rows  [32][1040 B]: bytes 0..1023 of slot t = c of token t;
@@ -100,6 +112,18 @@ __device__ __forceinline__ void issue_stage(const uint8_t *src0, uint32_t stage_
     dma16(stage_lds + LAT_BYTES + wave * 1024, rot_off, src0);
 }
 
+// fp8 cache: copy one stage (32 tokens) of a block into a staging buffer:
+// wave w copies latent bytes [4 KiB w, 4 KiB (w + 1)) (two 512-byte rows per
+// 1 KiB instruction) and the 8 rotary rows 8w..8w+7 (one instruction).
+__device__ __forceinline__ void issue_stage_fp8(const uint8_t *codes0, const uint8_t *rope0,
+                                                uint32_t staging_lds, int wave, uint32_t l16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma16(staging_lds + (4 * wave + k) * 1024, l16, codes0 + (4 * wave + k) * 1024);
+    dma16(staging_lds + FP8_LAT + wave * 1024, l16, rope0 + wave * 1024);
+}
+
+constexpr int DMA_PER_STAGE8 = 5;
+
 // Loads of wave-uniform values (plan, block table, lengths) through the
 // constant address space become scalar loads, which never wait on the
 // vector-memory counter of the asynchronous stage copies.
@@ -107,9 +131,26 @@ __device__ __forceinline__ int32_t sload(const int32_t *p, int64_t i) {
     return ((const __attribute__((address_space(4))) int32_t *)p)[i];
 }
 
+// An opaque copy of a per-lane value: offsets derived from it are computed
+// where they are used and die there, instead of being held in registers
+// across the stage loop (the fp8 copies and conversion use it).
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
 
-__global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem_[NSTAGE * STAGE_BYTES];
+
+// FP8: the cache stores e4m3 latents with one fp32 scale per 64-token block
+// and bf16 rotary keys.  Codes are converted exactly to bf16 (the scale is a
+// per-stage scalar): the score chain runs the 4 rotary k-steps first, scales
+// that partial sum by 1/sigma, then adds the latent k-steps, so that
+// sigma * acc = sigma (q~ . c8) + q^R . k^R; the probabilities are produced
+// already multiplied by sigma (value MFMAs then sum (sigma p) c8 = p c) and
+// the denominator takes psum / sigma.  (fp8 cache: huny.dev "DeepSeek MLA
+// 해부" §6 FP8 item; vLLM MLA page, "FP8 MLA 지원".)
+template <bool FP8>
+__global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_[lds_bytes<FP8>()];
     lds_u8 *smem = (lds_u8 *)smem_;
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
@@ -147,15 +188,32 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     const uint8_t *pool = (const uint8_t *)a.pool;
     const int64_t bt_row = (int64_t)b * a.bt_stride;
     const int64_t num_blocks = a.num_pool_blocks;
-    auto stage_src = [&](int st) {   // HBM row of the stage's first token
+    auto blk_id = [&](int st) {
         int64_t id = sload(a.block_table, bt_row + blk0 + (st >> 1));
-        id = id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
-        return pool + id * (int64_t)(kBlock * ROW_BYTES) + (st & 1) * HALF * ROW_BYTES;
+        return id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
     };
-    auto stage_off = [&](int st) { return (uint32_t)((st & (NSTAGE - 1)) * STAGE_BYTES); };
+    auto stage_src = [&](int st) {   // HBM row of the stage's first token (bf16 layout)
+        return pool + blk_id(st) * (int64_t)(kBlock * ROW_BYTES) + (st & 1) * HALF * ROW_BYTES;
+    };
+    // block scale of a stage (fp8)
+    auto sigma = [&](int st) {
+        return __int_as_float(sload((const int32_t *)a.block_scales, blk_id(st)));
+    };
+    auto stage_off = [&](int st) {
+        return FP8 ? (uint32_t)((st % NSTAGE8) * STAGE_BYTES) : (uint32_t)((st & (NSTAGE - 1)) * STAGE_BYTES);
+    };
+    auto staging_off = [&](int st) { return (uint32_t)(NSTAGE8 * STAGE_BYTES + (st & 1) * FP8_STAGE); };
     const uint32_t l16 = lane << 4;
-    const uint32_t rot_off = (uint32_t)((wave * 8 + (lane & 7)) * ROW_BYTES + CB + 16 * (lane >> 3));
-    auto issue = [&](int st) { issue_stage(stage_src(st), smem_addr + stage_off(st), wave, l16, rot_off); };
+    const uint32_t rot_off = FP8 ? 0u : (uint32_t)((wave * 8 + (lane & 7)) * ROW_BYTES + CB + 16 * (lane >> 3));
+    auto issue = [&](int st) {
+        if constexpr (FP8) {
+            const uint8_t *blk = pool + blk_id(st) * a.block_bytes;
+            issue_stage_fp8(blk + (st & 1) * FP8_LAT, blk + kBlock * DC + (st & 1) * HALF * RB,
+                            smem_addr + staging_off(st), wave, (uint32_t)opaque(lane) << 4);
+        } else {
+            issue_stage(stage_src(st), smem_addr + stage_off(st), wave, l16, rot_off);
+        }
+    };
 
     // ---- queries -> VGPRs (MFMA B fragments: lane (ln, g) holds, for k-step
     // ks, bytes 32 ks + 16 g .. +15 of row ln's 1152).  Each wave copies its 32
@@ -195,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     __syncthreads();   // every wave holds its queries: the stage buffers are free
     issue(0);
     if (nst_live > 1) issue(1);
-    if (nst_live > 2) issue(2);
+    if (!FP8 && nst_live > 2) issue(2);
 
     f32x16 oacc[MBLOCKS];
 #pragma unroll
@@ -232,24 +290,31 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
                                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lo + 16 * LPITCH)));
         return vf;
     };
+    // order of the score k-steps: fp8 runs the 4 rotary k-steps first
+    auto kstep = [](int i) { return FP8 ? (i < DR / 16 ? KC + i : i - DR / 16) : i; };
 
     // ---- score MFMAs: S^T[32 tokens x 32 rows] += K[32 x 16] . Q^T[16 x 32].
     // Written as inline asm with VGPR operands: the compiler gives every MFMA
     // builtin an AGPR accumulator, and the 256 AGPRs are all taken by O^T.
     // Hazards the compiler cannot see are covered by hand: the chain
     // accumulates back to back into the same registers (no wait states
-    // needed); s_nop 1 before each MFMA covers a VALU write of an operand; an
-    // s_nop 15 after the chain covers the MFMA-result -> VALU-read latency
-    // (>= 10 wait states for an 8-pass MFMA).
-    auto score_mfma = [&](f32x16 &acc, const bf16x8 &kf, int ks) {
+    // needed); s_nop 1 before each MFMA covers a VALU write of an operand or
+    // of the accumulator; an s_nop 15 after a chain covers the MFMA-result ->
+    // VALU-read latency (>= 10 wait states for an 8-pass MFMA).
+    auto score_mfma = [&](f32x16 &acc, const bf16x8 &kf, int i) {
         // the first MFMA writes the accumulator while reading its operands:
         // early clobber keeps them apart
-        if (ks == 0)
+        if (i == 0)
             asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                         : "=&v"(acc) : "v"(kf), "v"(qf[0]));
+                         : "=&v"(acc) : "v"(kf), "v"(qf[kstep(0)]));
         else
             asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                         : "+v"(acc) : "v"(kf), "v"(qf[ks]));
+                         : "+v"(acc) : "v"(kf), "v"(qf[kstep(i)]));
+    };
+    // fp8: after the rotary k-steps, divide the partial sum by the block scale
+    auto rope_to_latent_scale = [&](f32x16 &acc, float inv_sigma) {
+        asm volatile("s_nop 15" : "+v"(acc));
+        acc *= inv_sigma;
     };
 
     // Rows past the sequence end in a partial stage are zeroed in LDS so that
@@ -267,27 +332,74 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
             }
         }
     };
+    // fp8: staging buffer of stage st -> its bf16 stage buffer, by all 256
+    // threads: latent codes converted exactly (scale 1), rotary rows copied,
+    // rows past the sequence end written as zeros.
+    auto convert = [&](int st) {
+        const int valid = S - (p_first + st * HALF);
+        const lds_u8 *src = smem + staging_off(st);
+        lds_u8 *dst = smem + stage_off(st);
+        const int tid = opaque(threadIdx.x);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = tid + 256 * j;   // 16-byte chunk of the 16 KiB latent part
+            const int t = i >> 5, c16 = i & 31;
+            const uint4 v = *(const uint4 *)(src + i * 16);
+            uint32_t o[8];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false));
+                o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true));
+            }
+            const bool live = t < valid;
+            uint4 *d = (uint4 *)(dst + t * LPITCH + c16 * 32);
+            d[0] = live ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
+            d[1] = live ? make_uint4(o[4], o[5], o[6], o[7]) : make_uint4(0, 0, 0, 0);
+        }
+        {
+            const int t = tid >> 3, c = tid & 7;
+            const uint4 v = *(const uint4 *)(src + FP8_LAT + t * RB + c * 16);
+            *(uint4 *)(dst + LAT_BYTES + (t >> 3) * 1024 + c * 128 + (t & 7) * 16) =
+                t < valid ? v : make_uint4(0, 0, 0, 0);
+        }
+    };
 
-    // ---- prologue: score of stage 0 (wait for this wave's copy of stage 0;
-    // the barrier makes every wave's copies visible)
-    if (nst_live > 2)
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if (nst_live > 1)
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
+    // ---- prologue: score of stage 0
+    float sig_cur = 1.f, sig_next = 1.f;   // block scales of stages st, st+1 (fp8)
+    if constexpr (FP8) {
+        // stages 0 and 1 land in the staging buffers and are converted; stage 2
+        // then takes stage 0's staging buffer
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    zero_tail(0);
+        __syncthreads();
+        convert(0);
+        if (nst_live > 1) convert(1);
+        __syncthreads();
+        if (nst_live > 2) issue(2);
+        sig_cur = sigma(0);
+    } else {
+        // wait for this wave's copy of stage 0; the barrier makes every wave's
+        // copies visible
+        if (nst_live > 2)
+            asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else if (nst_live > 1)
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        zero_tail(0);
+    }
     f32x16 sA, sB;
     {
         const uint32_t kbs = kb0 + stage_off(0), rbs = rb0 + stage_off(0);
         bf16x8 kb[PFK];
 #pragma unroll
-        for (int j = 0; j < PFK; ++j) kb[j] = kld(kbs, rbs, j);
+        for (int j = 0; j < PFK; ++j) kb[j] = kld(kbs, rbs, kstep(j));
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            score_mfma(sA, kb[ks % PFK], ks);
-            if (ks + PFK < KS) kb[ks % PFK] = kld(kbs, rbs, ks + PFK);
+        for (int i = 0; i < KS; ++i) {
+            score_mfma(sA, kb[i % PFK], i);
+            if (i + PFK < KS) kb[i % PFK] = kld(kbs, rbs, kstep(i + PFK));
+            if (FP8 && i == DR / 16 - 1) rope_to_latent_scale(sA, 1.0f / sig_cur);
         }
         asm volatile("s_nop 15" : "+v"(sA));
     }
@@ -297,23 +409,32 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     // value MFMAs.
     auto iteration = [&](int st, f32x16 &cur, f32x16 &nxt) {
         const bool has_next = st + 1 < nst_live;
-        if (has_next) {
-            // stage st+1 landed for this wave (stage st+2 may be in flight)
-            if (st + 2 < nst_live)
-                asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (FP8) {
+            // stage st+1 was converted at the end of iteration st-1 (or in the
+            // prologue); every wave has finished iteration st-1, so the
+            // staging buffer of stage st+1 may be refilled with stage st+3
+            __syncthreads();
+            if (st + 3 < nst_live) issue(st + 3);
+            if (has_next) sig_next = sigma(st + 1);
+        } else {
+            if (has_next) {
+                // stage st+1 landed for this wave (stage st+2 may be in flight)
+                if (st + 2 < nst_live)
+                    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            // every wave's copy of stage st+1 is visible, and every wave has
+            // finished iteration st-1, so stage st-1's buffer may be refilled
+            __syncthreads();
+            if (st + 3 < nst_live) issue(st + 3);
+            if (has_next) zero_tail(st + 1);
         }
-        // every wave's copy of stage st+1 is visible, and every wave has
-        // finished iteration st-1, so stage st-1's buffer may be refilled
-        __syncthreads();
-        if (st + 3 < nst_live) issue(st + 3);
-        if (has_next) zero_tail(st + 1);
         const uint32_t kbs = kb0 + stage_off(st + 1), rbs = rb0 + stage_off(st + 1);
         bf16x8 kb[PFK];
         if (has_next) {
 #pragma unroll
-            for (int j = 0; j < PFK; ++j) kb[j] = kld(kbs, rbs, j);
+            for (int j = 0; j < PFK; ++j) kb[j] = kld(kbs, rbs, kstep(j));
         }
 
         // mask: entry r of lane half g is token tok_of(8 (r >> 2) + 4 g + (r & 3))
@@ -327,7 +448,11 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
                 cur[r] = (16 * (r >> 3) + 4 * (r & 3) + 2 * ((r >> 2) & 1)) < lim_rel ? cur[r] : -INFINITY;
         }
 
-        float mx = -INFINITY, m_new = m_run, m_ref = 0.f, alpha = 1.f, psum = 0.f;
+        // fp8: the scores are sigma * cur and the probabilities are produced
+        // multiplied by sigma (exp2 argument + log2 sigma)
+        const float s_l2 = FP8 ? a.scale_log2 * sig_cur : a.scale_log2;
+        const float l2sig = FP8 ? __builtin_amdgcn_logf(sig_cur) : 0.f;
+        float mx = -INFINITY, m_new = m_run, m_off = 0.f, alpha = 1.f, psum = 0.f;
         bool raise = false;
         bf16x8 pcur[2];
         bf16x8 vb[PF];
@@ -341,17 +466,17 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
             } else if (k == 8) {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx),
                                                                  false, false);
-                mx = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1])) * a.scale_log2;
+                mx = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1])) * s_l2;
                 // raise the reference max only when a score exceeds it by 2^8
                 raise = mx > m_run + 8.0f;
                 m_new = raise ? mx : m_run;
-                m_ref = m_new == -INFINITY ? 0.f : m_new;
+                m_off = (m_new == -INFINITY ? 0.f : m_new) - l2sig;
             } else if (k < 28) {
                 if (k == 9) alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
                 const int r = k - 10;
                 if (r >= 2 && r < 18) psum += cur[r - 2];
                 if (r >= 1 && r < 17) cur[r - 1] = __builtin_amdgcn_exp2f(cur[r - 1]);
-                if (r >= 0 && r < 16) cur[r] = __builtin_fmaf(cur[r], a.scale_log2, -m_ref);
+                if (r >= 0 && r < 16) cur[r] = __builtin_fmaf(cur[r], s_l2, -m_off);
             } else {
                 const int r = 2 * (k - 28);   // entries r, r+1 -> one packed pair of P
                 pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3)] = (__bf16)cur[r];
@@ -361,10 +486,11 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
 
         if (has_next) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                score_mfma(nxt, kb[ks % PFK], ks);
-                if (ks + PFK < KS) kb[ks % PFK] = kld(kbs, rbs, ks + PFK);
-                softmax_slice(ks);
+            for (int i = 0; i < KS; ++i) {
+                score_mfma(nxt, kb[i % PFK], i);
+                if (i + PFK < KS) kb[i % PFK] = kld(kbs, rbs, kstep(i + PFK));
+                if (FP8 && i == DR / 16 - 1) rope_to_latent_scale(nxt, 1.0f / sig_next);
+                softmax_slice(i);
                 __builtin_amdgcn_sched_barrier(0);
             }
             asm volatile("s_nop 15" : "+v"(nxt));
@@ -384,7 +510,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
                 asm volatile("" : "+a"(oacc[mb]));
             }
         }
-        l_lane = l_lane * alpha + psum;
+        l_lane = l_lane * alpha + (FP8 ? psum / sig_cur : psum);
         m_run = m_new;
 
         // value MFMAs: O^T[512 x 32] += V^T[512 x 32 tok] . P^T[32 tok x 32]
@@ -400,6 +526,20 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
             if (i + PF < 2 * MBLOCKS) vb[i % PF] = vld(vbs, i + PF);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i + PF < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        if constexpr (FP8) {
+            // stage st+2: wait for this wave's copy (stage st+3's may still be
+            // in flight), then convert it into the buffer of stage st-1, free
+            // since the barrier above; the next iteration's barrier publishes it
+            if (st + 2 < nst_live) {
+                if (st + 3 < nst_live)
+                    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();   // every wave's copy of stage st+2 has landed
+                convert(st + 2);
+            }
+            sig_cur = sig_next;
         }
     };
 
@@ -456,13 +596,15 @@ hipError_t launch_decode_bf16_mfma(const DecodeArgs &a, hipStream_t s) {
     // a multiple of 8 workgroups, one per (item, row chunk) plus padding
     const int units = a.num_items * a.row_chunks;
     dim3 grid((unsigned)((units + 7) / 8) * 8);
-    hipLaunchKernelGGL(decode_bf16_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_fp8_mfma(const DecodeArgs &a, hipStream_t s) {
-    // fp8 MFMA path not instantiated yet: the generic kernel serves fp8 caches
-    return launch_decode_generic(a, s);
+    const int units = a.num_items * a.row_chunks;
+    dim3 grid((unsigned)((units + 7) / 8) * 8);
+    hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace mla

@@ -108,8 +108,28 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
         if (seq_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %d < 0", b, seq_lens_host[b]);
         total_blocks += (seq_lens_host[b] + kBlock - 1) / kBlock;
     }
-    // Per-item share: spread all (block, row-chunk) work over the compute units.
+    // Per-item share: spread all (block, row-chunk) work over the compute
+    // units.  The balanced share ceil(total / CUs) can leave more work units
+    // than compute units on ragged batches (each sequence rounds its split
+    // count up), which costs a second round of workgroups; take instead the
+    // smallest share whose units fit in one round, when one exists.
+    int64_t max_nb = 0;
+    for (int b = 0; b < B; ++b) max_nb = std::max<int64_t>(max_nb, (seq_lens_host[b] + kBlock - 1) / kBlock);
+    auto units_for = [&](int64_t sh) {
+        int64_t u = 0;
+        for (int b = 0; b < B; ++b) u += (seq_lens_host[b] + kBlock - 1) / kBlock / sh +
+                                         (((seq_lens_host[b] + kBlock - 1) / kBlock) % sh != 0);
+        return u * row_chunks;
+    };
     int64_t share = std::max<int64_t>(1, (total_blocks * row_chunks + num_cus - 1) / num_cus);
+    if (max_nb > 0 && units_for(share) > num_cus && units_for(max_nb) <= num_cus) {
+        int64_t lo = share, hi = max_nb;   // units_for(hi) fits, units_for(lo) does not
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) / 2;
+            (units_for(mid) <= num_cus ? hi : lo) = mid;
+        }
+        share = hi;
+    }
 
     int64_t num_items = 0, num_partials = 0;
     int32_t max_splits = 0;

@@ -188,3 +188,20 @@ def test_cache_bytes():
     assert lib().mla_cache_bytes(ctypes.byref(_desc(num_blocks=3, kv_dtype=L.DT_FP8_E4M3))) == 3 * 40960
     assert lib().mla_cache_bytes(ctypes.byref(_desc(num_blocks=1, kv_dtype=L.DT_F32, d_c=64, d_r=16))) == 64 * 80 * 4
     assert lib().mla_cache_bytes(ctypes.byref(_desc(block_size=32))) == 0
+
+
+def test_plan_fits_one_round_on_ragged_batches():
+    """Ragged batches: the share is the smallest whose (item, row chunk) units
+    fit in one round of workgroups, so no compute unit runs two."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    for B, lo, hi, q_len, cus in [(64, 1024, 8192, 2, 256), (128, 1, 32768, 1, 256), (4, 65536, 131072, 1, 256),
+                                  (7, 1, 5000, 1, 16)]:
+        seq = rng.integers(lo, hi + 1, size=B).tolist()
+        info, p = plan(seq, q_len=q_len, cus=cus)
+        nb = [(S + 63) // 64 for S in seq]
+        units = lambda sh: sum(-(-n // sh) for n in nb) * info.row_chunks
+        assert info.num_items * info.row_chunks == units(info.blocks_per_item)
+        assert units(info.blocks_per_item) <= cus
+        if info.blocks_per_item > 1:
+            assert units(info.blocks_per_item - 1) > cus
