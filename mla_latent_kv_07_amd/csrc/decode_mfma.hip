@@ -63,7 +63,8 @@ constexpr int NSTAGE8 = 3;
 template <bool FP8>
 constexpr int lds_bytes() { return FP8 ? NSTAGE8 * STAGE_BYTES + 2 * FP8_STAGE : NSTAGE * STAGE_BYTES; }
 static_assert(lds_bytes<false>() <= 160 * 1024 && lds_bytes<true>() <= 160 * 1024, "stage buffers exceed LDS");
-static_assert(4 * 36864 <= lds_bytes<true>() && 4 * 36864 <= lds_bytes<false>(), "query staging exceeds LDS");
+static_assert(4 * 18432 <= 2 * STAGE_BYTES, "query halves exceed stage buffers 0-1");
+static_assert(2 * STAGE_BYTES <= NSTAGE8 * STAGE_BYTES, "fp8: query halves overlap the staging buffers");
 static_assert(4 * 32 * O_PITCH <= lds_bytes<true>() && 4 * 32 * O_PITCH <= lds_bytes<false>(),
               "epilogue staging exceeds the LDS allocation");
 
@@ -200,7 +201,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         return __int_as_float(sload((const int32_t *)a.block_scales, blk_id(st)));
     };
     auto stage_off = [&](int st) {
-        return FP8 ? (uint32_t)((st % NSTAGE8) * STAGE_BYTES) : (uint32_t)((st & (NSTAGE - 1)) * STAGE_BYTES);
+        // bf16: stage st in buffer (st + 2) mod 4 (buffers 0-1 hold the queries
+        // while stages 0-1 are copied)
+        return FP8 ? (uint32_t)((st % NSTAGE8) * STAGE_BYTES) : (uint32_t)(((st + 2) & (NSTAGE - 1)) * STAGE_BYTES);
     };
     auto staging_off = [&](int st) { return (uint32_t)(NSTAGE8 * STAGE_BYTES + (st & 1) * FP8_STAGE); };
     const uint32_t l16 = lane << 4;
@@ -216,45 +219,67 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     };
 
     // ---- queries -> VGPRs (MFMA B fragments: lane (ln, g) holds, for k-step
-    // ks, bytes 32 ks + 16 g .. +15 of row ln's 1152).  Each wave copies its 32
-    // rows into its own 36 KiB region of the not yet used stage buffers with
-    // coalesced 1 KiB copies: latent row r with its 16-byte chunks XOR-swizzled
-    // by r & 15 (lane i fetches chunk i ^ (r & 15)), so that 16 rows reading
-    // one chunk hit 16 distinct bank groups; the rotary parts as
-    // [r >> 3][chunk][r & 7].  Rows past the end of the sequence's rows read
-    // its last row (their scores are masked).
+    // ks, bytes 32 ks + 16 g .. +15 of row ln's 1152), in two halves of 16
+    // rows so that the copies of stages 0 and 1 start with the first half.
+    // Each wave copies a half into its own 18 KiB region of stage buffers 0-1
+    // (stages 0 and 1 go to buffers 2-3) with coalesced 1 KiB copies: latent
+    // row r with its 16-byte chunks XOR-swizzled by r & 15 (lane i fetches
+    // chunk i ^ (r & 15)), so that 16 rows reading one chunk hit 16 distinct
+    // bank groups; the rotary parts as [r >> 3][chunk][r & 7].  Lanes of rows
+    // 0-15 read the first half, lanes of rows 16-31 the second.  Rows past
+    // the end of the sequence's rows read its last row (their scores are
+    // masked).  VMEM loads complete in order, so waiting for the second half
+    // also waits for stages 0 and 1.
     bf16x8 qf[KS];
     {
-        const uint32_t qreg = smem_addr + wave * 36864;
+        const uint32_t qreg = smem_addr + wave * 18432;
         const int row_base = chunk * kRowsPerChunk + wave * 32;   // first row of this wave
         const int64_t seq_row0 = (int64_t)b * a.rows;
         const uint8_t *qlat = (const uint8_t *)a.q_lat + seq_row0 * CB;
         const uint8_t *qrope = (const uint8_t *)a.q_rope + seq_row0 * RB;
+        auto copy_half = [&](int h) {
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const int rr = min(row_base + r, a.rows - 1);
-            dma16(qreg + r * CB, l16 ^ (uint32_t)((r & 15) << 4), qlat + (int64_t)rr * CB);
+            for (int r = 0; r < 16; ++r) {
+                const int rr = min(row_base + 16 * h + r, a.rows - 1);
+                dma16(qreg + r * CB, l16 ^ (uint32_t)(r << 4), qlat + (int64_t)rr * CB);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                // lane i = 8 c + u: chunk c of row 16 h + 8 q + u
+                const int rr = min(row_base + 16 * h + 8 * q + (lane & 7), a.rows - 1);
+                dma16(qreg + 16 * CB + q * 1024, (uint32_t)(rr * RB + 16 * (lane >> 3)), qrope);
+            }
+        };
+        lds_u8 *qw = smem + wave * 18432;
+        const int lr = ln & 15;
+        auto read_half = [&]() {
+#pragma unroll
+            for (int ks = 0; ks < KC; ++ks)
+                qf[ks] = *(const bf16x8 *)(qw + lr * CB + (((2 * ks + g) ^ lr) << 4));
+#pragma unroll
+            for (int j = 0; j < DR / 16; ++j)
+                qf[KC + j] = *(const bf16x8 *)(qw + 16 * CB + (lr >> 3) * 1024 + (2 * j + g) * 128 + (lr & 7) * 16);
+        };
+        copy_half(0);
+        issue(0);
+        if (nst_live > 1) issue(1);
+        // the first half has landed when at most the stage copies are in flight
+        if (nst_live > 1) {
+            if constexpr (FP8) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        } else {
+            if constexpr (FP8) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            // lane i = 8 c + u: chunk c of row 8 q + u
-            const int rr = min(row_base + 8 * q + (lane & 7), a.rows - 1);
-            dma16(qreg + 32 * CB + q * 1024, (uint32_t)(rr * RB + 16 * (lane >> 3)), qrope);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies are in LDS
-        lds_u8 *qw = smem + wave * 36864;
-#pragma unroll
-        for (int ks = 0; ks < KC; ++ks)
-            qf[ks] = *(const bf16x8 *)(qw + ln * CB + (((2 * ks + g) ^ (ln & 15)) << 4));
-#pragma unroll
-        for (int j = 0; j < DR / 16; ++j)
-            qf[KC + j] = *(const bf16x8 *)(qw + 32 * CB + (ln >> 3) * 1024 + (2 * j + g) * 128 + (ln & 7) * 16);
+        if (ln < 16) read_half();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the region is refilled
+        copy_half(1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // second half, stages 0 and 1
+        if (ln >= 16) read_half();
     }
-    __syncthreads();   // every wave holds its queries: the stage buffers are free
-    issue(0);
-    if (nst_live > 1) issue(1);
-    if (!FP8 && nst_live > 2) issue(2);
-
+    // every wave holds its queries (the query regions are free) and every
+    // wave's copies of stages 0 and 1 are visible
+    __syncthreads();
     f32x16 oacc[MBLOCKS];
 #pragma unroll
     for (int mb = 0; mb < MBLOCKS; ++mb) oacc[mb] = f32x16{};
@@ -368,25 +393,15 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     // ---- prologue: score of stage 0
     float sig_cur = 1.f, sig_next = 1.f;   // block scales of stages st, st+1 (fp8)
     if constexpr (FP8) {
-        // stages 0 and 1 land in the staging buffers and are converted; stage 2
-        // then takes stage 0's staging buffer
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // stages 0 and 1 landed in the staging buffers and are converted;
+        // stage 2 then takes stage 0's staging buffer
         convert(0);
         if (nst_live > 1) convert(1);
         __syncthreads();
         if (nst_live > 2) issue(2);
         sig_cur = sigma(0);
     } else {
-        // wait for this wave's copy of stage 0; the barrier makes every wave's
-        // copies visible
-        if (nst_live > 2)
-            asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-        else if (nst_live > 1)
-            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        if (nst_live > 2) issue(2);
         zero_tail(0);
     }
     f32x16 sA, sB;
