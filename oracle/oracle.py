@@ -29,9 +29,10 @@ __all__ = [
     "PIN_STATUS", "FMT_F32", "FMT_BF16", "FMT_FP8_E4M3", "BLOCK",
     "lib", "build_oracle", "threads",
     "kv_bytes_per_token_layer", "kv_cache_bytes", "floats_per_token_all_layers",
-    "bf16_bits_to_f64", "e4m3_to_f64", "f64_to_e4m3", "block_bytes",
+    "bf16_bits_to_f64", "e4m3_to_f64", "f64_to_e4m3", "f64_to_bf16", "block_bytes",
     "gather", "decode", "combine", "decode_splits",
-    "rope", "project_kv", "project_queries_direct", "project_queries_lowrank",
+    "rope", "rope_inv_freq", "project_kv", "project_queries_direct", "project_queries_lowrank",
+    "cache_append", "project_queries_absorbed", "E4M3_MAX",
     "absorb_q", "absorb_out", "fused_out_weights", "absorb_out_fused",
     "score_split", "unabsorbed_mha",
 ]
@@ -55,6 +56,17 @@ PIN_STATUS = {
               "causal q_len=2 == q_len=1 on the truncated sequence",
     "combine": "pinned: split invariance against the unsplit decode for random partitions",
     "rope": "pinned: norm preservation, relative-position property, complex-multiply form",
+    "rope_inv_freq": "pinned: factor 1 is plain RoPE; YaRN's two limits (position interpolation p/s "
+                     "below beta_slow, plain RoPE above beta_fast) in closed form; relative-position "
+                     "property and the mscale norm factor with the scaled frequencies",
+    "f64_to_bf16": "pinned: torch's fp32->bf16 cast on fp32-exact values incl. ties and subnormals; "
+                   "nearest of the two neighbours (independently pinned decoder) on fp64 values",
+    "cache_append": "pinned: appended rows gather back as the single rounding of project_kv's rows "
+                    "(bf16, f32) over ragged call sizes; bytes outside written slots unchanged; fp8 "
+                    "whole-block scale = amax/448 with codes within half an e4m3 step; scale growth "
+                    "re-encodes earlier rows within two roundings; all-zero block takes scale 1",
+    "project_queries_lowrank": "pinned: equals the one-matrix projection with merged per-head weights",
+    "project_queries_absorbed": "pinned: absorbed scores equal scores against explicitly reconstructed keys",
     "absorb_q": "pinned: absorbed score equals score against explicitly reconstructed keys",
     "absorb_out": "pinned: equals explicit per-head value reconstruction followed by W^O",
     "absorb_out_fused": "pinned: W^UV W^O fusion equals the unfused path",
@@ -202,6 +214,23 @@ def f64_to_e4m3(x: np.ndarray) -> np.ndarray:
     return out.reshape(np.shape(x))
 
 
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns, rounded once to nearest-even from
+    the fp64 value (8 significant bits, binary32's exponent range with
+    subnormals; overflow -> inf; NaN -> quiet NaN)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
+    fin = np.isfinite(x)
+    a = np.abs(np.where(fin, x, 0.0))
+    m, e = np.frexp(a)                          # a = m 2^e, m in [0.5, 1)
+    e = np.maximum(e, -125)                     # below 2^-126 the spacing stays 2^-133
+    q = np.ldexp(np.rint(np.ldexp(a, 8 - e)), e - 8)   # rint: half to even
+    q = np.where(q > 3.3895313892515355e38, np.inf, q)  # past the largest finite bf16
+    out[...] = np.where(fin, np.copysign(q, x), x)
+    bits = (out.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return np.where(np.isnan(x), np.uint16(0x7FC0), bits)
+
+
 def block_bytes(fmt: int, d_c: int, d_r: int) -> int:
     return int(lib().oracle_block_bytes(fmt, d_c, d_r))
 
@@ -291,32 +320,67 @@ def decode_splits(pool, fmt, block_table, seq_lens, q_lat, q_rope, scale, bounds
 # Projections, RoPE and the un-absorbed reference (numpy, fp64)
 # ----------------------------------------------------------------------------
 
-def rope(x: np.ndarray, positions: np.ndarray, base: float = 10000.0) -> np.ndarray:
+def rope_inv_freq(d: int, base: float = 10000.0, factor: float = 1.0, orig_ctx: float = 4096.0,
+                  beta_fast: float = 32.0, beta_slow: float = 1.0) -> np.ndarray:
+    """Angular frequency theta_j of rotary pair j (j < d/2), in fp64.
+
+    Plain RoPE (factor == 1): theta_j = base^(-2j/d) ([huny] §2-3 decoupled
+    RoPE; [donmain] "위치 정보와 압축의 충돌").  The pages name YaRN for
+    128K+ contexts and say only that its base frequency and scaling factor
+    must match the model ([huny] §6, the YaRN item); they give no formula.
+    This follows the published YaRN method (Peng et al., 2023, "NTK-by-parts"
+    interpolation): pair j turns r_j = orig_ctx * theta_j / (2 pi) times over
+    the original context; pairs with r_j <= beta_slow are interpolated
+    (theta_j / factor), pairs with r_j >= beta_fast keep theta_j, and a
+    linear ramp gamma = (r_j - beta_slow) / (beta_fast - beta_slow) blends
+    the two in between: theta'_j = (1 - gamma) theta_j / factor + gamma theta_j."""
+    assert d % 2 == 0 and factor > 0
+    j = np.arange(d // 2, dtype=np.float64)
+    theta = base ** (-2.0 * j / d)
+    if factor == 1.0:
+        return theta
+    r = orig_ctx * theta / (2.0 * math.pi)
+    if beta_fast > beta_slow:
+        gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
+    else:
+        gamma = (r >= beta_fast).astype(np.float64)
+    return (1.0 - gamma) * theta / factor + gamma * theta
+
+
+def rope(x: np.ndarray, positions: np.ndarray, base: float = 10000.0, *,
+         inv_freq: np.ndarray | None = None, mscale: float = 1.0) -> np.ndarray:
     """Rotary position embedding of the last axis (decoupled RoPE input,
     [huny] §2-3; [donmain] "위치 정보와 압축의 충돌").  The pages do not fix
     the pairing: adjacent pairs (2j, 2j+1) are rotated by angle p * theta_j
-    with theta_j = base^(-2j/d).  positions broadcasts against x[..., 0]."""
+    with theta_j = base^(-2j/d), or the given inv_freq (rope_inv_freq's YaRN
+    frequencies); the result is multiplied by mscale (YaRN's magnitude
+    factor, 1 for plain RoPE).  positions broadcasts against x[..., 0]."""
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     assert d % 2 == 0
-    j = np.arange(d // 2, dtype=np.float64)
-    theta = base ** (-2.0 * j / d)
+    if inv_freq is None:
+        j = np.arange(d // 2, dtype=np.float64)
+        theta = base ** (-2.0 * j / d)
+    else:
+        theta = np.asarray(inv_freq, dtype=np.float64)
+        assert theta.shape == (d // 2,)
     ang = np.asarray(positions, dtype=np.float64)[..., None] * theta
     cos, sin = np.cos(ang), np.sin(ang)
     x0, x1 = x[..., 0::2], x[..., 1::2]
     out = np.empty_like(x)
     out[..., 0::2] = x0 * cos - x1 * sin
     out[..., 1::2] = x0 * sin + x1 * cos
-    return out
+    return out * mscale if mscale != 1.0 else out
 
 
-def project_kv(h: np.ndarray, w_dkv: np.ndarray, d_c: int, positions: np.ndarray):
+def project_kv(h: np.ndarray, w_dkv: np.ndarray, d_c: int, positions: np.ndarray, *,
+               inv_freq: np.ndarray | None = None, mscale: float = 1.0):
     """Cached row of each token: c = h W^DKV ([huny] §2-1 compression equation)
     and k^R = RoPE(h W^KR) ([huny] §2-3 shared rotary key).  W^DKV and W^KR
     are read as the first d_c and the remaining columns of one matrix."""
     z = np.asarray(h, np.float64) @ np.asarray(w_dkv, np.float64)
     c = z[:, :d_c]
-    kr = rope(z[:, d_c:], positions)
+    kr = rope(z[:, d_c:], positions, inv_freq=inv_freq, mscale=mscale)
     return c, kr
 
 
@@ -330,15 +394,107 @@ def project_queries_direct(h: np.ndarray, w_q: np.ndarray, n_h: int, d_nope: int
     return q_nope, q_rope
 
 
-def project_queries_lowrank(h, w_dq, w_uq, w_qr, n_h, d_nope, d_r, positions):
+def project_queries_lowrank(h, w_dq, w_uq, w_qr, n_h, d_nope, d_r, positions, *,
+                            inv_freq=None, mscale=1.0):
     """Low-rank query path: c^Q = h W^DQ, q^C_i = c^Q W^UQ_i ([huny] §2-2), and
     q^R_i = RoPE(h W^QR_i) ([huny] §2-3, read literally from h)."""
     h = np.asarray(h, np.float64)
     cq = h @ np.asarray(w_dq, np.float64)
     q_nope = (cq @ np.asarray(w_uq, np.float64)).reshape(-1, n_h, d_nope)
     q_rope = rope((h @ np.asarray(w_qr, np.float64)).reshape(-1, n_h, d_r),
-                  np.asarray(positions)[:, None])
+                  np.asarray(positions)[:, None], inv_freq=inv_freq, mscale=mscale)
     return q_nope, q_rope
+
+
+def project_queries_absorbed(h, w_dq, w_uq, w_qr, w_uk, n_h, d_nope, d_r, positions, *,
+                             inv_freq=None, mscale=1.0):
+    """The decode's query inputs straight from the hidden state: the low-rank
+    query path ([huny] §2-2, §2-3) followed by the W^UK absorption ([huny]
+    §3-1).  Returns (q_lat [T][n_h][d_c], q_rope [T][n_h][d_r])."""
+    q_nope, q_rope = project_queries_lowrank(h, w_dq, w_uq, w_qr, n_h, d_nope, d_r, positions,
+                                             inv_freq=inv_freq, mscale=mscale)
+    return absorb_q(q_nope, w_uk), q_rope
+
+
+E4M3_MAX = 448.0   # largest finite OCP E4M3 value
+
+
+def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, pos0,
+                 q_len: int, h, w_kv, *, inv_freq=None, mscale: float = 1.0) -> None:
+    """Write the cache rows of q_len new tokens per sequence, in place.
+
+    Token t = b q_len + i of sequence b sits at position p = pos0[b] + i.  Its
+    row [c | k^R] = project_kv(h_t) at p ([huny] §2-1 compression equation,
+    §2-3 shared rotary key) goes to slot p % 64 of block block_table[b][p // 64]
+    (paged cache of 64-token blocks, [vllm] "FlashMLABackend" and
+    "FlashMLAImpl").  The exact fp64 row is rounded once into the storage
+    format: f32 / bf16 rows to nearest-even.
+
+    fp8 (e4m3 latent, bf16 k^R, one scale per block: [huny] §6 FP8 item) — the
+    pages ask for a dynamic per-block scale and give no update rule for a
+    block that fills over several calls.  Reading used here:
+      - a block whose slot 0 is written by this call starts fresh: its scale
+        is amax|c| over the tokens written into it / 448 (1 if that is 0),
+        as for a block written whole;
+      - otherwise scale' = max(scale, amax / 448); when it grows, the codes
+        of the slots before the first one written are re-encoded,
+        code' = e4m3(value(code) * scale / scale');
+      - the new codes are e4m3(c / scale').
+    Scales are kept as float32; the codes use the stored float32 value.
+    pool: uint8 [num_blocks][block_bytes]; block_scales: float32 [num_blocks]
+    (fp8 only).  Both are modified."""
+    pool = np.asarray(pool)
+    bt = np.asarray(block_table)
+    pos0 = np.asarray(pos0)
+    B = bt.shape[0]
+    T = B * q_len
+    pos = (pos0[:, None].astype(np.int64) + np.arange(q_len)[None, :]).reshape(T)
+    c, kr = project_kv(h, w_kv, d_c, pos, inv_freq=inv_freq, mscale=mscale)
+    nblk_pool = pool.shape[0]
+    if fmt in (FMT_F32, FMT_BF16):
+        rows = np.concatenate([c, kr], axis=1)
+        if fmt == FMT_BF16:
+            enc = f64_to_bf16(rows).view(np.uint8).reshape(T, -1)
+        else:
+            enc = rows.astype(np.float32).view(np.uint8).reshape(T, -1)
+        rb = enc.shape[1]
+        for t in range(T):
+            b, p = t // q_len, int(pos[t])
+            blk = int(bt[b, p // BLOCK])
+            assert 0 <= blk < nblk_pool
+            pool[blk, (p % BLOCK) * rb:(p % BLOCK + 1) * rb] = enc[t]
+        return
+    assert fmt == FMT_FP8_E4M3
+    scales = np.asarray(block_scales)
+    kr_bits = f64_to_bf16(kr).view(np.uint8).reshape(T, -1)
+    for b in range(B):
+        # the sequence's tokens, grouped by the block they land in (in order)
+        groups: dict[int, list[int]] = {}
+        for i in range(q_len):
+            p = int(pos[b * q_len + i])
+            groups.setdefault(p // BLOCK, []).append(i)
+        for lb, idx in groups.items():
+            blk = int(bt[b, lb])
+            assert 0 <= blk < nblk_pool
+            toks = [b * q_len + i for i in idx]
+            slots = [int(pos[t]) % BLOCK for t in toks]
+            amax = float(np.max(np.abs(c[toks])))
+            fresh = min(slots) == 0
+            new = amax / E4M3_MAX
+            if fresh:
+                sc = float(np.float32(new if amax > 0 else 1.0))
+            else:
+                old = float(scales[blk])
+                sc = float(np.float32(max(old, new)))
+                if sc > old:
+                    s0 = min(slots)
+                    codes = pool[blk, :s0 * d_c]
+                    pool[blk, :s0 * d_c] = f64_to_e4m3(e4m3_to_f64(codes) * (old / sc))
+            scales[blk] = np.float32(sc)
+            for t, sl in zip(toks, slots):
+                pool[blk, sl * d_c:(sl + 1) * d_c] = f64_to_e4m3(c[t] / sc)
+                off = BLOCK * d_c + sl * 2 * d_r
+                pool[blk, off:off + 2 * d_r] = kr_bits[t]
 
 
 def absorb_q(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
