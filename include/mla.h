@@ -250,6 +250,94 @@ mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *bloc
                               int32_t bt_stride, const int32_t *seq_lens, int32_t B,
                               int32_t max_tokens, void *out, mla_stream_t stream);
 
+/*
+ * Rotary embedding of the decoupled RoPE parts (huny §2-3 rotary key and
+ * rotary query; donmain "위치 정보와 압축의 충돌").  Adjacent pairs
+ * (2j, 2j+1) of a d_r-wide vector at position p turn by p * theta'_j and the
+ * result is multiplied by mscale.
+ *   factor == 1: plain RoPE, theta'_j = base^(-2j/d_r).
+ *   factor  > 1: YaRN.  The huny page (§6, YaRN item) names the method for
+ *     128K+ contexts and asks that base and scaling factor match the model,
+ *     with no formula; this follows the published YaRN "NTK-by-parts" rule:
+ *     pair j turns r_j = orig_ctx * theta_j / (2 pi) times over the original
+ *     context; gamma_j = clamp((r_j - beta_slow) / (beta_fast - beta_slow), 0, 1);
+ *     theta'_j = (1 - gamma_j) theta_j / factor + gamma_j theta_j.
+ *     YaRN's magnitude factor (0.1 ln(factor) + 1 in the published method)
+ *     is the caller's mscale; a model that folds it into the softmax scale
+ *     passes 1 here.
+ * Angles are formed and rotated from fp64 p * theta'_j.
+ */
+typedef struct {
+    double base;        /* > 1, e.g. 10000 */
+    double factor;      /* > 0; 1 = plain RoPE */
+    double orig_ctx;    /* original context length (factor != 1) */
+    double beta_fast;   /* pairs turning >= beta_fast times keep theta_j */
+    double beta_slow;   /* pairs turning <= beta_slow times use theta_j / factor */
+    double mscale;      /* > 0; multiplies every rotated vector */
+} mla_rope_t;
+
+/* theta'_j for j < d_r/2 into theta_host (host only, no HIP call).
+ * INVALID_ARG on NULLs, d_r odd, < 2 or > 256, or out-of-range fields. */
+mla_status_t mla_rope_freqs(const mla_rope_t *rope, int32_t d_r, double *theta_host);
+
+/*
+ * mla_cache_append — write the cache rows of q_len new tokens per sequence
+ * (huny §2-1 compression equation c = h W^DKV and §2-3 shared rotary key
+ * k^R = RoPE(h W^KR); the row [c | k^R] is the kv_c_and_k_pe cache row of
+ * the vLLM MLA page, "FlashMLAImpl"):
+ *   token t = b * q_len + i of sequence b, at position p = pos0[b] + i:
+ *   [c | k^R] = h[t] . w_kv, k^R rotated at p (see mla_rope_t), stored in
+ *   slot p % 64 of block block_table[b][p / 64].
+ * h [T][d_model], w_kv [d_model][d_c + d_r] (W^DKV then W^KR columns), both
+ * dt (F32 or BF16); accumulation in fp32; pos0 [B] int32 (device).  The block
+ * table must already hold blocks for every written position; ids outside
+ * [0, num_blocks) are clamped, and tokens at p < 0 or p >= 64 bt_stride
+ * are not written.  Storage: F32 / BF16 rows rounded once to
+ * nearest even.  FP8_E4M3 (huny §6 FP8 item: a dynamic scale per block; the
+ * pages give no update rule — the reading here): a block whose slot 0 is
+ * written by this call takes scale amax|c| / 448 over the tokens written
+ * into it (1 if 0); otherwise scale' = max(scale, amax / 448), and when it
+ * grows the codes of the slots before the first written one are re-encoded
+ * at scale' (code' = e4m3(value(code) * scale / scale')).  New codes are
+ * e4m3(c / scale') (nearest even, saturating at 448); k^R is bf16.
+ * cache->base and cache->block_scales are written (the descriptor's const
+ * describes the decode's use).  Sequences of one call must be distinct.
+ * workspace: >= mla_cache_append_workspace() bytes, 256-byte aligned (fp32
+ * partial products).  rope may be NULL only when d_r == 0.
+ * Errors: INVALID_ARG, UNSUPPORTED (dt, cache format), ALIGN, WORKSPACE, HIP.
+ */
+int64_t mla_cache_append_workspace(int32_t T, int32_t d_model, int32_t d_c, int32_t d_r,
+                                   mla_dtype_t dt);
+mla_status_t mla_cache_append(const void *h, const void *w_kv, mla_dtype_t dt,
+                              const mla_cache_desc_t *cache, const int32_t *block_table,
+                              int32_t bt_stride, const int32_t *pos0, int32_t B, int32_t q_len,
+                              int32_t d_model, const mla_rope_t *rope, void *workspace,
+                              int64_t workspace_bytes, mla_stream_t stream);
+
+/*
+ * mla_project_q — the decode's query inputs straight from the hidden states
+ * (huny §2-2 low-rank query c^Q = h W^DQ, q^C_i = c^Q W^UQ_i; §2-3 rotary
+ * query q^R_i = RoPE(h W^QR_i), read from h as written there; §3-1 absorption
+ * q~_i = q^C_i W^UK_i^T):
+ *   q_lat [T][n_h][d_c] = q~,  q_rope [T][n_h][d_r] = q^R rotated at pos[t].
+ * h [T][d_model], w_dq [d_model][q_lora], w_uq [q_lora][n_h d_nope] (head i
+ * = columns i d_nope ..), w_qr [d_model][n_h d_r], w_uk [n_h][d_c][d_nope];
+ * all dt (F32 or BF16), pos [T] int32 (device).  fp32 accumulation; on the
+ * bf16 MFMA path c^Q and q^C are rounded to bf16 between the products.
+ * W^UQ and W^UK stay two products: the merged W^UQ W^UK^T would hold
+ * n_h * q_lora * d_c weights against q_lora * n_h * d_nope + n_h * d_c *
+ * d_nope (201 MB against 67 MB at the DeepSeek-V2 shape).
+ * workspace >= mla_project_q_workspace() bytes, 256-byte aligned.
+ */
+int64_t mla_project_q_workspace(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h,
+                                int32_t d_nope, int32_t d_c, int32_t d_r, mla_dtype_t dt);
+mla_status_t mla_project_q(const void *h, const void *w_dq, const void *w_uq, const void *w_qr,
+                           const void *w_uk, mla_dtype_t dt, const int32_t *pos, int32_t T,
+                           int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope,
+                           int32_t d_c, int32_t d_r, const mla_rope_t *rope, void *q_lat,
+                           void *q_rope, void *workspace, int64_t workspace_bytes,
+                           mla_stream_t stream);
+
 /* Bytes of the whole pool described by `cache` (0 on bad arguments). */
 int64_t mla_cache_bytes(const mla_cache_desc_t *cache);
 

@@ -44,6 +44,14 @@ class Plan(ctypes.Structure):
         return {k: getattr(self, k) for k, _ in self._fields_}
 
 
+class Rope(ctypes.Structure):
+    """mla_rope_t: plain RoPE (factor 1) or YaRN-scaled frequencies."""
+    _fields_ = [
+        ("base", ctypes.c_double), ("factor", ctypes.c_double), ("orig_ctx", ctypes.c_double),
+        ("beta_fast", ctypes.c_double), ("beta_slow", ctypes.c_double), ("mscale", ctypes.c_double),
+    ]
+
+
 class MLAError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -78,11 +86,21 @@ def load() -> ctypes.CDLL:
     L.mla_gather_paged.argtypes = [ctypes.POINTER(CacheDesc), P, c_int32, P, c_int32, c_int32, P, P]
     L.mla_cache_bytes.argtypes = [ctypes.POINTER(CacheDesc)]
     L.mla_cache_bytes.restype = c_int64
+    L.mla_rope_freqs.argtypes = [ctypes.POINTER(Rope), c_int32, P]
+    L.mla_cache_append_workspace.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32]
+    L.mla_cache_append_workspace.restype = c_int64
+    L.mla_cache_append.argtypes = [P, P, c_int32, ctypes.POINTER(CacheDesc), P, c_int32, P, c_int32,
+                                   c_int32, c_int32, ctypes.POINTER(Rope), P, c_int64, P]
+    L.mla_project_q_workspace.argtypes = [c_int32] * 8
+    L.mla_project_q_workspace.restype = c_int64
+    L.mla_project_q.argtypes = [P, P, P, P, P, c_int32, P, c_int32, c_int32, c_int32, c_int32,
+                                c_int32, c_int32, c_int32, ctypes.POINTER(Rope), P, P, P, c_int64, P]
     L.mla_last_error.restype = ctypes.c_char_p
     L.mla_version.restype = ctypes.c_char_p
     for name in ("mla_decode_plan", "mla_decode", "mla_decode_partial", "mla_decode_finish",
                  "mla_combine_lse", "mla_absorb_q",
-                 "mla_absorb_out", "mla_gather_paged"):
+                 "mla_absorb_out", "mla_gather_paged", "mla_rope_freqs", "mla_cache_append",
+                 "mla_project_q"):
         getattr(L, name).restype = c_int32
     _lib = L
     return L

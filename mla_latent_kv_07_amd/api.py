@@ -173,3 +173,58 @@ def gather_paged(cache: DeviceCache, block_table, seq_lens, max_tokens, stream=N
     L.check(L.load().mla_gather_paged(ctypes.byref(desc), _p(block_table), block_table.stride(0),
                                       _p(seq_lens), B, max_tokens, _p(out), _stream(stream)))
     return out
+
+
+def rope(base=10000.0, factor=1.0, orig_ctx=4096.0, beta_fast=32.0, beta_slow=1.0, mscale=1.0) -> L.Rope:
+    """mla_rope_t (factor 1: plain RoPE; factor > 1: YaRN)."""
+    return L.Rope(base, factor, orig_ctx, beta_fast, beta_slow, mscale)
+
+
+def rope_freqs(cfg: L.Rope, d_r: int):
+    """mla_rope_freqs (host): the d_r/2 angular frequencies as a list."""
+    out = (ctypes.c_double * (d_r // 2))()
+    L.check(L.load().mla_rope_freqs(ctypes.byref(cfg), d_r, ctypes.cast(out, ctypes.c_void_p)))
+    return list(out)
+
+
+def cache_append_workspace_bytes(T, d_model, d_c, d_r, dtype) -> int:
+    return int(L.load().mla_cache_append_workspace(T, d_model, d_c, d_r, _DT[dtype]))
+
+
+def cache_append(h, w_kv, cache: DeviceCache, block_table, pos0, q_len: int, rope_cfg: L.Rope,
+                 ws=None, stream=None):
+    """mla_cache_append: h [B*q_len, d_model], w_kv [d_model, d_c + d_r]; writes
+    the rows of positions pos0[b] .. pos0[b] + q_len - 1 into `cache`."""
+    T, d_model = h.shape
+    B = T // q_len
+    need = cache_append_workspace_bytes(T, d_model, cache.d_c, cache.d_r, h.dtype)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=h.device)
+    desc = cache.desc()
+    L.check(L.load().mla_cache_append(_p(h), _p(w_kv), _DT[h.dtype], ctypes.byref(desc), _p(block_table),
+                                      block_table.stride(0), _p(pos0), B, q_len, d_model,
+                                      ctypes.byref(rope_cfg), _p(ws), ws.numel(), _stream(stream)))
+
+
+def project_q_workspace_bytes(T, d_model, q_lora, n_h, d_nope, d_c, d_r, dtype) -> int:
+    return int(L.load().mla_project_q_workspace(T, d_model, q_lora, n_h, d_nope, d_c, d_r, _DT[dtype]))
+
+
+def project_q(h, w_dq, w_uq, w_qr, w_uk, pos, n_h: int, d_nope: int, d_r: int, rope_cfg: L.Rope,
+              q_lat=None, q_rope=None, ws=None, stream=None):
+    """mla_project_q: h [T, d_model] -> (q_lat [T, n_h, d_c], q_rope [T, n_h, d_r])."""
+    T, d_model = h.shape
+    q_lora = w_dq.shape[1]
+    d_c = w_uk.shape[1]
+    dev, dt = h.device, h.dtype
+    if q_lat is None:
+        q_lat = torch.empty((T, n_h, d_c), dtype=dt, device=dev)
+    if q_rope is None:
+        q_rope = torch.empty((T, n_h, d_r), dtype=dt, device=dev)
+    need = project_q_workspace_bytes(T, d_model, q_lora, n_h, d_nope, d_c, d_r, dt)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    L.check(L.load().mla_project_q(_p(h), _p(w_dq), _p(w_uq), _p(w_qr), _p(w_uk), _DT[dt], _p(pos), T, d_model,
+                                   q_lora, n_h, d_nope, d_c, d_r, ctypes.byref(rope_cfg), _p(q_lat), _p(q_rope),
+                                   _p(ws), ws.numel(), _stream(stream)))
+    return q_lat, q_rope

@@ -50,7 +50,7 @@ struct GemmArgs {
     int64_t ldb, bsb;
     void *C;             // C + b * bsc + s * css + m * ldc + n (bf16 or fp32 elements)
     int64_t ldc, bsc, css;
-    int32_t M, N, K;     // K of one split
+    int32_t M, N, K;     // K of one split; N a multiple of 8
     int32_t splits;      // z = b * splits + s; split s covers k in [s K, (s + 1) K)
 };
 
@@ -85,11 +85,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
         const int mrow = min(m0 + row, g.M - 1) - m0;
         a_off[d] = (uint32_t)(((int64_t)mrow * g.lda + ((pos ^ ((row >> 1) & 7)) << 3)) * 2);
         if (B_KCONTIG) {
-            b_off[d] = (uint32_t)(((int64_t)row * g.ldb + ((pos ^ ((row >> 1) & 7)) << 3)) * 2);
+            // columns past N read column N-1 (never stored)
+            const int nrow = min(n0 + row, g.N - 1) - n0;
+            b_off[d] = (uint32_t)(((int64_t)nrow * g.ldb + ((pos ^ ((row >> 1) & 7)) << 3)) * 2);
         } else {
-            // B: wave w copies k rows 16w + 4d .. +3 (lane i: row + i/16, position i%16)
+            // B: wave w copies k rows 16w + 4d .. +3 (lane i: row + i/16, position i%16);
+            // 8-column chunks past N read the last chunk (never stored)
             const int krow = 16 * wave + 4 * d + (lane >> 4), p16 = lane & 15;
-            b_off[d] = (uint32_t)(((int64_t)krow * g.ldb + ((p16 ^ (4 * (krow & 3))) << 3)) * 2);
+            const int col = min(8 * (p16 ^ (4 * (krow & 3))), g.N - 8 - n0);
+            b_off[d] = (uint32_t)(((int64_t)krow * g.ldb + col) * 2);
         }
     }
     auto issue = [&](int st) {
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     for (int idx = threadIdx.x; idx < BM * (BN / 8); idx += 256) {
         const int m = idx / (BN / 8), c8 = idx % (BN / 8);
         if (m0 + m >= g.M) break;   // rows are visited in increasing order
+        if (n0 + 8 * c8 >= g.N) continue;
         const float4 v0 = *(const float4 *)(ct + m * C_PITCH + 8 * c8);
         const float4 v1 = *(const float4 *)(ct + m * C_PITCH + 8 * c8 + 4);
         const int64_t off = cb + (int64_t)(m0 + m) * g.ldc + n0 + 8 * c8;
@@ -232,7 +237,7 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict_
 
 template <bool B_KCONTIG, bool OUT_F32>
 hipError_t launch_gemm(const GemmArgs &g, int batch, hipStream_t st) {
-    dim3 grid((unsigned)(g.N / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)(batch * g.splits));
+    dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)(batch * g.splits));
     hipLaunchKernelGGL((gemm_bf16_kernel<B_KCONTIG, OUT_F32>), grid, dim3(256), 0, st, g);
     return hipGetLastError();
 }
@@ -247,6 +252,51 @@ int out_splits(int32_t T, int32_t K, int32_t d_model) {
 }
 
 }  // namespace
+
+// Split count for C[M][N] = A[M][K] B[K][N]: the smallest power of two that
+// gives at least 128 workgroups, with every split a whole number of 64-wide
+// stages (at most 16 splits).
+int gemm_splits(int32_t M, int32_t N, int32_t K) {
+    const int tiles = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+    int sp = 1;
+    while (sp < 16 && sp * tiles < 128 && K % (sp * 2 * BK) == 0) sp *= 2;
+    return sp;
+}
+
+bool gemm_nn_mfma_ok(int32_t N, int32_t K) { return N % 8 == 0 && N >= 8 && K % BK == 0; }
+
+// ws[s][m][n] = sum over k in split s of A[m][k] B[k][n] (bf16 in, fp32 out),
+// A k-contiguous with row stride lda, B n-contiguous with row stride ldb.
+hipError_t launch_gemm_nn_f32(const void *A, int64_t lda, const void *B, int64_t ldb, float *ws,
+                              int32_t M, int32_t N, int32_t K, int splits, hipStream_t s) {
+    GemmArgs g{};
+    g.A = (const uint16_t *)A; g.lda = lda; g.bsa = 0;
+    g.B = (const uint16_t *)B; g.ldb = ldb; g.bsb = 0;
+    g.C = ws; g.ldc = N; g.bsc = 0; g.css = (int64_t)M * N;
+    g.M = M; g.N = N; g.K = K / splits; g.splits = splits;
+    return launch_gemm<false, true>(g, 1, s);
+}
+
+// C[m][n] = bf16(A[m][k] B[k][n]), one split.
+hipError_t launch_gemm_nn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                               int64_t ldc, int32_t M, int32_t N, int32_t K, hipStream_t s) {
+    GemmArgs g{};
+    g.A = (const uint16_t *)A; g.lda = lda; g.bsa = 0;
+    g.B = (const uint16_t *)B; g.ldb = ldb; g.bsb = 0;
+    g.C = C; g.ldc = ldc; g.bsc = 0; g.css = 0;
+    g.M = M; g.N = N; g.K = K; g.splits = 1;
+    return launch_gemm<false, false>(g, 1, s);
+}
+
+// out[i] = bf16(sum_s ws[s][i]) for n8 groups of 8 elements
+hipError_t launch_split_sum_bf16(const float *ws, int splits, int64_t split_stride, int64_t n8,
+                                 void *out, hipStream_t s) {
+    const int64_t nb = (n8 + 255) / 256;
+    const unsigned grid = (unsigned)(nb < 4096 ? (nb < 1 ? 1 : nb) : 4096);
+    hipLaunchKernelGGL(split_sum_kernel, dim3(grid), dim3(256), 0, s, ws, splits, split_stride, n8,
+                       (uint16_t *)out);
+    return hipGetLastError();
+}
 
 bool absorb_q_mfma_ok(int32_t d_nope, int32_t d_c, mla_dtype_t dt) {
     return dt == MLA_DT_BF16 && d_nope % BK == 0 && d_c % BN == 0;

@@ -60,6 +60,30 @@ hipError_t launch_absorb_out(const void *o_lat, const void *w_uv, const void *w_
                              void *out, float *ws, int32_t T, int32_t n_h, int32_t d_c,
                              int32_t d_v, int32_t d_model, mla_dtype_t dt, hipStream_t s);
 
+// RoPE frequency table of one call (plain or YaRN), passed by value.
+constexpr int kMaxRopePairs = 128;
+struct RopeTab {
+    double theta[kMaxRopePairs];   // angle per position of pair j
+    float mscale;                  // factor on every rotated vector
+    int32_t half;                  // d_r / 2
+};
+bool rope_table(const mla_rope_t *r, int32_t d_r, RopeTab *t);
+
+int64_t cache_append_workspace(int32_t T, int32_t d_model, int32_t d_c, int32_t d_r, mla_dtype_t dt);
+hipError_t launch_cache_append(const void *h, const void *w_kv, mla_dtype_t dt, uint8_t *pool,
+                               float *scales, int64_t block_bytes, int64_t num_blocks,
+                               mla_dtype_t kv, const int32_t *bt, int32_t bt_stride,
+                               const int32_t *pos0, int32_t B, int32_t q_len, int32_t d_model,
+                               int32_t d_c, int32_t d_r, const RopeTab &rt, float *ws,
+                               hipStream_t s);
+int64_t project_q_workspace(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope,
+                            int32_t d_c, int32_t d_r, mla_dtype_t dt);
+hipError_t launch_project_q(const void *h, const void *w_dq, const void *w_uq, const void *w_qr,
+                            const void *w_uk, mla_dtype_t dt, const int32_t *pos, int32_t T,
+                            int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope, int32_t d_c,
+                            int32_t d_r, const RopeTab &rt, void *q_lat, void *q_rope, void *ws,
+                            hipStream_t s);
+
 // ---------------------------------------------------------------- device helpers
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

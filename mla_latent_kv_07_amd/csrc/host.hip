@@ -376,6 +376,93 @@ mla_status_t mla_absorb_out(const void *o_lat, const void *w_uv, const void *w_o
                       "absorb_out launch");
 }
 
+mla_status_t mla_rope_freqs(const mla_rope_t *rope, int32_t d_r, double *theta_host) {
+    if (!rope || !theta_host) return fail(MLA_ERR_INVALID_ARG, "NULL rope/theta_host");
+    RopeTab t;
+    if (!rope_table(rope, d_r, &t))
+        return fail(MLA_ERR_INVALID_ARG, "bad rope (d_r=%d base=%g factor=%g orig_ctx=%g mscale=%g)", d_r,
+                    rope->base, rope->factor, rope->orig_ctx, rope->mscale);
+    for (int j = 0; j < t.half; ++j) theta_host[j] = t.theta[j];
+    return ok();
+}
+
+int64_t mla_cache_append_workspace(int32_t T, int32_t d_model, int32_t d_c, int32_t d_r,
+                                   mla_dtype_t dt) {
+    if (T < 1 || d_model < 1 || d_c < 1 || d_r < 0) return 0;
+    return cache_append_workspace(T, d_model, d_c, d_r, dt);
+}
+
+mla_status_t mla_cache_append(const void *h, const void *w_kv, mla_dtype_t dt,
+                              const mla_cache_desc_t *cache, const int32_t *block_table,
+                              int32_t bt_stride, const int32_t *pos0, int32_t B, int32_t q_len,
+                              int32_t d_model, const mla_rope_t *rope, void *workspace,
+                              int64_t workspace_bytes, mla_stream_t stream) {
+    mla_status_t st = check_cache(cache);
+    if (st != MLA_OK) return st;
+    if (!h || !w_kv || !block_table || !pos0) return fail(MLA_ERR_INVALID_ARG, "NULL h/w_kv/block_table/pos0");
+    if (B < 1 || q_len < 1 || d_model < 1 || bt_stride < 1)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d q_len=%d d_model=%d bt_stride=%d", B, q_len, d_model, bt_stride);
+    if (dt != MLA_DT_F32 && dt != MLA_DT_BF16) return fail(MLA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+    RopeTab t{};
+    if (cache->d_r > 0) {
+        if (!rope) return fail(MLA_ERR_INVALID_ARG, "rope is NULL with d_r=%d", cache->d_r);
+        if (!rope_table(rope, cache->d_r, &t))
+            return fail(MLA_ERR_INVALID_ARG, "bad rope (base=%g factor=%g orig_ctx=%g mscale=%g)", rope->base,
+                        rope->factor, rope->orig_ctx, rope->mscale);
+    }
+    const int32_t T = B * q_len;
+    const int64_t need = cache_append_workspace(T, d_model, cache->d_c, cache->d_r, dt);
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_WORKSPACE, "cache_append workspace %lld < %lld", (long long)workspace_bytes, (long long)need);
+    if (!workspace || !aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace NULL or not 256-byte aligned");
+    // (row alignment is part of the MFMA path's shape test; other shapes run a generic kernel)
+    if (!aligned(h, 16) || !aligned(w_kv, 16)) return fail(MLA_ERR_ALIGN, "h / w_kv must be 16-byte aligned");
+    return hip_status(launch_cache_append(h, w_kv, dt, (uint8_t *)cache->base, (float *)cache->block_scales,
+                                          block_bytes_of(cache->kv_dtype, cache->d_c, cache->d_r),
+                                          cache->num_blocks, cache->kv_dtype, block_table, bt_stride, pos0, B,
+                                          q_len, d_model, cache->d_c, cache->d_r, t, (float *)workspace,
+                                          (hipStream_t)stream),
+                      "cache_append launch");
+}
+
+int64_t mla_project_q_workspace(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h,
+                                int32_t d_nope, int32_t d_c, int32_t d_r, mla_dtype_t dt) {
+    if (T < 1 || d_model < 1 || q_lora < 1 || n_h < 1 || d_nope < 1 || d_c < 1 || d_r < 0) return 0;
+    return project_q_workspace(T, d_model, q_lora, n_h, d_nope, d_c, d_r, dt);
+}
+
+mla_status_t mla_project_q(const void *h, const void *w_dq, const void *w_uq, const void *w_qr,
+                           const void *w_uk, mla_dtype_t dt, const int32_t *pos, int32_t T,
+                           int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope,
+                           int32_t d_c, int32_t d_r, const mla_rope_t *rope, void *q_lat,
+                           void *q_rope, void *workspace, int64_t workspace_bytes,
+                           mla_stream_t stream) {
+    if (!h || !w_dq || !w_uq || !w_uk || !pos || !q_lat)
+        return fail(MLA_ERR_INVALID_ARG, "NULL h/w_dq/w_uq/w_uk/pos/q_lat");
+    if (T < 1 || d_model < 1 || q_lora < 1 || n_h < 1 || d_nope < 1 || d_c < 1 || d_r < 0)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes T=%d d_model=%d q_lora=%d n_h=%d d_nope=%d d_c=%d d_r=%d", T,
+                    d_model, q_lora, n_h, d_nope, d_c, d_r);
+    if (dt != MLA_DT_F32 && dt != MLA_DT_BF16) return fail(MLA_ERR_UNSUPPORTED, "dtype %d", (int)dt);
+    RopeTab t{};
+    if (d_r > 0) {
+        if (!w_qr || !q_rope || !rope) return fail(MLA_ERR_INVALID_ARG, "NULL w_qr/q_rope/rope with d_r=%d", d_r);
+        if (!rope_table(rope, d_r, &t))
+            return fail(MLA_ERR_INVALID_ARG, "bad rope (d_r=%d base=%g factor=%g orig_ctx=%g mscale=%g)", d_r,
+                        rope->base, rope->factor, rope->orig_ctx, rope->mscale);
+    }
+    const int64_t need = project_q_workspace(T, d_model, q_lora, n_h, d_nope, d_c, d_r, dt);
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_WORKSPACE, "project_q workspace %lld < %lld", (long long)workspace_bytes, (long long)need);
+    if (!workspace || !aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace NULL or not 256-byte aligned");
+    if (!aligned(h, 16) || !aligned(w_dq, 16) || !aligned(w_uq, 16) || !aligned(w_uk, 16) || !aligned(q_lat, 16) ||
+        (d_r > 0 && (!aligned(w_qr, 16) || !aligned(q_rope, 16))))
+        return fail(MLA_ERR_ALIGN, "project_q operands must be 16-byte aligned");
+    if (d_r == 0) return fail(MLA_ERR_UNSUPPORTED, "project_q needs d_r > 0");
+    return hip_status(launch_project_q(h, w_dq, w_uq, w_qr, w_uk, dt, pos, T, d_model, q_lora, n_h, d_nope, d_c,
+                                       d_r, t, q_lat, q_rope, workspace, (hipStream_t)stream),
+                      "project_q launch");
+}
+
 mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *block_table,
                               int32_t bt_stride, const int32_t *seq_lens, int32_t B,
                               int32_t max_tokens, void *out, mla_stream_t stream) {

@@ -1,0 +1,437 @@
+// The producers of the decode's inputs, from the hidden states of the new
+// tokens:
+//   cache append      c = h W^DKV, k^R = RoPE(h W^KR), written into the token's
+//                     slot of the paged cache (huny.dev "DeepSeek MLA 해부"
+//                     §2-1 compression equation and §2-3 shared rotary key;
+//                     vLLM MLA page, the kv_c_and_k_pe cache of "FlashMLAImpl")
+//   query production  c^Q = h W^DQ, q^C = c^Q W^UQ (§2-2), q~ = q^C W^UK^T
+//                     (§3-1 absorption), q^R = RoPE(h W^QR) (§2-3)
+// Products run on the bf16 MFMA GEMM (split over K into fp32 partials when
+// the output is small); a finishing kernel sums the partials and applies the
+// rotation, the storage rounding and, for fp8 caches, the block scale.
+// RoPE frequencies are plain (theta_j = base^(-2j/d)) or YaRN-scaled; the
+// huny page names YaRN for 128K+ contexts (§6, YaRN item) without a
+// formula: the table follows the published YaRN NTK-by-parts interpolation.
+#include <cmath>
+
+#include "common.hpp"
+
+namespace mla {
+
+bool gemm_nn_mfma_ok(int32_t N, int32_t K);
+int gemm_splits(int32_t M, int32_t N, int32_t K);
+hipError_t launch_gemm_nn_f32(const void *A, int64_t lda, const void *B, int64_t ldb, float *ws,
+                              int32_t M, int32_t N, int32_t K, int splits, hipStream_t s);
+hipError_t launch_gemm_nn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
+                               int64_t ldc, int32_t M, int32_t N, int32_t K, hipStream_t s);
+hipError_t launch_split_sum_bf16(const float *ws, int splits, int64_t split_stride, int64_t n8,
+                                 void *out, hipStream_t s);
+
+bool rope_table(const mla_rope_t *r, int32_t d_r, RopeTab *t) {
+    if (!r || d_r < 2 || d_r % 2 || d_r / 2 > kMaxRopePairs) return false;
+    if (!(r->base > 1.0) || !(r->factor > 0.0) || !(r->mscale > 0.0)) return false;
+    const int half = d_r / 2;
+    t->half = half;
+    t->mscale = (float)r->mscale;
+    for (int j = 0; j < half; ++j) {
+        const double theta = std::pow(r->base, -2.0 * j / d_r);
+        double th = theta;
+        if (r->factor != 1.0) {
+            if (!(r->orig_ctx > 0.0)) return false;
+            // turns of pair j over the original context, and the ramp between
+            // interpolation (theta / s) and the unchanged frequency
+            const double turns = r->orig_ctx * theta / (2.0 * M_PI);
+            double gamma;
+            if (r->beta_fast > r->beta_slow)
+                gamma = std::fmin(1.0, std::fmax(0.0, (turns - r->beta_slow) / (r->beta_fast - r->beta_slow)));
+            else
+                gamma = turns >= r->beta_fast ? 1.0 : 0.0;
+            th = (1.0 - gamma) * theta / r->factor + gamma * theta;
+        }
+        t->theta[j] = th;
+    }
+    return true;
+}
+
+namespace {
+
+// OCP E4M3 ("fn") from fp32: round to nearest even, |x| >= 448 saturates to
+// +-448, NaN -> 0x7F, the sign of zero dropped (as x < 0 decides the sign).
+__device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
+    if (x != x) return 0x7F;
+    const uint8_t sign = x < 0.f ? 0x80 : 0x00;
+    const float a = fabsf(x);
+    if (a >= 448.f) return sign | 0x7E;
+    if (a < 0.015625f) {   // below 2^-6: subnormal steps of 2^-9 (8 steps reach 2^-6 = code 8)
+        return sign | (uint8_t)__builtin_rintf(a * 512.f);
+    }
+    int e;
+    const float m = frexpf(a, &e);            // a = m 2^e, m in [0.5, 1): exponent e - 1
+    float q = __builtin_rintf(m * 16.f);      // 8..16: 1.mmm in eighths
+    if (q == 16.f) { q = 8.f; ++e; }
+    const int ef = e - 1 + 7;                 // biased exponent, 1..15
+    if (ef > 15 || (ef == 15 && q > 14.f)) return sign | 0x7E;
+    return sign | (uint8_t)((ef << 3) | ((int)q - 8));
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+    if ((c & 0x7F) == 0x7F) return __builtin_nanf("");
+    const int e = (c >> 3) & 15, m = c & 7;
+    const float v = e == 0 ? (float)m * 0.001953125f : ldexpf(1.f + (float)m * 0.125f, e - 7);
+    return (c & 0x80) ? -v : v;
+}
+
+struct AppendArgs {
+    const float *ws;          // fp32 partials [splits][T][d_c + d_r]
+    int64_t split_stride;
+    int32_t splits;
+    uint8_t *pool;
+    float *scales;
+    int64_t block_bytes, num_blocks;
+    const int32_t *bt;
+    int32_t bt_stride;
+    const int32_t *pos0;
+    int32_t q_len, d_c, d_r;
+};
+
+// One workgroup per sequence: its q_len tokens in order (positions outside
+// the block table, p < 0 or p >= 64 bt_stride, are skipped).  For f32 / bf16 the
+// rows are rounded once and stored; for fp8 the tokens that land in one
+// block are handled together: their amax sets or raises the block scale,
+// earlier slots are re-encoded when it grows, then the codes are written.
+template <int FMT>   // 0 f32, 1 bf16, 2 fp8 (e4m3 latent + bf16 k^R)
+__global__ __launch_bounds__(256) void append_finish_kernel(AppendArgs a, RopeTab rt) {
+    __shared__ float red[4];
+    __shared__ float sh[3];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int N = a.d_c + a.d_r;
+    const int p0 = a.pos0[b];
+    auto xval = [&](int t, int f) {
+        float v = 0.f;
+        for (int s = 0; s < a.splits; ++s) v += a.ws[s * a.split_stride + (int64_t)t * N + f];
+        return v;
+    };
+    auto block_of = [&](int p) {
+        int64_t id = a.bt[(int64_t)b * a.bt_stride + p / kBlock];
+        return id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
+    };
+    // rotary pair j of token t at position p: rotated, times mscale
+    auto rot = [&](int t, int p, int j, float &y0, float &y1) {
+        const float x0 = xval(t, a.d_c + 2 * j), x1 = xval(t, a.d_c + 2 * j + 1);
+        double sn, cs;
+        sincos((double)p * rt.theta[j], &sn, &cs);
+        const float c = (float)cs, s = (float)sn;
+        y0 = (x0 * c - x1 * s) * rt.mscale;
+        y1 = (x0 * s + x1 * c) * rt.mscale;
+    };
+
+    if constexpr (FMT != 2) {
+        constexpr int EB = FMT == 0 ? 4 : 2;
+        for (int i = 0; i < a.q_len; ++i) {
+            const int t = b * a.q_len + i, p = p0 + i;
+            if (p < 0 || p / kBlock >= a.bt_stride) continue;   // outside the table: not written
+            uint8_t *row = a.pool + block_of(p) * a.block_bytes + (int64_t)(p % kBlock) * N * EB;
+            for (int f = tid; f < a.d_c; f += 256) {
+                const float v = xval(t, f);
+                if constexpr (FMT == 0) ((float *)row)[f] = v;
+                else ((uint16_t *)row)[f] = f32_to_bf16(v);
+            }
+            for (int j = tid; j < rt.half; j += 256) {
+                float y0, y1;
+                rot(t, p, j, y0, y1);
+                if constexpr (FMT == 0) {
+                    ((float *)row)[a.d_c + 2 * j] = y0;
+                    ((float *)row)[a.d_c + 2 * j + 1] = y1;
+                } else {
+                    ((uint16_t *)row)[a.d_c + 2 * j] = f32_to_bf16(y0);
+                    ((uint16_t *)row)[a.d_c + 2 * j + 1] = f32_to_bf16(y1);
+                }
+            }
+        }
+    } else {
+        int i = 0;
+        while (i < a.q_len) {
+            const int p = p0 + i;
+            const int i_end = p < 0 ? i + 1 : min(a.q_len, (p / kBlock + 1) * kBlock - p0);   // same block
+            if (p < 0 || p / kBlock >= a.bt_stride) {   // outside the table: not written
+                i = i_end;
+                continue;
+            }
+            const int64_t blk = block_of(p);
+            uint8_t *base = a.pool + blk * a.block_bytes;
+            const int s0 = p % kBlock;
+            // amax of the new latents in this block
+            float m = 0.f;
+            for (int k = i; k < i_end; ++k)
+                for (int f = tid; f < a.d_c; f += 256) m = fmaxf(m, fabsf(xval(b * a.q_len + k, f)));
+            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+            if ((tid & 63) == 0) red[tid >> 6] = m;
+            __syncthreads();
+            if (tid == 0) {
+                const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+                const float old = a.scales[blk];
+                float sc;
+                bool grow = false;
+                if (s0 == 0) {
+                    sc = amax > 0.f ? amax / 448.f : 1.f;
+                } else {
+                    sc = fmaxf(old, amax / 448.f);
+                    grow = sc > old;
+                }
+                sh[0] = sc;
+                sh[1] = grow ? old / sc : 1.f;
+                sh[2] = grow ? 1.f : 0.f;
+                a.scales[blk] = sc;
+            }
+            __syncthreads();
+            const float sc = sh[0], ratio = sh[1];
+            if (sh[2] != 0.f) {
+                // re-encode the slots before the first new one at the larger scale
+                for (int idx = tid; idx < s0 * a.d_c; idx += 256)
+                    base[idx] = f32_to_e4m3(e4m3_to_f32(base[idx]) * ratio);
+            }
+            for (int k = i; k < i_end; ++k) {
+                const int t = b * a.q_len + k, pk = p0 + k, slot = pk % kBlock;
+                for (int f = tid; f < a.d_c; f += 256) base[slot * a.d_c + f] = f32_to_e4m3(xval(t, f) / sc);
+                uint16_t *kr = (uint16_t *)(base + (int64_t)kBlock * a.d_c + (int64_t)slot * a.d_r * 2);
+                for (int j = tid; j < rt.half; j += 256) {
+                    float y0, y1;
+                    rot(t, pk, j, y0, y1);
+                    kr[2 * j] = f32_to_bf16(y0);
+                    kr[2 * j + 1] = f32_to_bf16(y1);
+                }
+            }
+            __syncthreads();   // red / sh are reused by the next block
+            i = i_end;
+        }
+    }
+}
+
+// q^R: out[t][h][:] = RoPE(sum_s ws[s][t][h d_r ..]) at pos[t], times mscale.
+// One workgroup per token; cos / sin of its position computed once in fp64.
+template <typename OutT>
+__global__ __launch_bounds__(256) void rope_q_kernel(const float *__restrict__ ws, int64_t split_stride,
+                                                     int32_t splits, const int32_t *__restrict__ pos,
+                                                     int32_t n_h, int32_t d_r, OutT *__restrict__ out,
+                                                     RopeTab rt) {
+    __shared__ float cs[kMaxRopePairs], sn[kMaxRopePairs];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const int p = pos[t];
+    for (int j = tid; j < rt.half; j += 256) {
+        double s, c;
+        sincos((double)p * rt.theta[j], &s, &c);
+        cs[j] = (float)c;
+        sn[j] = (float)s;
+    }
+    __syncthreads();
+    const int W = n_h * d_r;
+    for (int idx = tid; idx < n_h * rt.half; idx += 256) {
+        const int h = idx / rt.half, j = idx % rt.half;
+        const int64_t o = (int64_t)t * W + h * d_r + 2 * j;
+        float x0 = 0.f, x1 = 0.f;
+        for (int s = 0; s < splits; ++s) {
+            x0 += ws[s * split_stride + o];
+            x1 += ws[s * split_stride + o + 1];
+        }
+        const float y0 = (x0 * cs[j] - x1 * sn[j]) * rt.mscale;
+        const float y1 = (x0 * sn[j] + x1 * cs[j]) * rt.mscale;
+        if constexpr (sizeof(OutT) == 2) {
+            out[o] = f32_to_bf16(y0);
+            out[o + 1] = f32_to_bf16(y1);
+        } else {
+            out[o] = y0;
+            out[o + 1] = y1;
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ float ldv(const T *p, int64_t i) {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(p[i]);
+    else return p[i];
+}
+
+// Generic C[z][m][n] = sum_k A[z][m][k] B[z](k, n) in fp32, one thread per
+// output; B(k, n) = B[z * bsb + k * sbk + n * sbn].  For fp32 data and shapes
+// the MFMA GEMM does not take.
+template <typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256) void gemm_generic_kernel(const TA *__restrict__ A, int64_t lda, int64_t bsa,
+                                                           const TB *__restrict__ B, int64_t sbk, int64_t sbn,
+                                                           int64_t bsb, TC *__restrict__ C, int64_t ldc,
+                                                           int64_t bsc, int32_t M, int32_t N, int32_t K,
+                                                           int32_t batch) {
+    const int64_t total = (int64_t)batch * M * N;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int n = (int)(i % N);
+        const int m = (int)((i / N) % M);
+        const int z = (int)(i / ((int64_t)M * N));
+        const TA *a = A + z * bsa + (int64_t)m * lda;
+        const TB *bb = B + z * bsb + (int64_t)n * sbn;
+        float acc = 0.f;
+        for (int k = 0; k < K; ++k) acc += ldv(a, k) * ldv(bb, (int64_t)k * sbk);
+        if constexpr (sizeof(TC) == 2) C[z * bsc + (int64_t)m * ldc + n] = f32_to_bf16(acc);
+        else C[z * bsc + (int64_t)m * ldc + n] = acc;
+    }
+}
+
+unsigned grid_of(int64_t n) {
+    const int64_t g = (n + 255) / 256;
+    return (unsigned)(g < 65536 ? (g < 1 ? 1 : g) : 65536);
+}
+
+template <typename TA, typename TB, typename TC>
+hipError_t gemm_generic(const TA *A, int64_t lda, int64_t bsa, const TB *B, int64_t sbk, int64_t sbn,
+                        int64_t bsb, TC *C, int64_t ldc, int64_t bsc, int32_t M, int32_t N, int32_t K,
+                        int32_t batch, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_generic_kernel<TA, TB, TC>), dim3(grid_of((int64_t)batch * M * N)), dim3(256),
+                       0, s, A, lda, bsa, B, sbk, sbn, bsb, C, ldc, bsc, M, N, K, batch);
+    return hipGetLastError();
+}
+
+bool append_mfma(mla_dtype_t dt, int32_t d_model, int32_t N) {
+    return dt == MLA_DT_BF16 && gemm_nn_mfma_ok(N, d_model);
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+int64_t cache_append_workspace(int32_t T, int32_t d_model, int32_t d_c, int32_t d_r, mla_dtype_t dt) {
+    const int32_t N = d_c + d_r;
+    const int sp = append_mfma(dt, d_model, N) ? gemm_splits(T, N, d_model) : 1;
+    return align256((int64_t)sp * T * N * 4);
+}
+
+hipError_t launch_cache_append(const void *h, const void *w_kv, mla_dtype_t dt, uint8_t *pool,
+                               float *scales, int64_t block_bytes, int64_t num_blocks,
+                               mla_dtype_t kv, const int32_t *bt, int32_t bt_stride,
+                               const int32_t *pos0, int32_t B, int32_t q_len, int32_t d_model,
+                               int32_t d_c, int32_t d_r, const RopeTab &rt, float *ws,
+                               hipStream_t s) {
+    const int32_t T = B * q_len, N = d_c + d_r;
+    int sp = 1;
+    hipError_t e;
+    if (append_mfma(dt, d_model, N)) {
+        sp = gemm_splits(T, N, d_model);
+        e = launch_gemm_nn_f32(h, d_model, w_kv, N, ws, T, N, d_model, sp, s);
+    } else if (dt == MLA_DT_BF16) {
+        e = gemm_generic((const uint16_t *)h, d_model, 0, (const uint16_t *)w_kv, N, 1, 0, ws, N, 0, T, N,
+                         d_model, 1, s);
+    } else {
+        e = gemm_generic((const float *)h, d_model, 0, (const float *)w_kv, N, 1, 0, ws, N, 0, T, N, d_model,
+                         1, s);
+    }
+    if (e != hipSuccess) return e;
+    AppendArgs a{};
+    a.ws = ws; a.split_stride = (int64_t)T * N; a.splits = sp;
+    a.pool = pool; a.scales = scales; a.block_bytes = block_bytes; a.num_blocks = num_blocks;
+    a.bt = bt; a.bt_stride = bt_stride; a.pos0 = pos0; a.q_len = q_len; a.d_c = d_c; a.d_r = d_r;
+    if (kv == MLA_DT_F32)
+        hipLaunchKernelGGL(append_finish_kernel<0>, dim3(B), dim3(256), 0, s, a, rt);
+    else if (kv == MLA_DT_BF16)
+        hipLaunchKernelGGL(append_finish_kernel<1>, dim3(B), dim3(256), 0, s, a, rt);
+    else
+        hipLaunchKernelGGL(append_finish_kernel<2>, dim3(B), dim3(256), 0, s, a, rt);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- queries
+
+namespace {
+
+struct QPlan {
+    bool mfma;
+    int sp1, sp3;                 // splits of h W^DQ and h W^QR
+    int64_t off_cq, off_qc, off_w1, off_w3, total;
+};
+
+QPlan q_plan(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope, int32_t d_c,
+             int32_t d_r, mla_dtype_t dt) {
+    QPlan q{};
+    const int32_t NQ = n_h * d_nope, NR = n_h * d_r;
+    q.mfma = dt == MLA_DT_BF16 && gemm_nn_mfma_ok(q_lora, d_model) && gemm_nn_mfma_ok(NQ, q_lora) &&
+             gemm_nn_mfma_ok(NR, d_model) && d_nope % 64 == 0 && d_c % 128 == 0;
+    q.sp1 = q.mfma ? gemm_splits(T, q_lora, d_model) : 1;
+    q.sp3 = q.mfma ? gemm_splits(T, NR, d_model) : 1;
+    // c^Q and q^C: bf16 on the MFMA path (the next product's operand), fp32 otherwise
+    const int eb = q.mfma ? 2 : 4;
+    int64_t o = 0;
+    q.off_cq = o; o = align256(o + (int64_t)T * q_lora * eb);
+    q.off_qc = o; o = align256(o + (int64_t)T * NQ * eb);
+    q.off_w1 = o; o = align256(o + (q.mfma ? (int64_t)q.sp1 * T * q_lora * 4 : 0));
+    q.off_w3 = o; o = align256(o + (int64_t)q.sp3 * T * NR * 4);
+    q.total = o;
+    return q;
+}
+
+}  // namespace
+
+int64_t project_q_workspace(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope,
+                            int32_t d_c, int32_t d_r, mla_dtype_t dt) {
+    return q_plan(T, d_model, q_lora, n_h, d_nope, d_c, d_r, dt).total;
+}
+
+hipError_t launch_project_q(const void *h, const void *w_dq, const void *w_uq, const void *w_qr,
+                            const void *w_uk, mla_dtype_t dt, const int32_t *pos, int32_t T,
+                            int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope, int32_t d_c,
+                            int32_t d_r, const RopeTab &rt, void *q_lat, void *q_rope, void *ws,
+                            hipStream_t s) {
+    const QPlan q = q_plan(T, d_model, q_lora, n_h, d_nope, d_c, d_r, dt);
+    const int32_t NQ = n_h * d_nope, NR = n_h * d_r;
+    uint8_t *w = (uint8_t *)ws;
+    hipError_t e;
+    if (q.mfma) {
+        // c^Q = h W^DQ (split over d_model, summed and rounded to bf16)
+        float *w1 = (float *)(w + q.off_w1);
+        e = launch_gemm_nn_f32(h, d_model, w_dq, q_lora, w1, T, q_lora, d_model, q.sp1, s);
+        if (e != hipSuccess) return e;
+        e = launch_split_sum_bf16(w1, q.sp1, (int64_t)T * q_lora, (int64_t)T * q_lora / 8, w + q.off_cq, s);
+        if (e != hipSuccess) return e;
+        // q^C = c^Q W^UQ
+        e = launch_gemm_nn_bf16(w + q.off_cq, q_lora, w_uq, NQ, w + q.off_qc, NQ, T, NQ, q_lora, s);
+        if (e != hipSuccess) return e;
+        // q~ = q^C W^UK^T per head
+        e = launch_absorb_q(w + q.off_qc, NQ, w_uk, q_lat, T, n_h, d_nope, d_c, dt, s);
+        if (e != hipSuccess) return e;
+        // h W^QR, rotated below
+        e = launch_gemm_nn_f32(h, d_model, w_qr, NR, (float *)(w + q.off_w3), T, NR, d_model, q.sp3, s);
+        if (e != hipSuccess) return e;
+    } else {
+        float *cq = (float *)(w + q.off_cq), *qc = (float *)(w + q.off_qc), *w3 = (float *)(w + q.off_w3);
+        if (dt == MLA_DT_BF16) {
+            const uint16_t *H = (const uint16_t *)h;
+            e = gemm_generic(H, d_model, 0, (const uint16_t *)w_dq, q_lora, 1, 0, cq, q_lora, 0, T, q_lora, d_model, 1, s);
+            if (e == hipSuccess)
+                e = gemm_generic((const float *)cq, q_lora, 0, (const uint16_t *)w_uq, NQ, 1, 0, qc, NQ, 0, T, NQ, q_lora, 1, s);
+            // q~[t][i][c] = sum_k q^C[t][i][k] W_UK[i][c][k]: batch over heads
+            if (e == hipSuccess)
+                e = gemm_generic((const float *)qc, NQ, d_nope, (const uint16_t *)w_uk, 1, d_nope,
+                                 (int64_t)d_c * d_nope, (uint16_t *)q_lat, (int64_t)n_h * d_c, d_c, T, d_c,
+                                 d_nope, n_h, s);
+            if (e == hipSuccess)
+                e = gemm_generic(H, d_model, 0, (const uint16_t *)w_qr, NR, 1, 0, w3, NR, 0, T, NR, d_model, 1, s);
+        } else {
+            const float *H = (const float *)h;
+            e = gemm_generic(H, d_model, 0, (const float *)w_dq, q_lora, 1, 0, cq, q_lora, 0, T, q_lora, d_model, 1, s);
+            if (e == hipSuccess)
+                e = gemm_generic((const float *)cq, q_lora, 0, (const float *)w_uq, NQ, 1, 0, qc, NQ, 0, T, NQ, q_lora, 1, s);
+            if (e == hipSuccess)
+                e = gemm_generic((const float *)qc, NQ, d_nope, (const float *)w_uk, 1, d_nope,
+                                 (int64_t)d_c * d_nope, (float *)q_lat, (int64_t)n_h * d_c, d_c, T, d_c,
+                                 d_nope, n_h, s);
+            if (e == hipSuccess)
+                e = gemm_generic(H, d_model, 0, (const float *)w_qr, NR, 1, 0, w3, NR, 0, T, NR, d_model, 1, s);
+        }
+        if (e != hipSuccess) return e;
+    }
+    const float *w3 = (const float *)(w + q.off_w3);
+    if (dt == MLA_DT_BF16)
+        hipLaunchKernelGGL(rope_q_kernel<uint16_t>, dim3(T), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
+                           n_h, d_r, (uint16_t *)q_rope, rt);
+    else
+        hipLaunchKernelGGL(rope_q_kernel<float>, dim3(T), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
+                           n_h, d_r, (float *)q_rope, rt);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,241 @@
+"""GPU parity of the decode's producers against the oracle: mla_cache_append
+(bf16 / f32 / fp8 caches, plain and YaRN RoPE, ragged call sizes that cross
+blocks, the fp8 block-scale growth) and mla_project_q (the MFMA chain at the
+DeepSeek-V2 shape and the generic fp32 path).  Cache bytes outside the
+written slots must come back unchanged."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mla_latent_kv_07_amd import api
+
+from parity import DEV, TOL, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+BLK = O.BLOCK
+KV = {O.FMT_F32: "f32", O.FMT_BF16: "bf16", O.FMT_FP8_E4M3: "fp8_e4m3"}
+
+
+def _bf16(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def _setup(fmt, B, max_tokens, d_c, d_r, d_model, seed):
+    rng = np.random.default_rng(seed)
+    nblk = (max_tokens + BLK - 1) // BLK
+    num_blocks = B * nblk + 5
+    perm = rng.permutation(num_blocks)
+    bt = perm[:B * nblk].reshape(B, nblk).astype(np.int32)
+    bb = O.block_bytes(fmt, d_c, d_r)
+    pool = rng.integers(0, 256, (num_blocks, bb), dtype=np.uint8)
+    scales = (rng.random(num_blocks) + 0.5).astype(np.float32)
+    return rng, bt, pool, scales
+
+
+def _run_appends(fmt, B, calls, d_c, d_r, d_model, seed, rope=None, dt=torch.bfloat16,
+                 start=None, h_scale=None):
+    """calls: list of q_len; every sequence appends q_len tokens per call from
+    a random start (or `start`), the hidden states of call k scaled by
+    h_scale[k].  Returns (gpu pool, gpu scales, oracle pool, oracle scales,
+    original pool, written-slot mask)."""
+    max_tokens = sum(calls) + 70
+    rng, bt, pool, scales = _setup(fmt, B, max_tokens, d_c, d_r, d_model, seed)
+    pool0 = pool.copy()
+    w = rng.standard_normal((d_model, d_c + d_r)) / math.sqrt(d_model)
+    if dt == torch.bfloat16:
+        w_dev = _bf16(w)
+        w = w_dev.double().numpy()
+    else:
+        w_dev = torch.from_numpy(w.astype(np.float32))
+        w = w_dev.double().numpy()
+    cfg = rope or api.rope()
+    inv = O.rope_inv_freq(d_r, cfg.base, cfg.factor, cfg.orig_ctx, cfg.beta_fast, cfg.beta_slow)
+    cache = api.DeviceCache(torch.from_numpy(pool).to(DEV),
+                            torch.from_numpy(scales).to(DEV) if fmt == O.FMT_FP8_E4M3 else None,
+                            KV[fmt], d_c, d_r)
+    o_pool, o_scales = pool.copy(), scales.copy()
+    bt_dev = torch.from_numpy(bt).to(DEV)
+    pos = (rng.integers(0, 40, B) if start is None else np.full(B, start)).astype(np.int32)
+    mask = np.zeros(pool.shape, bool)
+    w_dev = w_dev.to(DEV)
+    for k, ql in enumerate(calls):
+        h = rng.standard_normal((B * ql, d_model)) * (1.0 if h_scale is None else h_scale[k])
+        h_dev = (_bf16(h) if dt == torch.bfloat16 else torch.from_numpy(h.astype(np.float32)))
+        h = h_dev.double().numpy()
+        api.cache_append(h_dev.to(DEV), w_dev, cache, bt_dev, torch.from_numpy(pos).to(DEV), ql, cfg)
+        O.cache_append(o_pool, o_scales, fmt, d_c, d_r, bt, pos, ql, h, w, inv_freq=inv, mscale=cfg.mscale)
+        for b in range(B):
+            for i in range(ql):
+                p = int(pos[b]) + i
+                blk, sl = bt[b, p // BLK], p % BLK
+                if fmt == O.FMT_FP8_E4M3:
+                    mask[blk, :(sl + 1) * d_c] = True     # earlier codes may be re-encoded
+                    off = BLK * d_c + sl * 2 * d_r
+                    mask[blk, off:off + 2 * d_r] = True
+                else:
+                    rb = O.block_bytes(fmt, d_c, d_r) // BLK
+                    mask[blk, sl * rb:(sl + 1) * rb] = True
+        pos += ql
+    torch.cuda.synchronize()
+    g_scales = cache.block_scales.cpu().numpy() if fmt == O.FMT_FP8_E4M3 else None
+    return cache.pool.cpu().numpy(), g_scales, o_pool, o_scales, pool0, mask
+
+
+def _check_16bit_rows(got, want, mask, what):
+    """bf16 / f32 payloads: at most one unit in the last place apart (the GPU
+    sums in fp32, the oracle in fp64), mostly identical."""
+    g, w = got[mask], want[mask]
+    if what == "bf16":
+        gi = g.view(np.int16).astype(np.int32)
+        wi = w.view(np.int16).astype(np.int32)
+    else:
+        gi = g.view(np.int32).astype(np.int64)
+        wi = w.view(np.int32).astype(np.int64)
+    d = np.abs(gi - wi)
+    say(f"  {what}: {d.size} values, {np.count_nonzero(d)} differ by one ulp, max {d.max()}")
+    if what == "bf16":
+        # one ulp, except near zero: a sum that cancels to a small value keeps
+        # the fp32 accumulation's absolute error (~1e-6 of the row scale)
+        dec = lambda x: (x.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        gv, wv = dec(g), dec(w)
+        scale = np.sqrt(np.mean(wv[np.isfinite(wv)] ** 2))
+        ok = (d <= 1) | (np.abs(gv - wv) <= 2.0 ** -8 * np.abs(wv) + 1e-4 * scale)
+        assert ok.all()
+        assert np.count_nonzero(d) <= max(2, d.size // 200)
+    else:
+        # fp32 storage of an fp32 sum of d_model products vs the exact value
+        gf, wf = g.view(np.float32).astype(np.float64), w.view(np.float32).astype(np.float64)
+        assert np.all(np.abs(gf - wf) <= 1e-5 * np.maximum(1.0, np.abs(wf)))
+
+
+@pytest.mark.parametrize("calls", [[1], [3, 1, 70], [64, 2]])
+def test_append_bf16_mfma_shape(calls):
+    """d_c 512, d_r 64, d_model a multiple of 64: the MFMA product with a
+    ragged last column tile (576 = 4.5 x 128)."""
+    B, d_c, d_r, dm = 5, 512, 64, 256
+    got, _, want, _, pool0, mask = _run_appends(O.FMT_BF16, B, calls, d_c, d_r, dm, seed=len(calls))
+    assert np.array_equal(got[~mask], pool0[~mask])
+    _check_16bit_rows(got, want, mask, "bf16")
+
+
+def test_append_f32_generic():
+    B, d_c, d_r, dm = 3, 64, 16, 48
+    got, _, want, _, pool0, mask = _run_appends(O.FMT_F32, B, [2, 65, 1], d_c, d_r, dm, seed=21,
+                                                dt=torch.float32)
+    assert np.array_equal(got[~mask], pool0[~mask])
+    _check_16bit_rows(got, want, mask, "f32")
+
+
+def test_append_bf16_yarn():
+    cfg = api.rope(base=10000.0, factor=40.0, orig_ctx=4096.0, beta_fast=32.0, beta_slow=1.0,
+                   mscale=1.0 + 0.1 * math.log(40.0))
+    B, d_c, d_r, dm = 4, 512, 64, 128
+    got, _, want, _, pool0, mask = _run_appends(O.FMT_BF16, B, [1, 5], d_c, d_r, dm, seed=22, rope=cfg)
+    assert np.array_equal(got[~mask], pool0[~mask])
+    _check_16bit_rows(got, want, mask, "bf16")
+
+
+def test_append_fp8_scale_growth():
+    """Calls of 1, 3 and 70 tokens (fresh blocks, partial blocks, a block
+    crossing) where later tokens are larger: scales grow and earlier codes
+    are re-encoded.  Codes may differ by one step where the fp32 and fp64
+    products fall on opposite sides of a rounding point."""
+    B, d_c, d_r, dm = 4, 512, 64, 128
+    got, g_sc, want, w_sc, pool0, mask = _run_appends(O.FMT_FP8_E4M3, B, [1, 3, 70, 1], d_c, d_r, dm,
+                                                      seed=23, start=0, h_scale=[0.1, 1.0, 3.0, 10.0])
+    assert np.array_equal(got[~mask], pool0[~mask])
+    touched = np.unique(np.nonzero(mask)[0])
+    np.testing.assert_allclose(g_sc[touched], w_sc[touched], rtol=1e-6)
+    other = np.setdiff1d(np.arange(len(g_sc)), touched)
+    assert np.array_equal(g_sc[other], w_sc[other])
+    codes = np.zeros(mask.shape, bool)
+    codes[:, :BLK * d_c] = True
+    cm = mask & codes
+    g, w = got[cm], want[cm]
+    # one e4m3 step apart at most: compare the decoded magnitudes' code order
+    gv, wv = O.e4m3_to_f64(g), O.e4m3_to_f64(w)
+    diff = np.count_nonzero(g != w)
+    say(f"  fp8 codes: {g.size}, {diff} differ")
+    assert diff <= max(4, g.size // 500)
+    step = np.maximum(np.abs(wv) * 2.0 ** -3, 2.0 ** -9)
+    nan = np.isnan(wv)
+    assert np.array_equal(np.isnan(gv), nan)
+    assert np.all(np.abs(gv - wv)[~nan] <= step[~nan] * 1.0001)
+    rm = mask & ~codes
+    _check_16bit_rows(got[:, BLK * d_c:], want[:, BLK * d_c:], rm[:, BLK * d_c:], "bf16")
+
+
+def test_append_full_size_decode_step():
+    """The layer workload's append: 128 sequences, d_model 5120, one new
+    token each at positions up to 32K."""
+    B, d_c, d_r, dm = 128, 512, 64, 5120
+    rng = np.random.default_rng(24)
+    pos = rng.integers(0, 32768, B).astype(np.int32)
+    nblk = int(pos.max()) // BLK + 1
+    num_blocks = B + 3
+    bt = np.zeros((B, nblk), np.int32)
+    ids = rng.permutation(num_blocks)[:B]
+    bt[np.arange(B), pos // BLK] = ids
+    pool = rng.integers(0, 256, (num_blocks, O.block_bytes(O.FMT_BF16, d_c, d_r)), dtype=np.uint8)
+    pool0 = pool.copy()
+    w_dev = _bf16(rng.standard_normal((dm, d_c + d_r)) / math.sqrt(dm))
+    h_dev = _bf16(rng.standard_normal((B, dm)))
+    cache = api.DeviceCache(torch.from_numpy(pool).to(DEV), None, "bf16", d_c, d_r)
+    api.cache_append(h_dev.to(DEV), w_dev.to(DEV), cache, torch.from_numpy(bt).to(DEV),
+                     torch.from_numpy(pos).to(DEV), 1, api.rope())
+    got = cache.pool.cpu().numpy()
+    O.cache_append(pool, None, O.FMT_BF16, d_c, d_r, bt, pos, 1, h_dev.double().numpy(),
+                   w_dev.double().numpy())
+    mask = np.zeros(pool.shape, bool)
+    for b in range(B):
+        sl = int(pos[b]) % BLK
+        mask[ids[b], sl * 1152:(sl + 1) * 1152] = True
+    assert np.array_equal(got[~mask], pool0[~mask])
+    _check_16bit_rows(got, pool, mask, "bf16")
+
+
+@pytest.mark.parametrize("T", [128, 3])
+def test_project_q_full_shape(T):
+    """DeepSeek-V2 query path, d_model 5120, q_lora 1536, 128 heads: the MFMA
+    chain against the fp64 oracle from the same bf16 inputs."""
+    dm, ql, n_h, dn, dc, dr = 5120, 1536, 128, 128, 512, 64
+    rng = np.random.default_rng(25 + T)
+    bf = lambda shape, std: _bf16(rng.standard_normal(shape) * std)
+    h = bf((T, dm), 1.0)
+    w_dq, w_uq = bf((dm, ql), 1 / math.sqrt(dm)), bf((ql, n_h * dn), 1 / math.sqrt(ql))
+    w_qr, w_uk = bf((dm, n_h * dr), 1 / math.sqrt(dm)), bf((n_h, dc, dn), 1 / math.sqrt(dc))
+    pos = rng.integers(0, 131072, T).astype(np.int32)
+    cfg = api.rope(factor=40.0, mscale=1.0 + 0.1 * math.log(40.0))
+    q_lat, q_rope = api.project_q(h.to(DEV), w_dq.to(DEV), w_uq.to(DEV), w_qr.to(DEV), w_uk.to(DEV),
+                                  torch.from_numpy(pos).to(DEV), n_h, dn, dr, cfg)
+    torch.cuda.synchronize()
+    inv = O.rope_inv_freq(dr, 10000.0, 40.0, 4096.0, 32.0, 1.0)
+    ref_lat, ref_rope = O.project_queries_absorbed(h.double().numpy(), w_dq.double().numpy(),
+                                                   w_uq.double().numpy(), w_qr.double().numpy(),
+                                                   w_uk.double().numpy(), n_h, dn, dr, pos,
+                                                   inv_freq=inv, mscale=cfg.mscale)
+    e1 = row_rel_err(q_lat.float().cpu().numpy(), ref_lat)
+    e2 = row_rel_err(q_rope.float().cpu().numpy(), ref_rope)
+    say(f"  T={T}: q_lat {e1:.3e}  q_rope {e2:.3e}")
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_project_q_generic_f32():
+    T, dm, ql, n_h, dn, dc, dr = 5, 48, 24, 3, 8, 12, 6
+    rng = np.random.default_rng(26)
+    f = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32))
+    h, w_dq, w_uq, w_qr, w_uk = f(T, dm), f(dm, ql), f(ql, n_h * dn), f(dm, n_h * dr), f(n_h, dc, dn)
+    pos = rng.integers(0, 5000, T).astype(np.int32)
+    q_lat, q_rope = api.project_q(h.to(DEV), w_dq.to(DEV), w_uq.to(DEV), w_qr.to(DEV), w_uk.to(DEV),
+                                  torch.from_numpy(pos).to(DEV), n_h, dn, dr, api.rope())
+    ref_lat, ref_rope = O.project_queries_absorbed(h.double().numpy(), w_dq.double().numpy(),
+                                                   w_uq.double().numpy(), w_qr.double().numpy(),
+                                                   w_uk.double().numpy(), n_h, dn, dr, pos)
+    e1 = row_rel_err(q_lat.cpu().numpy(), ref_lat)
+    e2 = row_rel_err(q_rope.cpu().numpy(), ref_rope)
+    say(f"  f32: q_lat {e1:.3e}  q_rope {e2:.3e}")
+    assert e1 <= TOL["f32"] and e2 <= TOL["f32"]

@@ -205,3 +205,43 @@ def test_plan_fits_one_round_on_ragged_batches():
         assert units(info.blocks_per_item) <= cus
         if info.blocks_per_item > 1:
             assert units(info.blocks_per_item - 1) > cus
+
+
+def test_rope_freqs_match_the_oracle():
+    """The host's frequency table (plain and YaRN) against the oracle's own."""
+    import numpy as np
+    import oracle as O
+    for d_r, base, factor, L0, bf, bs in [(64, 10000.0, 1.0, 4096.0, 32.0, 1.0), (64, 10000.0, 40.0, 4096.0, 32.0, 1.0),
+                                          (16, 500.0, 8.0, 64.0, 8.0, 1.0), (128, 1e6, 4.0, 8192.0, 16.0, 2.0),
+                                          (8, 10000.0, 4.0, 64.0, 4.0, 4.0)]:
+        cfg = L.Rope(base, factor, L0, bf, bs, 1.0)
+        out = (ctypes.c_double * (d_r // 2))()
+        L.check(lib().mla_rope_freqs(ctypes.byref(cfg), d_r, ctypes.cast(out, ctypes.c_void_p)))
+        want = O.rope_inv_freq(d_r, base, factor, L0, bf, bs)
+        np.testing.assert_allclose(np.array(out[:]), want, rtol=1e-14, atol=0)
+
+
+def test_producers_reject_bad_arguments():
+    l = lib()
+    d = _desc()
+    good = L.Rope(10000.0, 1.0, 4096.0, 32.0, 1.0, 1.0)
+    R = ctypes.byref(good)
+    ws = 1 << 30
+    assert l.mla_cache_append(None, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 4, 1, 5120, R, A, ws, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_cache_append(A, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 0, 1, 5120, R, A, ws, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_cache_append(A, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 4, 1, 5120, None, A, ws, None) == L.MLA_ERR_INVALID_ARG
+    bad = L.Rope(10000.0, 0.0, 4096.0, 32.0, 1.0, 1.0)
+    assert l.mla_cache_append(A, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 4, 1, 5120, ctypes.byref(bad), A, ws, None) == L.MLA_ERR_INVALID_ARG
+    assert l.mla_cache_append(A, A, L.DT_FP8_E4M3, ctypes.byref(d), A, 64, A, 4, 1, 5120, R, A, ws, None) == L.MLA_ERR_UNSUPPORTED
+    assert l.mla_cache_append(A, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 4, 1, 5120, R, A, 16, None) == L.MLA_ERR_WORKSPACE
+    assert l.mla_cache_append(A + 2, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 4, 1, 5120, R, A, ws, None) == L.MLA_ERR_ALIGN
+    assert l.mla_cache_append(A, A, L.DT_BF16, ctypes.byref(_desc(block_size=32)), A, 64, A, 4, 1, 5120, R, A, ws, None) == L.MLA_ERR_UNSUPPORTED
+    assert l.mla_cache_append_workspace(128, 5120, 512, 64, L.DT_BF16) >= 128 * 576 * 4
+    args = [A, A, A, A, A, L.DT_BF16, A, 4, 5120, 1536, 128, 128, 512, 64, R, A, A, A, ws, None]
+    # each case differs from a valid call in one argument; every check runs before any launch
+    for i, v, st in [(0, None, L.MLA_ERR_INVALID_ARG), (7, 0, L.MLA_ERR_INVALID_ARG), (5, L.DT_FP8_E4M3, L.MLA_ERR_UNSUPPORTED),
+                     (18, 16, L.MLA_ERR_WORKSPACE), (15, A + 2, L.MLA_ERR_ALIGN), (14, ctypes.byref(bad), L.MLA_ERR_INVALID_ARG)]:
+        a = list(args)
+        a[i] = v
+        assert l.mla_project_q(*a) == st, (i, v)
+    assert l.mla_project_q_workspace(128, 5120, 1536, 128, 128, 512, 64, L.DT_BF16) > 0
