@@ -57,7 +57,7 @@ def parse():
                     help="cache pool replicas rotated per call (default: enough for >= 512 MB)")
     ap.add_argument("--workload", default="v2_decode_b32_s4096_bf16",
                     choices=["v2_decode_b32_s4096_bf16", "long_ctx_b4_s64k_128k_bf16",
-                             "fp8_cache_spec2_b64", "full_layer_b128_bf16"],
+                             "fp8_cache_spec2_b64", "full_layer_b128_bf16", "decode_step_b128_bf16"],
                     help="the measured batch (default) or one of the other parity workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -164,11 +164,14 @@ def main():
     from mla_latent_kv_07_amd import inputs as I
 
     torch.cuda.set_device(torch.device("cuda:0"))
-    wl = I.WORKLOADS[args.workload]
-    if wl.d_model:
-        out = run_layer(args, wl)
+    if args.workload == "decode_step_b128_bf16":
+        # the full-layer shapes, from hidden states: query production and the
+        # cache append take the place of the drawn queries
+        out = run_layer(args, I.C5, producers=True)
+    elif I.WORKLOADS[args.workload].d_model:
+        out = run_layer(args, I.WORKLOADS[args.workload])
     else:
-        out = run_decode(args, wl)
+        out = run_decode(args, I.WORKLOADS[args.workload])
     print(json.dumps(out), flush=True)
 
 
@@ -380,10 +383,13 @@ def run_decode(args, wl):
     return out
 
 
-def run_layer(args, wl):
+def run_layer(args, wl, producers=False):
     """The whole absorbed layer at decode: absorb_q -> split decode + combine
-    -> absorb_out.  Query production (h -> q^C, q^R) is not on the path: q^C
-    and q^R are drawn N(0, 1) from the workload's generator after its cache."""
+    -> absorb_out, with q^C and q^R drawn N(0, 1) from the workload's
+    generator after its cache.  With producers, one decode step from the
+    hidden states instead: mla_project_q (h -> q~, q^R at position S_b - 1)
+    and mla_cache_append (the new token's row written at S_b - 1, so the
+    decode attends to it) replace the drawn queries and absorb_q."""
     import torch
     from mla_latent_kv_07_amd import _lib as L
     from mla_latent_kv_07_amd import api
@@ -398,7 +404,8 @@ def run_layer(args, wl):
     T = wl.B * wl.q_len
     qn = torch.randn((T, wl.n_h, wl.d_nope), generator=g).to(bf).to(dev)
     qr = torch.randn((T, wl.n_h, wl.d_r), generator=g).to(bf).to(dev)
-    w = {k: v.to(bf).to(dev) for k, v in Lw["weights"].items() if k in ("w_uk", "w_uv", "w_o")}
+    keep = ("w_uk", "w_uv", "w_o") + (("w_dkv", "w_dq", "w_uq", "w_qr") if producers else ())
+    w = {k: v.to(bf).to(dev) for k, v in Lw["weights"].items() if k in keep}
     sl_h = Lw["seq_lens"]
     cache_bytes = cache.cache_bytes
     weight_bytes = sum(v.numel() * 2 for v in w.values())
@@ -433,8 +440,31 @@ def run_layer(args, wl):
           L.DT_BF16, sp)
     timer = Timer(torch, stream)
 
-    def step(i):
-        return lib.mla_absorb_q(*aq) | lib.mla_decode(*dargs[i % R]) | lib.mla_absorb_out(*ao)
+    if producers:
+        h = Lw["hidden"].to(bf).to(dev)
+        pos = (sl_h.to(torch.int32) - 1).to(dev)             # the new token of each sequence
+        rope = api.rope()
+        ws_a_bytes = api.cache_append_workspace_bytes(T, wl.d_model, wl.d_c, wl.d_r, bf)
+        ws_a = torch.empty(max(ws_a_bytes, 256), dtype=torch.uint8, device=dev)
+        ws_q_bytes = api.project_q_workspace_bytes(T, wl.d_model, wl.q_lora, wl.n_h, wl.d_nope, wl.d_c,
+                                                   wl.d_r, bf)
+        ws_q = torch.empty(max(ws_q_bytes, 256), dtype=torch.uint8, device=dev)
+        qr_p = torch.empty((T, wl.n_h, wl.d_r), dtype=bf, device=dev)
+        pq = (P(h.data_ptr()), P(w["w_dq"].data_ptr()), P(w["w_uq"].data_ptr()), P(w["w_qr"].data_ptr()),
+              P(w["w_uk"].data_ptr()), L.DT_BF16, P(pos.data_ptr()), T, wl.d_model, wl.q_lora, wl.n_h,
+              wl.d_nope, wl.d_c, wl.d_r, ctypes.byref(rope), P(q_lat.data_ptr()), P(qr_p.data_ptr()),
+              P(ws_q.data_ptr()), ws_q.numel(), sp)
+        cas = [(P(h.data_ptr()), P(w["w_dkv"].data_ptr()), L.DT_BF16, ctypes.byref(descs[r]), P(bt.data_ptr()),
+                bt.stride(0), P(pos.data_ptr()), wl.B, wl.q_len, wl.d_model, ctypes.byref(rope),
+                P(ws_a.data_ptr()), ws_a.numel(), sp) for r in range(R)]
+        dargs = [(P(q_lat.data_ptr()), P(qr_p.data_ptr())) + a[2:] for a in dargs]
+
+        def step(i):
+            return (lib.mla_project_q(*pq) | lib.mla_cache_append(*cas[i % R]) | lib.mla_decode(*dargs[i % R])
+                    | lib.mla_absorb_out(*ao))
+    else:
+        def step(i):
+            return lib.mla_absorb_q(*aq) | lib.mla_decode(*dargs[i % R]) | lib.mla_absorb_out(*ao)
 
     for i in range(args.warmup):
         L.check(step(i))
@@ -443,6 +473,9 @@ def run_layer(args, wl):
     ms_per_step, gpu_ms = timer.steps(step, K, L.check)
     n_leg = max(K, 20)
     q_ms = timer.legs(lib.mla_absorb_q, [aq], n_leg, L.check)
+    if producers:
+        pq_ms = timer.legs(lib.mla_project_q, [pq], n_leg, L.check)
+        ca_ms = timer.legs(lib.mla_cache_append, cas, n_leg, L.check)
     dec_ms = timer.legs(lib.mla_decode_partial, dargs, n_leg, L.check)
     fin = (ctypes.byref(dec.info), P(dec.plan_dev.data_ptr()), P(dec.workspace.data_ptr()),
            dec.workspace.numel(), L.DT_BF16, P(o_lat.data_ptr()), P(lse.data_ptr()), sp)
@@ -454,7 +487,9 @@ def run_layer(args, wl):
     layer_bytes = cache_bytes + weight_bytes
     S = sl_h.tolist()
     out = {
-        "metric": f"MLA absorbed layer (absorb_q, decode, absorb_out) cache+weight GB/s, {wl.name}",
+        "metric": (f"MLA decode step from hidden states (project_q, cache_append, decode, absorb_out) "
+                   f"cache+weight GB/s, decode_step_b128_bf16" if producers else
+                   f"MLA absorbed layer (absorb_q, decode, absorb_out) cache+weight GB/s, {wl.name}"),
         "value": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -466,7 +501,8 @@ def run_layer(args, wl):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "seq_len": [min(S), max(S)], "q_len": wl.q_len,
+        "config": {"workload": "decode_step_b128_bf16" if producers else wl.name, "B": wl.B,
+                   "seq_len": [min(S), max(S)], "q_len": wl.q_len,
                    "n_h": wl.n_h, "d_c": wl.d_c, "d_r": wl.d_r, "d_nope": wl.d_nope, "d_v": wl.d_v,
                    "d_model": wl.d_model, "cache_bytes": cache_bytes, "weight_bytes": weight_bytes,
                    "pool_replicas": R, "work_items": dec.info.num_items},
@@ -484,8 +520,24 @@ def run_layer(args, wl):
         "roofline": roofline(wl, kernel, dec_ms, cache_bytes, flops_dec, traffic_for(kernel, wl.name)),
         "cpu_baseline": None,
     }
+    if producers:
+        # weight-streaming rates of the producers (bytes: weights read +
+        # activations read + outputs written, once each)
+        b_pq = (sum(w[k].numel() for k in ("w_dq", "w_uq", "w_qr", "w_uk")) + h.numel()
+                + q_lat.numel() + qr_p.numel()) * 2
+        b_ca = (w["w_dkv"].numel() + h.numel() + T * (wl.d_c + wl.d_r)) * 2
+        out["producers"] = {
+            "project_q_us": round(pq_ms * 1e3, 2), "project_q_gbs": round(b_pq / (pq_ms * 1e-3) / 1e9, 1),
+            "project_q_bytes": b_pq,
+            "cache_append_us": round(ca_ms * 1e3, 2), "cache_append_gbs": round(b_ca / (ca_ms * 1e-3) / 1e9, 1),
+            "cache_append_bytes": b_ca,
+        }
+        out["tflops"] = None
+        del out["absorb_q_us"]
+        out["absorb_gemm_gbs"].pop("absorb_q")
     if not args.no_cpu_baseline:
-        d = I.DecodeInputs(wl=wl, cache=cache, q_lat=q_lat.cpu(), q_rope=qr.cpu(), scale=wl.scale)
+        d = I.DecodeInputs(wl=wl, cache=cache, q_lat=q_lat.cpu(), q_rope=(qr_p if producers else qr).cpu(),
+                           scale=wl.scale)
         out["cpu_baseline"] = cpu_baseline(d, cache_bytes, max_rows=1024)
     return out
 

@@ -50,8 +50,9 @@ struct GemmArgs {
     int64_t ldb, bsb;
     void *C;             // C + b * bsc + s * css + m * ldc + n (bf16 or fp32 elements)
     int64_t ldc, bsc, css;
-    int32_t M, N, K;     // K of one split; N a multiple of 8
-    int32_t splits;      // z = b * splits + s; split s covers k in [s K, (s + 1) K)
+    int32_t M, N, K;     // K a multiple of 64; N a multiple of 8
+    int32_t splits;      // z = b * splits + s; split s covers the 64-wide stages
+                         // [s nk / splits, (s + 1) nk / splits) of the nk = K / 64
 };
 
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const void *src) {
@@ -69,8 +70,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int z = blockIdx.z, b = z / g.splits, s = z % g.splits;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int64_t k_begin = (int64_t)s * g.K;
-    const int nk = g.K / BK;
+    const int nk_all = g.K / BK;
+    const int st0 = (int)((int64_t)s * nk_all / g.splits), nk = (int)((int64_t)(s + 1) * nk_all / g.splits) - st0;
+    const int64_t k_begin = (int64_t)st0 * BK;
 
     // ---- copy offsets (bytes, relative to a per-stage scalar base)
     const uint16_t *a_base = g.A + (int64_t)b * g.bsa + (int64_t)m0 * g.lda + k_begin;
@@ -242,25 +244,18 @@ hipError_t launch_gemm(const GemmArgs &g, int batch, hipStream_t st) {
     return hipGetLastError();
 }
 
-// split count of the W_O product: enough (item, split) workgroups to fill
-// the device (~256-512), with every split a whole number of 64-wide stages
-int out_splits(int32_t T, int32_t K, int32_t d_model) {
-    const int tiles = (d_model / BN) * ((T + BM - 1) / BM);
-    int sp = 1;
-    while (sp * 2 * tiles <= 512 && K % (sp * 2 * BK) == 0) sp *= 2;
-    return sp;
-}
-
 }  // namespace
 
-// Split count for C[M][N] = A[M][K] B[K][N]: the smallest power of two that
-// gives at least 128 workgroups, with every split a whole number of 64-wide
-// stages (at most 16 splits).
+// Split count for C[M][N] = A[M][K] B[K][N]: as many splits as keep the
+// workgroups within one round on the device (256 compute units), at most 16,
+// with at least 4 of the 64-wide stages per split.
 int gemm_splits(int32_t M, int32_t N, int32_t K) {
     const int tiles = ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
-    int sp = 1;
-    while (sp < 16 && sp * tiles < 128 && K % (sp * 2 * BK) == 0) sp *= 2;
-    return sp;
+    const int nk = K / BK;
+    int sp = 256 / tiles;
+    sp = sp < 16 ? sp : 16;
+    sp = sp < nk / 4 ? sp : nk / 4;
+    return sp < 1 ? 1 : sp;
 }
 
 bool gemm_nn_mfma_ok(int32_t N, int32_t K) { return N % 8 == 0 && N >= 8 && K % BK == 0; }
@@ -273,7 +268,7 @@ hipError_t launch_gemm_nn_f32(const void *A, int64_t lda, const void *B, int64_t
     g.A = (const uint16_t *)A; g.lda = lda; g.bsa = 0;
     g.B = (const uint16_t *)B; g.ldb = ldb; g.bsb = 0;
     g.C = ws; g.ldc = N; g.bsc = 0; g.css = (int64_t)M * N;
-    g.M = M; g.N = N; g.K = K / splits; g.splits = splits;
+    g.M = M; g.N = N; g.K = K; g.splits = splits;
     return launch_gemm<false, true>(g, 1, s);
 }
 
@@ -319,7 +314,7 @@ bool absorb_out_mfma_ok(int32_t n_h, int32_t d_c, int32_t d_v, int32_t d_model, 
 }
 
 int64_t absorb_out_mfma_workspace(int32_t T, int32_t n_h, int32_t d_v, int32_t d_model) {
-    const int sp = out_splits(T, n_h * d_v, d_model);
+    const int sp = gemm_splits(T, d_model, n_h * d_v);
     return (int64_t)sp * T * d_model * 4;
 }
 
@@ -336,12 +331,12 @@ hipError_t launch_absorb_out_mfma(const void *o_lat, const void *w_uv, const voi
     if (e != hipSuccess) return e;
     // out = u . W_O over K = n_h d_v, split into fp32 partials, then summed
     const int32_t K = n_h * d_v;
-    const int sp = out_splits(T, K, d_model);
+    const int sp = gemm_splits(T, d_model, K);
     GemmArgs g2{};
     g2.A = (const uint16_t *)u_ws; g2.lda = K; g2.bsa = 0;
     g2.B = (const uint16_t *)w_o;  g2.ldb = d_model; g2.bsb = 0;
     g2.C = ws; g2.ldc = d_model; g2.bsc = 0; g2.css = (int64_t)T * d_model;
-    g2.M = T; g2.N = d_model; g2.K = K / sp; g2.splits = sp;
+    g2.M = T; g2.N = d_model; g2.K = K; g2.splits = sp;
     e = launch_gemm<false, true>(g2, 1, s);
     if (e != hipSuccess) return e;
     const int64_t n8 = (int64_t)T * d_model / 8;

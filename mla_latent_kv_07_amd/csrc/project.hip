@@ -81,6 +81,20 @@ __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
     return (c & 0x80) ? -v : v;
 }
 
+// sum over splits of ws[s * stride + i] (independent loads in flight)
+__device__ __forceinline__ float split_sum(const float *__restrict__ ws, int64_t stride, int splits, int64_t i) {
+    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+        v0 += ws[(s + 0) * stride + i];
+        v1 += ws[(s + 1) * stride + i];
+        v2 += ws[(s + 2) * stride + i];
+        v3 += ws[(s + 3) * stride + i];
+    }
+    for (; s < splits; ++s) v0 += ws[s * stride + i];
+    return (v0 + v1) + (v2 + v3);
+}
+
 struct AppendArgs {
     const float *ws;          // fp32 partials [splits][T][d_c + d_r]
     int64_t split_stride;
@@ -91,26 +105,22 @@ struct AppendArgs {
     const int32_t *bt;
     int32_t bt_stride;
     const int32_t *pos0;
+    int32_t pos0_count;       // B
     int32_t q_len, d_c, d_r;
 };
 
-// One workgroup per sequence: its q_len tokens in order (positions outside
-// the block table, p < 0 or p >= 64 bt_stride, are skipped).  For f32 / bf16 the
-// rows are rounded once and stored; for fp8 the tokens that land in one
-// block are handled together: their amax sets or raises the block scale,
-// earlier slots are re-encoded when it grows, then the codes are written.
-template <int FMT>   // 0 f32, 1 bf16, 2 fp8 (e4m3 latent + bf16 k^R)
-__global__ __launch_bounds__(256) void append_finish_kernel(AppendArgs a, RopeTab rt) {
+// fp8 caches (e4m3 latent + bf16 k^R): one workgroup per sequence, its q_len
+// tokens in order (positions outside the block table, p < 0 or
+// p >= 64 bt_stride, are skipped).  The tokens that land in one block are
+// handled together: their amax sets or raises the block scale, earlier slots
+// are re-encoded when it grows, then the codes are written.
+__global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab rt) {
     __shared__ float red[4];
     __shared__ float sh[3];
     const int b = blockIdx.x, tid = threadIdx.x;
     const int N = a.d_c + a.d_r;
     const int p0 = a.pos0[b];
-    auto xval = [&](int t, int f) {
-        float v = 0.f;
-        for (int s = 0; s < a.splits; ++s) v += a.ws[s * a.split_stride + (int64_t)t * N + f];
-        return v;
-    };
+    auto xval = [&](int t, int f) { return split_sum(a.ws, a.split_stride, a.splits, (int64_t)t * N + f); };
     auto block_of = [&](int p) {
         int64_t id = a.bt[(int64_t)b * a.bt_stride + p / kBlock];
         return id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
@@ -125,123 +135,118 @@ __global__ __launch_bounds__(256) void append_finish_kernel(AppendArgs a, RopeTa
         y1 = (x0 * s + x1 * c) * rt.mscale;
     };
 
-    if constexpr (FMT != 2) {
-        constexpr int EB = FMT == 0 ? 4 : 2;
-        for (int i = 0; i < a.q_len; ++i) {
-            const int t = b * a.q_len + i, p = p0 + i;
-            if (p < 0 || p / kBlock >= a.bt_stride) continue;   // outside the table: not written
-            uint8_t *row = a.pool + block_of(p) * a.block_bytes + (int64_t)(p % kBlock) * N * EB;
-            for (int f = tid; f < a.d_c; f += 256) {
-                const float v = xval(t, f);
-                if constexpr (FMT == 0) ((float *)row)[f] = v;
-                else ((uint16_t *)row)[f] = f32_to_bf16(v);
+    int i = 0;
+    while (i < a.q_len) {
+        const int p = p0 + i;
+        const int i_end = p < 0 ? i + 1 : min(a.q_len, (p / kBlock + 1) * kBlock - p0);   // same block
+        if (p < 0 || p / kBlock >= a.bt_stride) {   // outside the table: not written
+            i = i_end;
+            continue;
+        }
+        const int64_t blk = block_of(p);
+        uint8_t *base = a.pool + blk * a.block_bytes;
+        const int s0 = p % kBlock;
+        // amax of the new latents in this block
+        float m = 0.f;
+        for (int k = i; k < i_end; ++k)
+            for (int f = tid; f < a.d_c; f += 256) m = fmaxf(m, fabsf(xval(b * a.q_len + k, f)));
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        __syncthreads();
+        if (tid == 0) {
+            const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            const float old = a.scales[blk];
+            float sc;
+            bool grow = false;
+            if (s0 == 0) {
+                sc = amax > 0.f ? amax / 448.f : 1.f;
+            } else {
+                sc = fmaxf(old, amax / 448.f);
+                grow = sc > old;
             }
+            sh[0] = sc;
+            sh[1] = grow ? old / sc : 1.f;
+            sh[2] = grow ? 1.f : 0.f;
+            a.scales[blk] = sc;
+        }
+        __syncthreads();
+        const float sc = sh[0], ratio = sh[1];
+        if (sh[2] != 0.f) {
+            // re-encode the slots before the first new one at the larger scale
+            for (int idx = tid; idx < s0 * a.d_c; idx += 256)
+                base[idx] = f32_to_e4m3(e4m3_to_f32(base[idx]) * ratio);
+        }
+        for (int k = i; k < i_end; ++k) {
+            const int t = b * a.q_len + k, pk = p0 + k, slot = pk % kBlock;
+            for (int f = tid; f < a.d_c; f += 256) base[slot * a.d_c + f] = f32_to_e4m3(xval(t, f) / sc);
+            uint16_t *kr = (uint16_t *)(base + (int64_t)kBlock * a.d_c + (int64_t)slot * a.d_r * 2);
             for (int j = tid; j < rt.half; j += 256) {
                 float y0, y1;
-                rot(t, p, j, y0, y1);
-                if constexpr (FMT == 0) {
-                    ((float *)row)[a.d_c + 2 * j] = y0;
-                    ((float *)row)[a.d_c + 2 * j + 1] = y1;
-                } else {
-                    ((uint16_t *)row)[a.d_c + 2 * j] = f32_to_bf16(y0);
-                    ((uint16_t *)row)[a.d_c + 2 * j + 1] = f32_to_bf16(y1);
-                }
+                rot(t, pk, j, y0, y1);
+                kr[2 * j] = f32_to_bf16(y0);
+                kr[2 * j + 1] = f32_to_bf16(y1);
             }
         }
-    } else {
-        int i = 0;
-        while (i < a.q_len) {
-            const int p = p0 + i;
-            const int i_end = p < 0 ? i + 1 : min(a.q_len, (p / kBlock + 1) * kBlock - p0);   // same block
-            if (p < 0 || p / kBlock >= a.bt_stride) {   // outside the table: not written
-                i = i_end;
-                continue;
-            }
-            const int64_t blk = block_of(p);
-            uint8_t *base = a.pool + blk * a.block_bytes;
-            const int s0 = p % kBlock;
-            // amax of the new latents in this block
-            float m = 0.f;
-            for (int k = i; k < i_end; ++k)
-                for (int f = tid; f < a.d_c; f += 256) m = fmaxf(m, fabsf(xval(b * a.q_len + k, f)));
-            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-            if ((tid & 63) == 0) red[tid >> 6] = m;
-            __syncthreads();
-            if (tid == 0) {
-                const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-                const float old = a.scales[blk];
-                float sc;
-                bool grow = false;
-                if (s0 == 0) {
-                    sc = amax > 0.f ? amax / 448.f : 1.f;
-                } else {
-                    sc = fmaxf(old, amax / 448.f);
-                    grow = sc > old;
-                }
-                sh[0] = sc;
-                sh[1] = grow ? old / sc : 1.f;
-                sh[2] = grow ? 1.f : 0.f;
-                a.scales[blk] = sc;
-            }
-            __syncthreads();
-            const float sc = sh[0], ratio = sh[1];
-            if (sh[2] != 0.f) {
-                // re-encode the slots before the first new one at the larger scale
-                for (int idx = tid; idx < s0 * a.d_c; idx += 256)
-                    base[idx] = f32_to_e4m3(e4m3_to_f32(base[idx]) * ratio);
-            }
-            for (int k = i; k < i_end; ++k) {
-                const int t = b * a.q_len + k, pk = p0 + k, slot = pk % kBlock;
-                for (int f = tid; f < a.d_c; f += 256) base[slot * a.d_c + f] = f32_to_e4m3(xval(t, f) / sc);
-                uint16_t *kr = (uint16_t *)(base + (int64_t)kBlock * a.d_c + (int64_t)slot * a.d_r * 2);
-                for (int j = tid; j < rt.half; j += 256) {
-                    float y0, y1;
-                    rot(t, pk, j, y0, y1);
-                    kr[2 * j] = f32_to_bf16(y0);
-                    kr[2 * j + 1] = f32_to_bf16(y1);
-                }
-            }
-            __syncthreads();   // red / sh are reused by the next block
-            i = i_end;
-        }
+        __syncthreads();   // red / sh are reused by the next block
+        i = i_end;
     }
 }
 
-// q^R: out[t][h][:] = RoPE(sum_s ws[s][t][h d_r ..]) at pos[t], times mscale.
-// One workgroup per token; cos / sin of its position computed once in fp64.
+// f32 / bf16 caches: one thread per (token, pair of row values); the rotary
+// pairs turn by p theta_j (fp64 angle), then every value is rounded once.
+template <int FMT>   // 0 f32, 1 bf16
+__global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab rt) {
+    const int N = a.d_c + a.d_r, P2 = N / 2;
+    const int64_t idx = blockIdx.x * 256ll + threadIdx.x;
+    if (idx >= (int64_t)a.q_len * a.pos0_count * P2) return;
+    const int t = (int)(idx / P2), k = (int)(idx % P2);
+    const int b = t / a.q_len, p = a.pos0[b] + t % a.q_len;
+    if (p < 0 || p / kBlock >= a.bt_stride) return;   // outside the table: not written
+    int64_t blk = a.bt[(int64_t)b * a.bt_stride + p / kBlock];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    const int64_t o = (int64_t)t * N + 2 * k;
+    float y0 = split_sum(a.ws, a.split_stride, a.splits, o);
+    float y1 = split_sum(a.ws, a.split_stride, a.splits, o + 1);
+    if (2 * k >= a.d_c) {
+        const int j = k - a.d_c / 2;
+        double sn, cs;
+        sincos((double)p * rt.theta[j], &sn, &cs);
+        const float c = (float)cs, s = (float)sn;
+        const float x0 = y0, x1 = y1;
+        y0 = (x0 * c - x1 * s) * rt.mscale;
+        y1 = (x0 * s + x1 * c) * rt.mscale;
+    }
+    uint8_t *row = a.pool + blk * a.block_bytes + (int64_t)(p % kBlock) * N * (FMT == 0 ? 4 : 2);
+    if constexpr (FMT == 0) {
+        *(float2 *)((float *)row + 2 * k) = make_float2(y0, y1);
+    } else {
+        *(uint32_t *)((uint16_t *)row + 2 * k) = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+    }
+}
+
+// q^R: out[t][h][2j, 2j+1] = RoPE of the summed partials at pos[t], times
+// mscale; one thread per (token, head, pair), angle p theta_j in fp64.
 template <typename OutT>
 __global__ __launch_bounds__(256) void rope_q_kernel(const float *__restrict__ ws, int64_t split_stride,
                                                      int32_t splits, const int32_t *__restrict__ pos,
-                                                     int32_t n_h, int32_t d_r, OutT *__restrict__ out,
+                                                     int32_t T, int32_t n_h, int32_t d_r, OutT *__restrict__ out,
                                                      RopeTab rt) {
-    __shared__ float cs[kMaxRopePairs], sn[kMaxRopePairs];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const int p = pos[t];
-    for (int j = tid; j < rt.half; j += 256) {
-        double s, c;
-        sincos((double)p * rt.theta[j], &s, &c);
-        cs[j] = (float)c;
-        sn[j] = (float)s;
-    }
-    __syncthreads();
-    const int W = n_h * d_r;
-    for (int idx = tid; idx < n_h * rt.half; idx += 256) {
-        const int h = idx / rt.half, j = idx % rt.half;
-        const int64_t o = (int64_t)t * W + h * d_r + 2 * j;
-        float x0 = 0.f, x1 = 0.f;
-        for (int s = 0; s < splits; ++s) {
-            x0 += ws[s * split_stride + o];
-            x1 += ws[s * split_stride + o + 1];
-        }
-        const float y0 = (x0 * cs[j] - x1 * sn[j]) * rt.mscale;
-        const float y1 = (x0 * sn[j] + x1 * cs[j]) * rt.mscale;
-        if constexpr (sizeof(OutT) == 2) {
-            out[o] = f32_to_bf16(y0);
-            out[o + 1] = f32_to_bf16(y1);
-        } else {
-            out[o] = y0;
-            out[o + 1] = y1;
-        }
+    const int64_t idx = blockIdx.x * 256ll + threadIdx.x;
+    const int64_t per_t = (int64_t)n_h * rt.half;
+    if (idx >= T * per_t) return;
+    const int t = (int)(idx / per_t), hj = (int)(idx % per_t);
+    const int h = hj / rt.half, j = hj % rt.half;
+    const int64_t o = (int64_t)t * n_h * d_r + (int64_t)h * d_r + 2 * j;
+    const float x0 = split_sum(ws, split_stride, splits, o), x1 = split_sum(ws, split_stride, splits, o + 1);
+    double sn, cs;
+    sincos((double)pos[t] * rt.theta[j], &sn, &cs);
+    const float c = (float)cs, s = (float)sn;
+    const float y0 = (x0 * c - x1 * s) * rt.mscale, y1 = (x0 * s + x1 * c) * rt.mscale;
+    if constexpr (sizeof(OutT) == 2) {
+        *(uint32_t *)(out + o) = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+    } else {
+        out[o] = y0;
+        out[o + 1] = y1;
     }
 }
 
@@ -325,13 +330,15 @@ hipError_t launch_cache_append(const void *h, const void *w_kv, mla_dtype_t dt, 
     AppendArgs a{};
     a.ws = ws; a.split_stride = (int64_t)T * N; a.splits = sp;
     a.pool = pool; a.scales = scales; a.block_bytes = block_bytes; a.num_blocks = num_blocks;
-    a.bt = bt; a.bt_stride = bt_stride; a.pos0 = pos0; a.q_len = q_len; a.d_c = d_c; a.d_r = d_r;
+    a.bt = bt; a.bt_stride = bt_stride; a.pos0 = pos0; a.pos0_count = B; a.q_len = q_len;
+    a.d_c = d_c; a.d_r = d_r;
+    const unsigned rows_grid = (unsigned)(((int64_t)T * (N / 2) + 255) / 256);
     if (kv == MLA_DT_F32)
-        hipLaunchKernelGGL(append_finish_kernel<0>, dim3(B), dim3(256), 0, s, a, rt);
+        hipLaunchKernelGGL(append_rows_kernel<0>, dim3(rows_grid), dim3(256), 0, s, a, rt);
     else if (kv == MLA_DT_BF16)
-        hipLaunchKernelGGL(append_finish_kernel<1>, dim3(B), dim3(256), 0, s, a, rt);
+        hipLaunchKernelGGL(append_rows_kernel<1>, dim3(rows_grid), dim3(256), 0, s, a, rt);
     else
-        hipLaunchKernelGGL(append_finish_kernel<2>, dim3(B), dim3(256), 0, s, a, rt);
+        hipLaunchKernelGGL(append_fp8_kernel, dim3(B), dim3(256), 0, s, a, rt);
     return hipGetLastError();
 }
 
@@ -425,12 +432,13 @@ hipError_t launch_project_q(const void *h, const void *w_dq, const void *w_uq, c
         if (e != hipSuccess) return e;
     }
     const float *w3 = (const float *)(w + q.off_w3);
+    const unsigned rg = (unsigned)(((int64_t)T * n_h * (d_r / 2) + 255) / 256);
     if (dt == MLA_DT_BF16)
-        hipLaunchKernelGGL(rope_q_kernel<uint16_t>, dim3(T), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
-                           n_h, d_r, (uint16_t *)q_rope, rt);
+        hipLaunchKernelGGL(rope_q_kernel<uint16_t>, dim3(rg), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
+                           T, n_h, d_r, (uint16_t *)q_rope, rt);
     else
-        hipLaunchKernelGGL(rope_q_kernel<float>, dim3(T), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
-                           n_h, d_r, (float *)q_rope, rt);
+        hipLaunchKernelGGL(rope_q_kernel<float>, dim3(rg), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
+                           T, n_h, d_r, (float *)q_rope, rt);
     return hipGetLastError();
 }
 
