@@ -86,18 +86,25 @@ C5 = Workload("full_layer_b128_bf16", 1005, "bf16", "bf16", B=128, q_len=1, n_h=
 
 WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5)}
 
-_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+# fp8 cache formats: torch code type, largest finite value, whether k^R is coded too
+_FP8 = {"fp8_e4m3": (torch.float8_e4m3fn, 448.0, False),
+        "fp8_e5m2": (torch.float8_e5m2, 57344.0, False),
+        "fp8_e4m3_row": (torch.float8_e4m3fn, 448.0, True)}
 
 
 def block_bytes(kv_dtype: str, d_c: int, d_r: int) -> int:
-    """Bytes of one 64-token block: [64][d_c + d_r] rows for f32/bf16; for fp8,
-    64 x d_c e4m3 codes followed by 64 x d_r bf16 RoPE keys."""
+    """Bytes of one 64-token block: [64][d_c + d_r] rows for f32/bf16/f16; for
+    fp8_e4m3 / fp8_e5m2, 64 x d_c codes followed by 64 x d_r bf16 RoPE keys;
+    for fp8_e4m3_row, 64 rows of d_c + d_r e4m3 codes."""
     if kv_dtype == "f32":
         return BLOCK * (d_c + d_r) * 4
-    if kv_dtype == "bf16":
+    if kv_dtype in ("bf16", "f16"):
         return BLOCK * (d_c + d_r) * 2
-    if kv_dtype == "fp8_e4m3":
+    if kv_dtype in ("fp8_e4m3", "fp8_e5m2"):
         return BLOCK * d_c + BLOCK * d_r * 2
+    if kv_dtype == "fp8_e4m3_row":
+        return BLOCK * (d_c + d_r)
     raise ValueError(kv_dtype)
 
 
@@ -270,26 +277,33 @@ def page_cache(wl: Workload, g: torch.Generator, seq_lens: torch.Tensor,
     bb = block_bytes(wl.kv_dtype, d_c, d_r)
     pool = torch.empty((num_blocks, bb), dtype=torch.uint8)
     scales = None
-    if wl.kv_dtype in ("f32", "bf16"):
+    if wl.kv_dtype in ("f32", "bf16", "f16"):
         dt = _TORCH_DT[wl.kv_dtype]
         typed = pool.view(dt).view(num_blocks, BLOCK, d_c + d_r)
         typed[:] = float("nan")
         typed[perm[:total]] = logical
     else:
-        # fp8: one scale per block = absmax of its valid latent values / 448
-        # (448 = largest finite e4m3); an all-zero block takes scale 1.
-        c = logical[:, :, :d_c]
+        # fp8: one scale per block = absmax of its valid coded values / the
+        # format's largest finite value (448 e4m3, 57344 e5m2); an all-zero
+        # block takes scale 1.  The coded values are the latent, or the whole
+        # row for fp8_e4m3_row.
+        code_dt, top, full = _FP8[wl.kv_dtype]
+        c = logical if full else logical[:, :, :d_c]
         finite = torch.nan_to_num(c, nan=0.0).abs()
         amax = finite.amax(dim=(1, 2))
-        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-        scaled = (c / sc[:, None, None]).clamp(-448.0, 448.0)   # NaN stays NaN
-        codes = scaled.to(torch.float8_e4m3fn).view(torch.uint8)
-        kr = logical[:, :, d_c:].to(torch.bfloat16).view(torch.uint8).reshape(total, -1)
-        blk = torch.cat([codes.reshape(total, -1), kr], dim=1)
+        sc = torch.where(amax > 0, amax / top, torch.ones_like(amax))
+        scaled = (c / sc[:, None, None]).clamp(-top, top)   # NaN stays NaN
+        codes = scaled.to(code_dt).view(torch.uint8)
         pool[:] = 0
-        # spare blocks: NaN codes and NaN RoPE keys
-        pool[:, :BLOCK * d_c] = 0x7F
-        pool[:, BLOCK * d_c:].view(torch.bfloat16)[:] = float("nan")
+        if full:
+            blk = codes.reshape(total, -1)
+            pool[:] = 0x7F                      # spare blocks: NaN codes
+        else:
+            kr = logical[:, :, d_c:].to(torch.bfloat16).view(torch.uint8).reshape(total, -1)
+            blk = torch.cat([codes.reshape(total, -1), kr], dim=1)
+            # spare blocks: NaN codes and NaN RoPE keys
+            pool[:, :BLOCK * d_c] = 0x7F
+            pool[:, BLOCK * d_c:].view(torch.bfloat16)[:] = float("nan")
         pool[perm[:total]] = blk
         scales = torch.full((num_blocks,), float("nan"), dtype=torch.float32)
         scales[perm[:total]] = sc

@@ -26,7 +26,8 @@
 #include <string.h>
 
 /* Storage formats of a cached token row [c (d_c) | k^R (d_r)]. */
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2, ORACLE_F16 = 3, ORACLE_FP8_E5M2 = 4,
+       ORACLE_FP8_E4M3_ROW = 5 };
 
 /* Tokens per paged block: the FlashMLA backend accepts only 64
  * ([vllm], "FlashMLABackend: 하드웨어 요구사항"). */
@@ -64,6 +65,57 @@ double oracle_e4m3_to_f64(uint8_t code)
     return s ? -v : v;
 }
 
+/* IEEE binary16: 1 sign, 5 exponent bits (bias 15), 10 mantissa bits;
+ * exponent field 0 is subnormal (m * 2^-24), 31 is inf / NaN.  The fp16 cache
+ * is one of the kv-cache dtypes of [vllm] "FlashMLABackend". */
+double oracle_f16_to_f64(uint16_t bits)
+{
+    int s = bits >> 15, e = (bits >> 10) & 0x1F, m = bits & 0x3FF;
+    double v;
+    if (e == 31) return m ? NAN : (s ? -INFINITY : INFINITY);
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else
+        v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+    return s ? -v : v;
+}
+
+/* OCP FP8 E5M2: 1 sign, 5 exponent bits (bias 15), 2 mantissa bits, IEEE-like
+ * (exponent 31: mantissa 0 = inf, else NaN), exponent 0 subnormal (m/4 2^-14).
+ * [huny] §6 names E4M3 or E5M2 for the latent cache. */
+double oracle_e5m2_to_f64(uint8_t code)
+{
+    int s = code >> 7, e = (code >> 2) & 0x1F, m = code & 3;
+    double v;
+    if (e == 31) return m ? NAN : (s ? -INFINITY : INFINITY);
+    if (e == 0)
+        v = ldexp((double)m, -16);                /* m/4 * 2^(1-15) */
+    else
+        v = ldexp(1.0 + (double)m / 4.0, e - 15);
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even into E5M2, saturating to +-57344 (the largest finite
+ * value) as the E4M3 encoder saturates; NaN -> 0x7F.  Scan of every
+ * non-negative finite code, ties to the even mantissa. */
+uint8_t oracle_f64_to_e5m2(double x)
+{
+    if (isnan(x)) return 0x7F;
+    uint8_t sign = (x < 0) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (a >= 57344.0) return sign | 0x7B;
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7B; ++c) {
+        double err = fabs(oracle_e5m2_to_f64((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
 /* Round-to-nearest-even into E4M3, saturating to +-448 (the largest finite
  * value).  Done the slow, obvious way: scan every non-negative finite code for
  * the nearest value; on a tie take the code whose mantissa LSB is 0. */
@@ -95,13 +147,21 @@ uint8_t oracle_f64_to_e4m3(double x)
  *              [donmain] "위치 정보와 압축의 충돌").
  *  FP8:        c as e4m3 codes [64][d_c], then k^R kept in bf16 [64][d_r]
  *              ([huny] §6: the RoPE key keeps 16-bit precision), with one
- *              fp32 scale per block held in a separate array. */
+ *              fp32 scale per block held in a separate array.
+ *  F16:        64 rows of [c | k^R] in IEEE fp16 ([vllm] kv-cache dtypes).
+ *  FP8 E5M2:   as FP8 with e5m2 codes ([huny] §6 "E4M3 or E5M2").
+ *  FP8 E4M3 row: the whole row [c | k^R] as e4m3 codes [64][d_c + d_r], one
+ *              scale per block for both parts (an fp8 cache read literally
+ *              as "the cache stored as e4m3"). */
 int64_t oracle_block_bytes(int fmt, int d_c, int d_r)
 {
     switch (fmt) {
     case ORACLE_F32:  return (int64_t)ORACLE_BLOCK * (d_c + d_r) * 4;
     case ORACLE_BF16: return (int64_t)ORACLE_BLOCK * (d_c + d_r) * 2;
-    case ORACLE_FP8_E4M3: return (int64_t)ORACLE_BLOCK * d_c + (int64_t)ORACLE_BLOCK * d_r * 2;
+    case ORACLE_FP8_E4M3:
+    case ORACLE_FP8_E5M2: return (int64_t)ORACLE_BLOCK * d_c + (int64_t)ORACLE_BLOCK * d_r * 2;
+    case ORACLE_F16: return (int64_t)ORACLE_BLOCK * (d_c + d_r) * 2;
+    case ORACLE_FP8_E4M3_ROW: return (int64_t)ORACLE_BLOCK * (d_c + d_r);
     default: return -1;
     }
 }
@@ -124,11 +184,21 @@ static void load_row(const uint8_t *pool, int fmt, const float *blk_scale,
         const uint16_t *row = (const uint16_t *)base + (int64_t)slot * (d_c + d_r);
         for (int f = 0; f < d_c; ++f) c[f] = oracle_bf16_to_f64(row[f]);
         for (int f = 0; f < d_r; ++f) kr[f] = oracle_bf16_to_f64(row[d_c + f]);
+    } else if (fmt == ORACLE_F16) {
+        const uint16_t *row = (const uint16_t *)base + (int64_t)slot * (d_c + d_r);
+        for (int f = 0; f < d_c; ++f) c[f] = oracle_f16_to_f64(row[f]);
+        for (int f = 0; f < d_r; ++f) kr[f] = oracle_f16_to_f64(row[d_c + f]);
+    } else if (fmt == ORACLE_FP8_E4M3_ROW) {
+        const uint8_t *row = base + (int64_t)slot * (d_c + d_r);
+        double sc = (double)blk_scale[blk];
+        for (int f = 0; f < d_c; ++f) c[f] = oracle_e4m3_to_f64(row[f]) * sc;
+        for (int f = 0; f < d_r; ++f) kr[f] = oracle_e4m3_to_f64(row[d_c + f]) * sc;
     } else {
         const uint8_t *crow = base + (int64_t)slot * d_c;
         const uint16_t *krow = (const uint16_t *)(base + (int64_t)ORACLE_BLOCK * d_c) + (int64_t)slot * d_r;
         double sc = (double)blk_scale[blk];
-        for (int f = 0; f < d_c; ++f) c[f] = oracle_e4m3_to_f64(crow[f]) * sc;
+        for (int f = 0; f < d_c; ++f)
+            c[f] = (fmt == ORACLE_FP8_E5M2 ? oracle_e5m2_to_f64(crow[f]) : oracle_e4m3_to_f64(crow[f])) * sc;
         for (int f = 0; f < d_r; ++f) kr[f] = oracle_bf16_to_f64(krow[f]);
     }
 }
@@ -153,7 +223,7 @@ int oracle_gather(const void *pool_v, int fmt, int d_c, int d_r,
             int slot = p % ORACLE_BLOCK;
             uint8_t *dst = out + ((int64_t)b * max_tokens + p) * row_bytes;
             const uint8_t *base = pool + blk * blk_bytes;
-            if (fmt == ORACLE_FP8_E4M3) {
+            if (fmt == ORACLE_FP8_E4M3 || fmt == ORACLE_FP8_E5M2) {
                 memcpy(dst, base + (int64_t)slot * d_c, (size_t)d_c);
                 memcpy(dst + d_c, base + (int64_t)ORACLE_BLOCK * d_c + (int64_t)slot * d_r * 2,
                        (size_t)d_r * 2);

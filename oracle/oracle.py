@@ -26,7 +26,9 @@ from pathlib import Path
 import numpy as np
 
 __all__ = [
-    "PIN_STATUS", "FMT_F32", "FMT_BF16", "FMT_FP8_E4M3", "BLOCK",
+    "PIN_STATUS", "FMT_F32", "FMT_BF16", "FMT_FP8_E4M3", "FMT_F16", "FMT_FP8_E5M2", "FMT_FP8_E4M3_ROW",
+    "FP8_SPLIT", "SCALED", "FP8_MAX", "BLOCK", "f16_bits_to_f64", "e5m2_to_f64", "f64_to_e5m2", "f64_to_f16",
+    "fp8_decode", "fp8_encode",
     "lib", "build_oracle", "threads",
     "kv_bytes_per_token_layer", "kv_cache_bytes", "floats_per_token_all_layers",
     "bf16_bits_to_f64", "e4m3_to_f64", "f64_to_e4m3", "f64_to_bf16", "block_bytes",
@@ -41,7 +43,10 @@ _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "mla_oracle.c"
 _SO = _HERE / "liboracle.so"
 
-FMT_F32, FMT_BF16, FMT_FP8_E4M3 = 0, 1, 2
+FMT_F32, FMT_BF16, FMT_FP8_E4M3, FMT_F16, FMT_FP8_E5M2, FMT_FP8_E4M3_ROW = 0, 1, 2, 3, 4, 5
+FP8_SPLIT = (FMT_FP8_E4M3, FMT_FP8_E5M2)        # 8-bit latent codes + bf16 k^R
+SCALED = (FMT_FP8_E4M3, FMT_FP8_E5M2, FMT_FP8_E4M3_ROW)
+FP8_MAX = {FMT_FP8_E4M3: 448.0, FMT_FP8_E4M3_ROW: 448.0, FMT_FP8_E5M2: 57344.0}
 BLOCK = 64  # tokens per paged block ([vllm] "FlashMLABackend: 하드웨어 요구사항")
 
 # How each oracle function is pinned to something other than itself.
@@ -59,6 +64,13 @@ PIN_STATUS = {
     "rope_inv_freq": "pinned: factor 1 is plain RoPE; YaRN's two limits (position interpolation p/s "
                      "below beta_slow, plain RoPE above beta_fast) in closed form; relative-position "
                      "property and the mscale norm factor with the scaled frequencies",
+    "f16_bits_to_f64": "pinned: numpy's fp16 decode over all 65536 codes",
+    "f64_to_f16": "pinned: torch's fp32->fp16 cast on fp32 values (numpy's correctly rounded cast is the step)",
+    "e5m2_to_f64": "pinned: OCP E5M2 landmarks + torch float8_e5m2->fp64 over all 256 codes",
+    "f64_to_e5m2": "pinned: torch float8_e5m2 cast below the saturation point (RNE, ties, subnormals); "
+                   "saturation to +-57344",
+    "decode (f16, fp8_e5m2, fp8_e4m3_row caches)": "pinned: torch SDPA fp64 on the f16-rounded rows; fp8 "
+                   "variants equal the fp32 cache of torch-decoded codes times the block scale",
     "f64_to_bf16": "pinned: torch's fp32->bf16 cast on fp32-exact values incl. ties and subnormals; "
                    "nearest of the two neighbours (independently pinned decoder) on fp64 values",
     "cache_append": "pinned: appended rows gather back as the single rounding of project_kv's rows "
@@ -109,6 +121,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_to_f64.restype = dbl
         L.oracle_f64_to_e4m3.argtypes = [dbl]
         L.oracle_f64_to_e4m3.restype = ctypes.c_uint8
+        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_f64.restype = dbl
+        L.oracle_e5m2_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_e5m2_to_f64.restype = dbl
+        L.oracle_f64_to_e5m2.argtypes = [dbl]
+        L.oracle_f64_to_e5m2.restype = ctypes.c_uint8
         L.oracle_block_bytes.argtypes = [i32, i32, i32]
         L.oracle_block_bytes.restype = i64
         L.oracle_gather.argtypes = [P, i32, i32, i32, P, i32, P, i32, i32, P]
@@ -229,6 +247,42 @@ def f64_to_bf16(x: np.ndarray) -> np.ndarray:
     out[...] = np.where(fin, np.copysign(q, x), x)
     bits = (out.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     return np.where(np.isnan(x), np.uint16(0x7FC0), bits)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """IEEE fp16 bit patterns -> float64, from the format definition."""
+    L = lib()
+    table = np.array([L.oracle_f16_to_f64(c) for c in range(65536)], dtype=np.float64)
+    return table[np.asarray(bits, dtype=np.uint16)]
+
+
+def f64_to_f16(x: np.ndarray) -> np.ndarray:
+    """float64 -> IEEE fp16 bit patterns, one round-to-nearest-even step
+    (numpy's double -> half conversion; overflow -> inf)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def e5m2_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E5M2 codes -> float64, from the format definition."""
+    L = lib()
+    table = np.array([L.oracle_e5m2_to_f64(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def f64_to_e5m2(x: np.ndarray) -> np.ndarray:
+    """float64 -> E5M2 codes, round-to-nearest-even, saturating at +-57344."""
+    L = lib()
+    flat = np.asarray(x, dtype=np.float64).ravel()
+    out = np.array([L.oracle_f64_to_e5m2(float(v)) for v in flat], dtype=np.uint8)
+    return out.reshape(np.shape(x))
+
+
+def fp8_decode(fmt: int, codes: np.ndarray) -> np.ndarray:
+    return e5m2_to_f64(codes) if fmt == FMT_FP8_E5M2 else e4m3_to_f64(codes)
+
+
+def fp8_encode(fmt: int, x: np.ndarray) -> np.ndarray:
+    return f64_to_e5m2(x) if fmt == FMT_FP8_E5M2 else f64_to_e4m3(x)
 
 
 def block_bytes(fmt: int, d_c: int, d_r: int) -> int:
@@ -430,16 +484,20 @@ def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, 
     "FlashMLAImpl").  The exact fp64 row is rounded once into the storage
     format: f32 / bf16 rows to nearest-even.
 
-    fp8 (e4m3 latent, bf16 k^R, one scale per block: [huny] §6 FP8 item) — the
-    pages ask for a dynamic per-block scale and give no update rule for a
-    block that fills over several calls.  Reading used here:
+    fp16 rows round to nearest-even once too.
+
+    fp8 (e4m3 or e5m2 latent with bf16 k^R, or the whole row in e4m3; one
+    scale per block: [huny] §6 FP8 item) — the pages ask for a dynamic
+    per-block scale and give no update rule for a block that fills over
+    several calls.  Reading used here (M = 448 for e4m3, 57344 for e5m2; the
+    amax covers the coded values: c, or c and k^R for the whole-row format):
       - a block whose slot 0 is written by this call starts fresh: its scale
-        is amax|c| over the tokens written into it / 448 (1 if that is 0),
-        as for a block written whole;
-      - otherwise scale' = max(scale, amax / 448); when it grows, the codes
-        of the slots before the first one written are re-encoded,
-        code' = e4m3(value(code) * scale / scale');
-      - the new codes are e4m3(c / scale').
+        is amax over the tokens written into it / M (1 if that is 0), as for
+        a block written whole;
+      - otherwise scale' = max(scale, amax / M); when it grows, the codes of
+        the slots before the first one written are re-encoded,
+        code' = fp8(value(code) * scale / scale');
+      - the new codes are fp8(value / scale').
     Scales are kept as float32; the codes use the stored float32 value.
     pool: uint8 [num_blocks][block_bytes]; block_scales: float32 [num_blocks]
     (fp8 only).  Both are modified."""
@@ -451,10 +509,12 @@ def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, 
     pos = (pos0[:, None].astype(np.int64) + np.arange(q_len)[None, :]).reshape(T)
     c, kr = project_kv(h, w_kv, d_c, pos, inv_freq=inv_freq, mscale=mscale)
     nblk_pool = pool.shape[0]
-    if fmt in (FMT_F32, FMT_BF16):
+    if fmt in (FMT_F32, FMT_BF16, FMT_F16):
         rows = np.concatenate([c, kr], axis=1)
         if fmt == FMT_BF16:
             enc = f64_to_bf16(rows).view(np.uint8).reshape(T, -1)
+        elif fmt == FMT_F16:
+            enc = f64_to_f16(rows).view(np.uint8).reshape(T, -1)
         else:
             enc = rows.astype(np.float32).view(np.uint8).reshape(T, -1)
         rb = enc.shape[1]
@@ -464,7 +524,11 @@ def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, 
             assert 0 <= blk < nblk_pool
             pool[blk, (p % BLOCK) * rb:(p % BLOCK + 1) * rb] = enc[t]
         return
-    assert fmt == FMT_FP8_E4M3
+    assert fmt in SCALED
+    full = fmt == FMT_FP8_E4M3_ROW
+    W = d_c + d_r if full else d_c                  # code bytes per token
+    vals = np.concatenate([c, kr], axis=1) if full else c
+    top = FP8_MAX[fmt]
     scales = np.asarray(block_scales)
     kr_bits = f64_to_bf16(kr).view(np.uint8).reshape(T, -1)
     for b in range(B):
@@ -478,9 +542,9 @@ def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, 
             assert 0 <= blk < nblk_pool
             toks = [b * q_len + i for i in idx]
             slots = [int(pos[t]) % BLOCK for t in toks]
-            amax = float(np.max(np.abs(c[toks])))
+            amax = float(np.max(np.abs(vals[toks])))
             fresh = min(slots) == 0
-            new = amax / E4M3_MAX
+            new = amax / top
             if fresh:
                 sc = float(np.float32(new if amax > 0 else 1.0))
             else:
@@ -488,13 +552,14 @@ def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, 
                 sc = float(np.float32(max(old, new)))
                 if sc > old:
                     s0 = min(slots)
-                    codes = pool[blk, :s0 * d_c]
-                    pool[blk, :s0 * d_c] = f64_to_e4m3(e4m3_to_f64(codes) * (old / sc))
+                    codes = pool[blk, :s0 * W]
+                    pool[blk, :s0 * W] = fp8_encode(fmt, fp8_decode(fmt, codes) * (old / sc))
             scales[blk] = np.float32(sc)
             for t, sl in zip(toks, slots):
-                pool[blk, sl * d_c:(sl + 1) * d_c] = f64_to_e4m3(c[t] / sc)
-                off = BLOCK * d_c + sl * 2 * d_r
-                pool[blk, off:off + 2 * d_r] = kr_bits[t]
+                pool[blk, sl * W:(sl + 1) * W] = fp8_encode(fmt, vals[t] / sc)
+                if not full:
+                    off = BLOCK * d_c + sl * 2 * d_r
+                    pool[blk, off:off + 2 * d_r] = kr_bits[t]
 
 
 def absorb_q(q_nope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:

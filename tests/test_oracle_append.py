@@ -151,7 +151,10 @@ def _touched(d, fmt):
     for b, L in enumerate(d["lens"]):
         for p in range(L):
             blk, sl = d["bt"][b, p // BLK], p % BLK
-            if fmt == O.FMT_FP8_E4M3:
+            if fmt == O.FMT_FP8_E4M3_ROW:
+                W = d["d_c"] + d["d_r"]
+                m[blk, sl * W:(sl + 1) * W] = True
+            elif fmt in O.FP8_SPLIT:
                 m[blk, sl * d["d_c"]:(sl + 1) * d["d_c"]] = True
                 off = BLK * d["d_c"] + sl * 2 * d["d_r"]
                 m[blk, off:off + 2 * d["d_r"]] = True
@@ -160,7 +163,7 @@ def _touched(d, fmt):
     return m
 
 
-@pytest.mark.parametrize("fmt", [O.FMT_BF16, O.FMT_F32])
+@pytest.mark.parametrize("fmt", [O.FMT_BF16, O.FMT_F32, O.FMT_F16])
 def test_append_writes_rounded_projected_rows(fmt):
     lens = [1, 64, 65, 130, 7]
     d = _append_all(fmt, lens, [1, 2, 3, 64, 1, 1, 5, 64, 64, 64, 1, 1, 1, 1, 1, 1, 1, 1], seed=1)
@@ -171,6 +174,8 @@ def test_append_writes_rounded_projected_rows(fmt):
         exact = np.concatenate([c, kr], axis=1)
         if fmt == O.FMT_BF16:
             want = O.f64_to_bf16(exact).view(np.uint8).reshape(L, -1)
+        elif fmt == O.FMT_F16:
+            want = O.f64_to_f16(exact).view(np.uint8).reshape(L, -1)
         else:
             want = exact.astype(np.float32).view(np.uint8).reshape(L, -1)
         assert np.array_equal(rows[b, :L], want)
@@ -283,3 +288,32 @@ def test_absorbed_queries_give_the_unabsorbed_scores():
         for i in range(n_h):
             full = np.concatenate([q_nope[t, i], q_rope2[t, i]]) @ np.concatenate([c @ w_uk[i], kr], axis=1).T
             np.testing.assert_allclose(q_lat[t, i] @ c.T + q_rope[t, i] @ kr.T, full, rtol=1e-10)
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_FP8_E5M2, O.FMT_FP8_E4M3_ROW])
+def test_append_other_fp8_whole_block(fmt):
+    # e5m2 latent: scale = amax|c| / 57344; whole-row e4m3: one scale from the
+    # amax over c and k^R, every row value coded; within half a code step
+    d = _append_all(fmt, [64, 128], [64, 64], seed=8)
+    full = fmt == O.FMT_FP8_E4M3_ROW
+    W = 48 if full else 32
+    top = O.FP8_MAX[fmt]
+    half_step = 2.0 ** -4 if fmt != O.FMT_FP8_E5M2 else 2.0 ** -3
+    sub = 2.0 ** -10 if fmt != O.FMT_FP8_E5M2 else 2.0 ** -17
+    for b, L in enumerate([64, 128]):
+        c, kr = O.project_kv(d["H"][b, :L], d["w"], 32, np.arange(L))
+        vals = np.concatenate([c, kr], axis=1) if full else c
+        for lb in range(L // BLK):
+            blk = d["bt"][b, lb]
+            vb = vals[lb * BLK:(lb + 1) * BLK]
+            sc = np.float32(np.abs(vb).max() / top)
+            assert d["scales"][blk] == sc
+            codes = d["pool"][blk, :BLK * W].reshape(BLK, W)
+            val = O.fp8_decode(fmt, codes) * float(sc)
+            bound = np.maximum(np.abs(vb) * half_step, sub * float(sc)) * 1.0000001
+            assert np.all(np.abs(val - vb) <= bound)
+            if not full:
+                krb = d["pool"][blk, BLK * 32:].copy().view(np.uint16).reshape(BLK, 16)
+                assert np.array_equal(krb, O.f64_to_bf16(kr[lb * BLK:(lb + 1) * BLK]))
+    m = _touched(d, fmt)
+    assert np.array_equal(d["pool"][~m], d["pool0"][~m])

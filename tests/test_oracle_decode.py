@@ -27,7 +27,8 @@ def _paged(wl, rows, seed, seq_lens):
 
 
 def _fmt(kv):
-    return {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "fp8_e4m3": O.FMT_FP8_E4M3}[kv]
+    return {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "fp8_e4m3": O.FMT_FP8_E4M3, "f16": O.FMT_F16,
+            "fp8_e5m2": O.FMT_FP8_E5M2, "fp8_e4m3_row": O.FMT_FP8_E4M3_ROW}[kv]
 
 
 def _small(kv="bf16", n_h=16, d_c=64, d_r=16, q_len=1, seq=(1, 70, 200)):
@@ -39,10 +40,12 @@ def _rounded_rows(wl, rows):
     """Logical rows as the cache stores them (exact values)."""
     if wl.kv_dtype == "bf16":
         return rows.to(torch.bfloat16).to(torch.float64)
+    if wl.kv_dtype == "f16":
+        return rows.to(torch.float16).to(torch.float64)
     return rows.to(torch.float64)
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "f16"])
 def test_decode_matches_sdpa_fp64(kv):
     wl = _small(kv)
     g = _gen(11)
@@ -116,7 +119,7 @@ def test_decode_block_table_permutation_invariant():
 
 
 def test_gather_returns_logical_rows():
-    for kv in ("f32", "bf16", "fp8_e4m3"):
+    for kv in ("f32", "bf16", "fp8_e4m3", "f16", "fp8_e5m2", "fp8_e4m3_row"):
         wl = _small(kv, seq=(3, 64, 129))
         rows = I.draw_cache_rows(wl, _gen(15), torch.tensor(wl.seq_lens))
         cache = _paged(wl, rows, 6, wl.seq_lens)
@@ -128,6 +131,13 @@ def test_gather_returns_logical_rows():
                 want = rows[start:start + S].numpy().view(np.uint8).reshape(S, -1)
             elif kv == "bf16":
                 want = rows[start:start + S].to(torch.bfloat16).view(torch.int16).numpy().view(np.uint8).reshape(S, -1)
+            elif kv == "f16":
+                want = rows[start:start + S].to(torch.float16).view(torch.int16).numpy().view(np.uint8).reshape(S, -1)
+            elif kv == "fp8_e4m3_row":
+                # the whole row's codes, straight from the pool block the table names
+                W = wl.d_c + wl.d_r
+                want = np.stack([cache.pool[int(cache.block_table[b, p // 64])].numpy()[(p % 64) * W:(p % 64 + 1) * W]
+                                 for p in range(S)])
             else:
                 # rebuild the row bytes from the pool block the table names:
                 # codes of the latent, then the bf16 RoPE key
@@ -218,6 +228,34 @@ def test_fp8_cache_reads_codes_times_block_scale():
     pool32 = torch.cat([c, kr], dim=2).contiguous().view(torch.uint8).view(nb, -1)
     o32, l32 = O.decode(pool32, O.FMT_F32, cache.block_table, cache.seq_lens, ql, qr, wl.scale, q_len=2)
     # fp32 rounding of code * scale is the only difference
+    np.testing.assert_allclose(o8, o32, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(l8, l32, rtol=1e-6, atol=1e-6)
+    assert np.all(np.isfinite(o8))
+
+
+@pytest.mark.parametrize("kv,code_dt", [("fp8_e5m2", torch.float8_e5m2), ("fp8_e4m3_row", torch.float8_e4m3fn)])
+def test_other_fp8_caches_read_codes_times_block_scale(kv, code_dt):
+    """e5m2 latent codes (+ bf16 k^R), and the whole row in e4m3 under one
+    block scale, decoded by torch's fp8 casts and stored as an fp32 cache."""
+    wl = _small(kv, q_len=2, seq=(3, 100, 200))
+    g = _gen(31)
+    rows = I.draw_cache_rows(wl, g, torch.tensor(wl.seq_lens))
+    ql = torch.randn(wl.B * 2, wl.n_h, wl.d_c, generator=g).double()
+    qr = torch.randn(wl.B * 2, wl.n_h, wl.d_r, generator=g).double()
+    cache = _paged(wl, rows, 10, wl.seq_lens)
+    fmt = _fmt(kv)
+    o8, l8 = O.decode(cache.pool, fmt, cache.block_table, cache.seq_lens, ql, qr,
+                      wl.scale, q_len=2, block_scales=cache.block_scales)
+    nb, W = cache.num_blocks, wl.d_c + wl.d_r
+    sc = cache.block_scales[:, None, None]
+    if kv == "fp8_e4m3_row":
+        full = cache.pool.contiguous().view(code_dt).to(torch.float32).view(nb, 64, W) * sc
+    else:
+        c = cache.pool[:, :64 * wl.d_c].contiguous().view(code_dt).to(torch.float32).view(nb, 64, wl.d_c) * sc
+        kr = cache.pool[:, 64 * wl.d_c:].contiguous().view(torch.bfloat16).to(torch.float32).view(nb, 64, wl.d_r)
+        full = torch.cat([c, kr], dim=2)
+    pool32 = full.contiguous().view(torch.uint8).view(nb, -1)
+    o32, l32 = O.decode(pool32, O.FMT_F32, cache.block_table, cache.seq_lens, ql, qr, wl.scale, q_len=2)
     np.testing.assert_allclose(o8, o32, rtol=1e-6, atol=1e-6)
     np.testing.assert_allclose(l8, l32, rtol=1e-6, atol=1e-6)
     assert np.all(np.isfinite(o8))
