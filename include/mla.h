@@ -52,7 +52,10 @@ typedef enum {
 typedef enum {
     MLA_DT_F32 = 0,
     MLA_DT_BF16 = 1,
-    MLA_DT_FP8_E4M3 = 2       /* OCP E4M3 ("fn": no infinities, S.1111.111 = NaN) */
+    MLA_DT_FP8_E4M3 = 2,      /* OCP E4M3 ("fn": no infinities, S.1111.111 = NaN) */
+    MLA_DT_F16 = 3,           /* IEEE binary16 (cache rows only) */
+    MLA_DT_FP8_E5M2 = 4,      /* OCP E5M2 latent codes (cache only; huny §6 "E4M3 or E5M2") */
+    MLA_DT_FP8_E4M3_ROW = 5   /* the whole [c | k^R] row as E4M3 codes (cache only) */
 } mla_dtype_t;
 
 /* Tokens per paged block.  The pages' decode kernel accepts only 64-token
@@ -66,11 +69,17 @@ typedef enum {
  * 64 token rows each:
  *   kv_dtype F32 / BF16: block = [64][d_c + d_r] rows of [c | k^R] in that type
  *                        (bf16 at d_c=512, d_r=64: 73,728 B per block);
+ *   kv_dtype F16:        as BF16 with IEEE fp16 rows (a kv-cache dtype of the
+ *                        vLLM MLA page, "FlashMLABackend").
  *   kv_dtype FP8_E4M3:   block = c codes [64][d_c] (e4m3) followed by k^R
  *                        [64][d_r] in bf16 (the rotary key keeps 16-bit
  *                        precision, huny §6 FP8 item; 40,960 B per block), and
  *                        block_scales[num_blocks] (fp32) holds the one
  *                        dequantisation scale of each block: c = code * scale.
+ *   kv_dtype FP8_E5M2:   as FP8_E4M3 with e5m2 latent codes (huny §6).
+ *   kv_dtype FP8_E4M3_ROW: block = [64][d_c + d_r] e4m3 codes of the whole
+ *                        row, one scale per block for both parts:
+ *                        [c | k^R] = code * scale (36,864 B per block).
  * Blocks are 256-byte aligned when base is (block bytes are multiples of 256
  * for the instantiated dims).  Rows past a sequence's length may hold
  * anything, including NaN: no result depends on them.

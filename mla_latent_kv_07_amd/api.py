@@ -15,7 +15,8 @@ import torch
 from . import _lib as L
 
 _DT = {torch.float32: L.DT_F32, torch.bfloat16: L.DT_BF16}
-_KV = {"f32": L.DT_F32, "bf16": L.DT_BF16, "fp8_e4m3": L.DT_FP8_E4M3}
+_KV = {"f32": L.DT_F32, "bf16": L.DT_BF16, "fp8_e4m3": L.DT_FP8_E4M3, "f16": L.DT_F16,
+       "fp8_e5m2": L.DT_FP8_E5M2, "fp8_e4m3_row": L.DT_FP8_E4M3_ROW}
 
 
 def _p(t):

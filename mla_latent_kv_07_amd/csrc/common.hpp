@@ -41,8 +41,9 @@ __host__ __device__ inline int64_t plan_flags_off(int32_t num_items, int32_t B) 
 }
 
 hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_decode_bf16_mfma(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_decode_fp8_mfma(const DecodeArgs &a, hipStream_t s);
+// MFMA decode of the DeepSeek-V2 shape (d_c 512, d_r 64, bf16 queries) for
+// every 16-bit and 8-bit cache format
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *lse_part,
                           const int32_t *split_off, const int32_t *seq_flags, int32_t B,
                           int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dt, float *lse,

@@ -1,5 +1,6 @@
 // Generic absorbed-MLA decode: any d_c <= 1024, d_r <= 256 (multiples of 4),
-// fp32 / bf16 / fp8-e4m3 cache, fp32 / bf16 queries.  One wave per query row,
+// fp32 / bf16 / fp16 / fp8 (e4m3 or e5m2 latent, or the whole row in e4m3)
+// cache, fp32 / bf16 queries.  One wave per query row,
 // one cached token at a time with a wavefront reduction for the 576-wide
 // (d_c + d_r) dot product.  This is the path for the small fp32 layer and any
 // shape the MFMA kernels are not instantiated for; the DeepSeek-V2 shape runs
@@ -26,22 +27,49 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
     return s ? -v : v;
 }
 
+// E5M2 code -> fp32: bias 15, 2 mantissa bits, exponent field 0 subnormal,
+// exponent 31 infinity (mantissa 0) or NaN.
+__device__ __forceinline__ float e5m2_to_f32(uint32_t code) {
+    const uint32_t s = (code >> 7) & 1u, e = (code >> 2) & 31u, m = code & 3u;
+    float v;
+    if (e == 0)
+        v = (float)m * 1.52587890625e-05f;  // m * 2^-16
+    else if (e == 31)
+        v = __uint_as_float(m ? 0x7fc00000u : 0x7f800000u);
+    else
+        v = __uint_as_float(((e + 112u) << 23) | (m << 21));  // (1 + m/4) * 2^(e-15)
+    return s ? -v : v;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
 template <int KV>
 __device__ __forceinline__ float load_c(const uint8_t *blk, int slot, int f, int d_c, int d_r) {
     if constexpr (KV == MLA_DT_F32)
         return ((const float *)blk)[(int64_t)slot * (d_c + d_r) + f];
     else if constexpr (KV == MLA_DT_BF16)
         return bf16_to_f32(((const uint16_t *)blk)[(int64_t)slot * (d_c + d_r) + f]);
+    else if constexpr (KV == MLA_DT_F16)
+        return f16_to_f32(((const uint16_t *)blk)[(int64_t)slot * (d_c + d_r) + f]);
+    else if constexpr (KV == MLA_DT_FP8_E4M3_ROW)
+        return e4m3_to_f32(blk[(int64_t)slot * (d_c + d_r) + f]);
+    else if constexpr (KV == MLA_DT_FP8_E5M2)
+        return e5m2_to_f32(blk[(int64_t)slot * d_c + f]);
     else
         return e4m3_to_f32(blk[(int64_t)slot * d_c + f]);
 }
 
+// rotary key value (for the whole-row e4m3 format: the code, before the block scale)
 template <int KV>
 __device__ __forceinline__ float load_r(const uint8_t *blk, int slot, int f, int d_c, int d_r) {
     if constexpr (KV == MLA_DT_F32)
         return ((const float *)blk)[(int64_t)slot * (d_c + d_r) + d_c + f];
     else if constexpr (KV == MLA_DT_BF16)
         return bf16_to_f32(((const uint16_t *)blk)[(int64_t)slot * (d_c + d_r) + d_c + f]);
+    else if constexpr (KV == MLA_DT_F16)
+        return f16_to_f32(((const uint16_t *)blk)[(int64_t)slot * (d_c + d_r) + d_c + f]);
+    else if constexpr (KV == MLA_DT_FP8_E4M3_ROW)
+        return e4m3_to_f32(blk[(int64_t)slot * (d_c + d_r) + d_c + f]);
     else
         return bf16_to_f32(((const uint16_t *)(blk + (int64_t)kBlock * d_c))[(int64_t)slot * d_r + f]);
 }
@@ -95,7 +123,9 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
             blk = blk < 0 ? 0 : (blk >= a.num_pool_blocks ? a.num_pool_blocks - 1 : blk);
             const int sl = p % kBlock;
             const uint8_t *base = pool + blk * a.block_bytes;
-            const float bs = KV == MLA_DT_FP8_E4M3 ? a.block_scales[blk] : 1.0f;
+            constexpr bool SCALED = KV == MLA_DT_FP8_E4M3 || KV == MLA_DT_FP8_E5M2 || KV == MLA_DT_FP8_E4M3_ROW;
+            const float bs = SCALED ? a.block_scales[blk] : 1.0f;
+            const float rs = KV == MLA_DT_FP8_E4M3_ROW ? bs : 1.0f;   // scale of the rotary values
             float c[kMaxC];
             float part = 0.f;
 #pragma unroll
@@ -107,7 +137,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < kMaxR; ++j) {
                 const int f = lane + 64 * j;
-                if (f < a.d_r) part += qrr[j] * load_r<KV>(base, sl, f, a.d_c, a.d_r);
+                if (f < a.d_r) part += qrr[j] * (load_r<KV>(base, sl, f, a.d_c, a.d_r) * rs);
             }
             const float s = wave_sum(part) * a.scale_log2;
             const float m_new = fmaxf(m, s);
@@ -170,6 +200,9 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
     case MLA_DT_F32: return launch_kv<MLA_DT_F32>(a, s);
     case MLA_DT_BF16: return launch_kv<MLA_DT_BF16>(a, s);
     case MLA_DT_FP8_E4M3: return launch_kv<MLA_DT_FP8_E4M3>(a, s);
+    case MLA_DT_F16: return launch_kv<MLA_DT_F16>(a, s);
+    case MLA_DT_FP8_E5M2: return launch_kv<MLA_DT_FP8_E5M2>(a, s);
+    case MLA_DT_FP8_E4M3_ROW: return launch_kv<MLA_DT_FP8_E4M3_ROW>(a, s);
     }
     return hipErrorInvalidValue;
 }

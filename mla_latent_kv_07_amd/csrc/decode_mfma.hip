@@ -30,10 +30,25 @@
 #include "common.hpp"
 
 namespace mla {
+
+// Cache formats of the MFMA decode (template tags): 16-bit rows (bf16 or
+// fp16), or 8-bit codes with one scale per block (e4m3 / e5m2 latent with bf16
+// rotary keys, or the whole row in e4m3).
+namespace kv {
+struct Bf16 { static constexpr bool fp8 = false, half = false, row = false, e5m2 = false; };
+struct F16 { static constexpr bool fp8 = false, half = true, row = false, e5m2 = false; };
+struct E4m3 { static constexpr bool fp8 = true, half = false, row = false, e5m2 = false; };
+struct E5m2 { static constexpr bool fp8 = true, half = false, row = false, e5m2 = true; };
+struct E4m3Row { static constexpr bool fp8 = true, half = false, row = true, e5m2 = false; };
+}  // namespace kv
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -123,6 +138,17 @@ __device__ __forceinline__ void issue_stage_fp8(const uint8_t *codes0, const uin
     dma16(staging_lds + FP8_LAT + wave * 1024, l16, rope0 + wave * 1024);
 }
 
+// whole-row e4m3 cache: one stage is 32 contiguous rows of 576 codes (18 KiB)
+// of the block's [64][576]; wave w copies KiB 4w..4w+3 and KiB 16 + (w & 1)
+// (waves 2 and 3 repeat the copies of waves 0 and 1: same bytes, same place),
+// so every wave issues as many copies as for the split layout.
+__device__ __forceinline__ void issue_stage_row(const uint8_t *rows0, uint32_t staging_lds, int wave, uint32_t l16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma16(staging_lds + (4 * wave + k) * 1024, l16, rows0 + (4 * wave + k) * 1024);
+    dma16(staging_lds + (16 + (wave & 1)) * 1024, l16, rows0 + (16 + (wave & 1)) * 1024);
+}
+static_assert(HALF * (DC + DR) <= 18 * 1024 && 18 * 1024 <= FP8_STAGE, "row stage copy");
+
 constexpr int DMA_PER_STAGE8 = 5;
 
 // Loads of wave-uniform values (plan, block table, lengths) through the
@@ -141,16 +167,22 @@ __device__ __forceinline__ int opaque(int v) {
 }
 
 
-// FP8: the cache stores e4m3 latents with one fp32 scale per 64-token block
-// and bf16 rotary keys.  Codes are converted exactly to bf16 (the scale is a
-// per-stage scalar): the score chain runs the 4 rotary k-steps first, scales
-// that partial sum by 1/sigma, then adds the latent k-steps, so that
-// sigma * acc = sigma (q~ . c8) + q^R . k^R; the probabilities are produced
-// already multiplied by sigma (value MFMAs then sum (sigma p) c8 = p c) and
-// the denominator takes psum / sigma.  (fp8 cache: huny.dev "DeepSeek MLA
-// 해부" §6 FP8 item; vLLM MLA page, "FP8 MLA 지원".)
-template <bool FP8>
+// FP8: the cache stores e4m3 (or e5m2) latents with one fp32 scale per
+// 64-token block and bf16 rotary keys.  Codes are converted exactly to bf16
+// (the scale is a per-stage scalar): the score chain runs the 4 rotary
+// k-steps first, scales that partial sum by 1/sigma, then adds the latent
+// k-steps, so that sigma * acc = sigma (q~ . c8) + q^R . k^R; the
+// probabilities are produced already multiplied by sigma (value MFMAs then
+// sum (sigma p) c8 = p c) and the denominator takes psum / sigma.  With the
+// whole row in e4m3 the rotary codes carry the same scale, so the chain has
+// no 1/sigma step.  (fp8 cache: huny.dev "DeepSeek MLA 해부" §6 FP8 item;
+// vLLM MLA page, "FP8 MLA 지원".)
+// F16: rows of IEEE fp16 run the same pipeline on fp16 MFMAs; the bf16
+// queries are rounded to fp16 once in the prologue (exact for magnitudes in
+// [2^-14, 65504]; larger ones saturate) and the probabilities are fp16.
+template <typename KV>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
+    constexpr bool FP8 = KV::fp8, ROW = KV::row, H16 = KV::half;
     __shared__ __attribute__((aligned(1024))) uint8_t smem_[lds_bytes<FP8>()];
     lds_u8 *smem = (lds_u8 *)smem_;
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
@@ -209,12 +241,24 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     const uint32_t l16 = lane << 4;
     const uint32_t rot_off = FP8 ? 0u : (uint32_t)((wave * 8 + (lane & 7)) * ROW_BYTES + CB + 16 * (lane >> 3));
     auto issue = [&](int st) {
-        if constexpr (FP8) {
+        if constexpr (ROW) {
+            const uint8_t *blk = pool + blk_id(st) * a.block_bytes;
+            issue_stage_row(blk + (st & 1) * HALF * (DC + DR), smem_addr + staging_off(st), wave,
+                            (uint32_t)opaque(lane) << 4);
+        } else if constexpr (FP8) {
             const uint8_t *blk = pool + blk_id(st) * a.block_bytes;
             issue_stage_fp8(blk + (st & 1) * FP8_LAT, blk + kBlock * DC + (st & 1) * HALF * RB,
                             smem_addr + staging_off(st), wave, (uint32_t)opaque(lane) << 4);
         } else {
-            issue_stage(stage_src(st), smem_addr + stage_off(st), wave, l16, rot_off);
+            if constexpr (H16) {
+                // the fp16 variant's register allocation spills these two
+                // offsets; recomputed where they are used instead
+                const int ol = opaque(lane);
+                issue_stage(stage_src(st), smem_addr + stage_off(st), wave, (uint32_t)ol << 4,
+                            (uint32_t)((wave * 8 + (ol & 7)) * ROW_BYTES + CB + 16 * (ol >> 3)));
+            } else {
+                issue_stage(stage_src(st), smem_addr + stage_off(st), wave, l16, rot_off);
+            }
         }
     };
 
@@ -276,6 +320,16 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         copy_half(1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // second half, stages 0 and 1
         if (ln >= 16) read_half();
+        if constexpr (H16) {
+            // fp16 cache: the queries as fp16 (saturating)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = fminf(fmaxf((float)qf[ks][e], -65504.f), 65504.f);
+                    qf[ks][e] = __builtin_bit_cast(__bf16, (_Float16)f);
+                }
+        }
     }
     // every wave holds its queries (the query regions are free) and every
     // wave's copies of stages 0 and 1 are visible
@@ -329,12 +383,21 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     auto score_mfma = [&](f32x16 &acc, const bf16x8 &kf, int i) {
         // the first MFMA writes the accumulator while reading its operands:
         // early clobber keeps them apart
-        if (i == 0)
-            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                         : "=&v"(acc) : "v"(kf), "v"(qf[kstep(0)]));
-        else
-            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                         : "+v"(acc) : "v"(kf), "v"(qf[kstep(i)]));
+        if constexpr (H16) {
+            if (i == 0)
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0"
+                             : "=&v"(acc) : "v"(kf), "v"(qf[kstep(0)]));
+            else
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                             : "+v"(acc) : "v"(kf), "v"(qf[kstep(i)]));
+        } else {
+            if (i == 0)
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                             : "=&v"(acc) : "v"(kf), "v"(qf[kstep(0)]));
+            else
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+v"(acc) : "v"(kf), "v"(qf[kstep(i)]));
+        }
     };
     // fp8: after the rotary k-steps, divide the partial sum by the block scale
     auto rope_to_latent_scale = [&](f32x16 &acc, float inv_sigma) {
@@ -360,22 +423,37 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     // fp8: staging buffer of stage st -> its bf16 stage buffer, by all 256
     // threads: latent codes converted exactly (scale 1), rotary rows copied,
     // rows past the sequence end written as zeros.
+    // codes 0-1 (lo) or 2-3 (hi) of a packed word -> two bf16 (exact; scale 1)
+    auto cvt_lo = [](uint32_t w) {
+        if constexpr (KV::e5m2)
+            return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false));
+        else
+            return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    };
+    auto cvt_hi = [](uint32_t w) {
+        if constexpr (KV::e5m2)
+            return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true));
+        else
+            return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    };
     auto convert = [&](int st) {
         const int valid = S - (p_first + st * HALF);
         const lds_u8 *src = smem + staging_off(st);
         lds_u8 *dst = smem + stage_off(st);
         const int tid = opaque(threadIdx.x);
+        // latent codes of token t: [t][512] (split layout) or the first 512 of [t][576]
+        constexpr int CODE_PITCH = ROW ? DC + DR : DC;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int i = tid + 256 * j;   // 16-byte chunk of the 16 KiB latent part
+            const int i = tid + 256 * j;   // 16-byte chunk of the 16 KiB of latent codes
             const int t = i >> 5, c16 = i & 31;
-            const uint4 v = *(const uint4 *)(src + i * 16);
+            const uint4 v = *(const uint4 *)(src + (ROW ? t * CODE_PITCH + c16 * 16 : i * 16));
             uint32_t o[8];
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false));
-                o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true));
+                o[2 * e] = cvt_lo(w[e]);
+                o[2 * e + 1] = cvt_hi(w[e]);
             }
             const bool live = t < valid;
             uint4 *d = (uint4 *)(dst + t * LPITCH + c16 * 32);
@@ -384,7 +462,14 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         }
         {
             const int t = tid >> 3, c = tid & 7;
-            const uint4 v = *(const uint4 *)(src + FP8_LAT + t * RB + c * 16);
+            uint4 v;
+            if constexpr (ROW) {
+                // rotary codes 8c..8c+7 of token t
+                const uint2 w = *(const uint2 *)(src + t * CODE_PITCH + DC + c * 8);
+                v = make_uint4(cvt_lo(w.x), cvt_hi(w.x), cvt_lo(w.y), cvt_hi(w.y));
+            } else {
+                v = *(const uint4 *)(src + FP8_LAT + t * RB + c * 16);
+            }
             *(uint4 *)(dst + LAT_BYTES + (t >> 3) * 1024 + c * 128 + (t & 7) * 16) =
                 t < valid ? v : make_uint4(0, 0, 0, 0);
         }
@@ -414,7 +499,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         for (int i = 0; i < KS; ++i) {
             score_mfma(sA, kb[i % PFK], i);
             if (i + PFK < KS) kb[i % PFK] = kld(kbs, rbs, kstep(i + PFK));
-            if (FP8 && i == DR / 16 - 1) rope_to_latent_scale(sA, 1.0f / sig_cur);
+            if (FP8 && !ROW && i == DR / 16 - 1) rope_to_latent_scale(sA, 1.0f / sig_cur);
         }
         asm volatile("s_nop 15" : "+v"(sA));
     }
@@ -494,8 +579,15 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
                 if (r >= 0 && r < 16) cur[r] = __builtin_fmaf(cur[r], s_l2, -m_off);
             } else {
                 const int r = 2 * (k - 28);   // entries r, r+1 -> one packed pair of P
-                pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3)] = (__bf16)cur[r];
-                pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3) + 1] = (__bf16)cur[r + 1];
+                if constexpr (H16) {
+                    // one packed fp32 -> fp16 conversion per pair
+                    const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{cur[r], cur[r + 1]}, f16x2));
+                    pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3)] = __builtin_bit_cast(__bf16, (uint16_t)u);
+                    pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3) + 1] = __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
+                } else {
+                    pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3)] = (__bf16)cur[r];
+                    pcur[(r >> 2) & 1][((r >> 3) << 2) | (r & 3) + 1] = (__bf16)cur[r + 1];
+                }
             }
         };
 
@@ -504,7 +596,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             for (int i = 0; i < KS; ++i) {
                 score_mfma(nxt, kb[i % PFK], i);
                 if (i + PFK < KS) kb[i % PFK] = kld(kbs, rbs, kstep(i + PFK));
-                if (FP8 && i == DR / 16 - 1) rope_to_latent_scale(nxt, 1.0f / sig_next);
+                if (FP8 && !ROW && i == DR / 16 - 1) rope_to_latent_scale(nxt, 1.0f / sig_next);
                 softmax_slice(i);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -536,8 +628,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);   // the prefetch reads first
 #pragma unroll
         for (int i = 0; i < 2 * MBLOCKS; ++i) {
-            oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % PF], pcur[i / MBLOCKS],
-                                                                        oacc[i % MBLOCKS], 0, 0, 0);
+            if constexpr (H16)
+                oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(f16x8, vb[i % PF]), __builtin_bit_cast(f16x8, pcur[i / MBLOCKS]),
+                    oacc[i % MBLOCKS], 0, 0, 0);
+            else
+                oacc[i % MBLOCKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % PF], pcur[i / MBLOCKS],
+                                                                            oacc[i % MBLOCKS], 0, 0, 0);
             if (i + PF < 2 * MBLOCKS) vb[i % PF] = vld(vbs, i + PF);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i + PF < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -607,18 +704,20 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16_mfma(const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
     // a multiple of 8 workgroups, one per (item, row chunk) plus padding
     const int units = a.num_items * a.row_chunks;
     dim3 grid((unsigned)((units + 7) / 8) * 8);
-    hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_decode_fp8_mfma(const DecodeArgs &a, hipStream_t s) {
-    const int units = a.num_items * a.row_chunks;
-    dim3 grid((unsigned)((units + 7) / 8) * 8);
-    hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, dim3(256), 0, s, a);
+    switch (a.kv_dtype) {
+    case MLA_DT_BF16: hipLaunchKernelGGL(decode_mfma_kernel<kv::Bf16>, grid, dim3(256), 0, s, a); break;
+    case MLA_DT_F16: hipLaunchKernelGGL(decode_mfma_kernel<kv::F16>, grid, dim3(256), 0, s, a); break;
+    case MLA_DT_FP8_E4M3: hipLaunchKernelGGL(decode_mfma_kernel<kv::E4m3>, grid, dim3(256), 0, s, a); break;
+    case MLA_DT_FP8_E5M2: hipLaunchKernelGGL(decode_mfma_kernel<kv::E5m2>, grid, dim3(256), 0, s, a); break;
+    case MLA_DT_FP8_E4M3_ROW:
+        hipLaunchKernelGGL(decode_mfma_kernel<kv::E4m3Row>, grid, dim3(256), 0, s, a);
+        break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

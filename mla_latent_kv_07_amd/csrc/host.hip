@@ -40,6 +40,9 @@ int elem_bytes(mla_dtype_t dt) {
     case MLA_DT_F32: return 4;
     case MLA_DT_BF16: return 2;
     case MLA_DT_FP8_E4M3: return 1;
+    case MLA_DT_F16: return 2;
+    case MLA_DT_FP8_E5M2: return 1;
+    case MLA_DT_FP8_E4M3_ROW: return 1;
     }
     return 0;
 }
@@ -48,13 +51,22 @@ int64_t block_bytes_of(mla_dtype_t kv, int32_t d_c, int32_t d_r) {
     switch (kv) {
     case MLA_DT_F32: return (int64_t)kBlock * (d_c + d_r) * 4;
     case MLA_DT_BF16: return (int64_t)kBlock * (d_c + d_r) * 2;
-    case MLA_DT_FP8_E4M3: return (int64_t)kBlock * d_c + (int64_t)kBlock * d_r * 2;
+    case MLA_DT_FP8_E4M3:
+    case MLA_DT_FP8_E5M2: return (int64_t)kBlock * d_c + (int64_t)kBlock * d_r * 2;
+    case MLA_DT_F16: return (int64_t)kBlock * (d_c + d_r) * 2;
+    case MLA_DT_FP8_E4M3_ROW: return (int64_t)kBlock * (d_c + d_r);
     }
     return -1;
 }
 
+bool is_kv_dtype(mla_dtype_t kv) { return kv >= MLA_DT_F32 && kv <= MLA_DT_FP8_E4M3_ROW; }
+
+bool is_fp8_kv(mla_dtype_t kv) {
+    return kv == MLA_DT_FP8_E4M3 || kv == MLA_DT_FP8_E5M2 || kv == MLA_DT_FP8_E4M3_ROW;
+}
+
 bool is_fast_shape(mla_dtype_t kv, int32_t d_c, int32_t d_r) {
-    return (kv == MLA_DT_BF16 || kv == MLA_DT_FP8_E4M3) && d_c == 512 && d_r == 64;
+    return kv != MLA_DT_F32 && is_kv_dtype(kv) && d_c == 512 && d_r == 64;
 }
 
 mla_status_t check_cache(const mla_cache_desc_t *c) {
@@ -63,12 +75,11 @@ mla_status_t check_cache(const mla_cache_desc_t *c) {
     if (c->num_blocks < 1) return fail(MLA_ERR_INVALID_ARG, "cache is empty (num_blocks=%lld)", (long long)c->num_blocks);
     if (c->block_size != kBlock)
         return fail(MLA_ERR_UNSUPPORTED, "block_size %d unsupported (only %d)", c->block_size, kBlock);
-    if (c->kv_dtype != MLA_DT_F32 && c->kv_dtype != MLA_DT_BF16 && c->kv_dtype != MLA_DT_FP8_E4M3)
-        return fail(MLA_ERR_UNSUPPORTED, "kv dtype %d unsupported", (int)c->kv_dtype);
+    if (!is_kv_dtype(c->kv_dtype)) return fail(MLA_ERR_UNSUPPORTED, "kv dtype %d unsupported", (int)c->kv_dtype);
     if (c->d_c < 4 || c->d_c > 1024 || c->d_c % 4 || c->d_r < 0 || c->d_r > 256 || c->d_r % 4)
         return fail(MLA_ERR_UNSUPPORTED, "cache dims d_c=%d d_r=%d unsupported (d_c in [4,1024], d_r in [0,256], multiples of 4)",
                     c->d_c, c->d_r);
-    if (c->kv_dtype == MLA_DT_FP8_E4M3 && !c->block_scales)
+    if (is_fp8_kv(c->kv_dtype) && !c->block_scales)
         return fail(MLA_ERR_INVALID_ARG, "fp8 cache needs block_scales");
     if (!aligned(c->base, 16)) return fail(MLA_ERR_ALIGN, "cache base not 16-byte aligned");
     return MLA_OK;
@@ -97,8 +108,7 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     if (B < 1 || q_len < 1 || n_h < 1 || d_c < 1 || d_r < 0)
         return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d q_len=%d n_h=%d d_c=%d d_r=%d", B, q_len, n_h, d_c, d_r);
     if (num_cus < 1) return fail(MLA_ERR_INVALID_ARG, "num_cus=%d", num_cus);
-    if (kv_dtype != MLA_DT_F32 && kv_dtype != MLA_DT_BF16 && kv_dtype != MLA_DT_FP8_E4M3)
-        return fail(MLA_ERR_UNSUPPORTED, "kv dtype %d unsupported", (int)kv_dtype);
+    if (!is_kv_dtype(kv_dtype)) return fail(MLA_ERR_UNSUPPORTED, "kv dtype %d unsupported", (int)kv_dtype);
     int64_t rows = (int64_t)q_len * n_h;
     if (rows > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "q_len*n_h too large");
     int32_t row_chunks = (int32_t)((rows + kRowsPerChunk - 1) / kRowsPerChunk);
@@ -244,8 +254,7 @@ mla_status_t prepare_decode(const void *q_lat, const void *q_rope, mla_dtype_t q
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     if (a.num_items == 0) return hipSuccess;
-    if (is_fast_shape(a.kv_dtype, a.d_c, a.d_r) && a.q_dtype == MLA_DT_BF16)
-        return a.kv_dtype == MLA_DT_BF16 ? launch_decode_bf16_mfma(a, s) : launch_decode_fp8_mfma(a, s);
+    if (is_fast_shape(a.kv_dtype, a.d_c, a.d_r) && a.q_dtype == MLA_DT_BF16) return launch_decode_mfma(a, s);
     return launch_decode_generic(a, s);
 }
 
@@ -473,7 +482,7 @@ mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *bloc
         return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d max_tokens=%d bt_stride=%d", B, max_tokens, bt_stride);
     if (!aligned(out, 16)) return fail(MLA_ERR_ALIGN, "out not 16-byte aligned");
     int eb = elem_bytes(cache->kv_dtype);
-    bool split = cache->kv_dtype == MLA_DT_FP8_E4M3;
+    bool split = cache->kv_dtype == MLA_DT_FP8_E4M3 || cache->kv_dtype == MLA_DT_FP8_E5M2;
     int32_t c_bytes = split ? cache->d_c : (cache->d_c + cache->d_r) * eb;
     int32_t r_bytes = split ? cache->d_r * 2 : 0;
     return hip_status(launch_gather((const uint8_t *)cache->base,

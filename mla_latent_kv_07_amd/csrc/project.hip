@@ -74,6 +74,30 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
     return sign | (uint8_t)((ef << 3) | ((int)q - 8));
 }
 
+// OCP E5M2 from fp32: round to nearest even, |x| >= 57344 saturates to
+// +-57344 (as the e4m3 encoder saturates), NaN -> 0x7F, sign as x < 0.
+__device__ __forceinline__ uint8_t f32_to_e5m2(float x) {
+    if (x != x) return 0x7F;
+    const uint8_t sign = x < 0.f ? 0x80 : 0x00;
+    const float a = fabsf(x);
+    if (a >= 57344.f) return sign | 0x7B;
+    if (a < 6.103515625e-05f)   // below 2^-14: subnormal steps of 2^-16 (4 steps reach code 4)
+        return sign | (uint8_t)__builtin_rintf(a * 65536.f);
+    int e;
+    const float m = frexpf(a, &e);            // a = m 2^e, m in [0.5, 1)
+    float q = __builtin_rintf(m * 8.f);       // 4..8: 1.mm in quarters
+    if (q == 8.f) { q = 4.f; ++e; }
+    const int ef = e - 1 + 15;                // biased exponent, 1..30
+    return sign | (uint8_t)((ef << 2) | ((int)q - 4));
+}
+
+__device__ __forceinline__ float e5m2_to_f32(uint8_t c) {
+    const int e = (c >> 2) & 31, m = c & 3;
+    if (e == 31) return m ? __builtin_nanf("") : ((c & 0x80) ? -__builtin_inff() : __builtin_inff());
+    const float v = e == 0 ? (float)m * 1.52587890625e-05f : ldexpf(1.f + (float)m * 0.25f, e - 15);
+    return (c & 0x80) ? -v : v;
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
     if ((c & 0x7F) == 0x7F) return __builtin_nanf("");
     const int e = (c >> 3) & 15, m = c & 7;
@@ -109,12 +133,19 @@ struct AppendArgs {
     int32_t q_len, d_c, d_r;
 };
 
-// fp8 caches (e4m3 latent + bf16 k^R): one workgroup per sequence, its q_len
-// tokens in order (positions outside the block table, p < 0 or
-// p >= 64 bt_stride, are skipped).  The tokens that land in one block are
-// handled together: their amax sets or raises the block scale, earlier slots
-// are re-encoded when it grows, then the codes are written.
+// fp8 caches (e4m3 or e5m2 latent + bf16 k^R, or the whole row in e4m3): one
+// workgroup per sequence, its q_len tokens in order (positions outside the
+// block table, p < 0 or p >= 64 bt_stride, are skipped).  The tokens that land
+// in one block are handled together: the amax of their coded values sets or
+// raises the block scale, earlier slots are re-encoded when it grows, then
+// the codes are written.
+template <int CODE>   // 0 e4m3 latent, 1 e5m2 latent, 2 e4m3 whole row
 __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab rt) {
+    constexpr bool ROWC = CODE == 2;
+    constexpr float TOP = CODE == 1 ? 57344.f : 448.f;
+    auto enc = [](float v) { return CODE == 1 ? f32_to_e5m2(v) : f32_to_e4m3(v); };
+    auto dec = [](uint8_t c) { return CODE == 1 ? e5m2_to_f32(c) : e4m3_to_f32(c); };
+    const int W = ROWC ? a.d_c + a.d_r : a.d_c;   // code bytes per token
     __shared__ float red[4];
     __shared__ float sh[3];
     const int b = blockIdx.x, tid = threadIdx.x;
@@ -148,8 +179,16 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab r
         const int s0 = p % kBlock;
         // amax of the new latents in this block
         float m = 0.f;
-        for (int k = i; k < i_end; ++k)
+        for (int k = i; k < i_end; ++k) {
             for (int f = tid; f < a.d_c; f += 256) m = fmaxf(m, fabsf(xval(b * a.q_len + k, f)));
+            if constexpr (ROWC) {
+                for (int j = tid; j < rt.half; j += 256) {
+                    float y0, y1;
+                    rot(b * a.q_len + k, p0 + k, j, y0, y1);
+                    m = fmaxf(m, fmaxf(fabsf(y0), fabsf(y1)));
+                }
+            }
+        }
         for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
         if ((tid & 63) == 0) red[tid >> 6] = m;
         __syncthreads();
@@ -159,9 +198,9 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab r
             float sc;
             bool grow = false;
             if (s0 == 0) {
-                sc = amax > 0.f ? amax / 448.f : 1.f;
+                sc = amax > 0.f ? amax / TOP : 1.f;
             } else {
-                sc = fmaxf(old, amax / 448.f);
+                sc = fmaxf(old, amax / TOP);
                 grow = sc > old;
             }
             sh[0] = sc;
@@ -173,18 +212,22 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab r
         const float sc = sh[0], ratio = sh[1];
         if (sh[2] != 0.f) {
             // re-encode the slots before the first new one at the larger scale
-            for (int idx = tid; idx < s0 * a.d_c; idx += 256)
-                base[idx] = f32_to_e4m3(e4m3_to_f32(base[idx]) * ratio);
+            for (int idx = tid; idx < s0 * W; idx += 256) base[idx] = enc(dec(base[idx]) * ratio);
         }
         for (int k = i; k < i_end; ++k) {
             const int t = b * a.q_len + k, pk = p0 + k, slot = pk % kBlock;
-            for (int f = tid; f < a.d_c; f += 256) base[slot * a.d_c + f] = f32_to_e4m3(xval(t, f) / sc);
-            uint16_t *kr = (uint16_t *)(base + (int64_t)kBlock * a.d_c + (int64_t)slot * a.d_r * 2);
+            for (int f = tid; f < a.d_c; f += 256) base[slot * W + f] = enc(xval(t, f) / sc);
             for (int j = tid; j < rt.half; j += 256) {
                 float y0, y1;
                 rot(t, pk, j, y0, y1);
-                kr[2 * j] = f32_to_bf16(y0);
-                kr[2 * j + 1] = f32_to_bf16(y1);
+                if constexpr (ROWC) {
+                    base[slot * W + a.d_c + 2 * j] = enc(y0 / sc);
+                    base[slot * W + a.d_c + 2 * j + 1] = enc(y1 / sc);
+                } else {
+                    uint16_t *kr = (uint16_t *)(base + (int64_t)kBlock * a.d_c + (int64_t)slot * a.d_r * 2);
+                    kr[2 * j] = f32_to_bf16(y0);
+                    kr[2 * j + 1] = f32_to_bf16(y1);
+                }
             }
         }
         __syncthreads();   // red / sh are reused by the next block
@@ -194,7 +237,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab r
 
 // f32 / bf16 caches: one thread per (token, pair of row values); the rotary
 // pairs turn by p theta_j (fp64 angle), then every value is rounded once.
-template <int FMT>   // 0 f32, 1 bf16
+template <int FMT>   // 0 f32, 1 bf16, 2 f16
 __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab rt) {
     const int N = a.d_c + a.d_r, P2 = N / 2;
     const int64_t idx = blockIdx.x * 256ll + threadIdx.x;
@@ -219,8 +262,11 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab 
     uint8_t *row = a.pool + blk * a.block_bytes + (int64_t)(p % kBlock) * N * (FMT == 0 ? 4 : 2);
     if constexpr (FMT == 0) {
         *(float2 *)((float *)row + 2 * k) = make_float2(y0, y1);
-    } else {
+    } else if constexpr (FMT == 1) {
         *(uint32_t *)((uint16_t *)row + 2 * k) = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+    } else {
+        *(uint32_t *)((uint16_t *)row + 2 * k) = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y0) |
+                                                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y1) << 16);
     }
 }
 
@@ -337,8 +383,14 @@ hipError_t launch_cache_append(const void *h, const void *w_kv, mla_dtype_t dt, 
         hipLaunchKernelGGL(append_rows_kernel<0>, dim3(rows_grid), dim3(256), 0, s, a, rt);
     else if (kv == MLA_DT_BF16)
         hipLaunchKernelGGL(append_rows_kernel<1>, dim3(rows_grid), dim3(256), 0, s, a, rt);
+    else if (kv == MLA_DT_F16)
+        hipLaunchKernelGGL(append_rows_kernel<2>, dim3(rows_grid), dim3(256), 0, s, a, rt);
+    else if (kv == MLA_DT_FP8_E4M3)
+        hipLaunchKernelGGL(append_fp8_kernel<0>, dim3(B), dim3(256), 0, s, a, rt);
+    else if (kv == MLA_DT_FP8_E5M2)
+        hipLaunchKernelGGL(append_fp8_kernel<1>, dim3(B), dim3(256), 0, s, a, rt);
     else
-        hipLaunchKernelGGL(append_fp8_kernel, dim3(B), dim3(256), 0, s, a, rt);
+        hipLaunchKernelGGL(append_fp8_kernel<2>, dim3(B), dim3(256), 0, s, a, rt);
     return hipGetLastError();
 }
 

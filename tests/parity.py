@@ -13,12 +13,15 @@ import oracle as O
 from mla_latent_kv_07_amd import api
 from mla_latent_kv_07_amd import inputs as I
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8_e4m3": 6e-2}
+# fp16 rows take the bf16 bound (16-bit cache, fp32 accumulation); every fp8
+# format takes the fp8 bound
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8_e4m3": 6e-2, "f16": 2e-2, "fp8_e5m2": 6e-2, "fp8_e4m3_row": 6e-2}
 # lse is a log of a sum of exponentials of fp32-accumulated scores; its
 # absolute error follows the score error: fp32 ~1e-6, bf16 inputs with fp32
 # accumulation ~1e-5, fp8 (quantised query / weights) ~ the logit noise.
-LSE_TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3": 6e-2}
-FMT = {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "fp8_e4m3": O.FMT_FP8_E4M3}
+LSE_TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3": 6e-2, "f16": 2e-3, "fp8_e5m2": 6e-2, "fp8_e4m3_row": 6e-2}
+FMT = {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "fp8_e4m3": O.FMT_FP8_E4M3, "f16": O.FMT_F16,
+       "fp8_e5m2": O.FMT_FP8_E5M2, "fp8_e4m3_row": O.FMT_FP8_E4M3_ROW}
 DEV = "cuda:0"
 
 

@@ -19,7 +19,7 @@ def small(kv="bf16", seq=(1, 100, 333), q_len=1, n_h=128, d_c=512, d_r=64, seed=
         q_len=q_len, n_h=n_h, d_c=d_c, d_r=d_r, seq_lens=tuple(seq), heavy_frac=heavy))
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "fp8_e4m3", "f16", "fp8_e5m2", "fp8_e4m3_row"])
 def test_gather_bit_exact(kv):
     d = small(kv, seq=(3, 64, 129, 0), d_c=512 if kv != "f32" else 64, d_r=64 if kv != "f32" else 16, n_h=8)
     cache, bt, sl, _, _ = to_device(d)
@@ -149,3 +149,25 @@ def test_decode_measured_batch_full_size_sampled():
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(32 * 128, size=96, replace=False))
     compare_decode(d, o, lse, rows=rows)
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e5m2", "fp8_e4m3_row"])
+def test_decode_cache_format_variants_mfma(kv):
+    """fp16 rows (fp16 MFMAs), e5m2 latent codes, and the whole row in e4m3
+    (one block scale for c and k^R) on the MFMA kernel: ragged lengths, NaN
+    tails, several splits and the combine, then the causal query pair."""
+    d = small(kv, seq=(1, 700, 1500, 64, 0, 129), seed=31, heavy=0.02)
+    o, lse, dec = run_decode(d, cus=8)
+    assert dec.info.max_splits > 1
+    compare_decode(d, o, lse)
+    d = small(kv, seq=(2, 3, 64, 65, 500), q_len=2, seed=32)
+    o, lse, _ = run_decode(d, cus=16)
+    compare_decode(d, o, lse)
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e5m2", "fp8_e4m3_row"])
+def test_decode_cache_format_variants_generic(kv):
+    """The same formats at a shape the MFMA kernel does not take (generic kernel)."""
+    d = small(kv, seq=(1, 70, 200), n_h=8, d_c=64, d_r=16, seed=33)
+    o, lse, _ = run_decode(d, cus=4)
+    compare_decode(d, o, lse)

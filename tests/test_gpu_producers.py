@@ -17,7 +17,8 @@ from parity import DEV, TOL, row_rel_err, say
 pytestmark = pytest.mark.gpu
 
 BLK = O.BLOCK
-KV = {O.FMT_F32: "f32", O.FMT_BF16: "bf16", O.FMT_FP8_E4M3: "fp8_e4m3"}
+KV = {O.FMT_F32: "f32", O.FMT_BF16: "bf16", O.FMT_FP8_E4M3: "fp8_e4m3", O.FMT_F16: "f16",
+      O.FMT_FP8_E5M2: "fp8_e5m2", O.FMT_FP8_E4M3_ROW: "fp8_e4m3_row"}
 
 
 def _bf16(x: np.ndarray) -> torch.Tensor:
@@ -55,7 +56,7 @@ def _run_appends(fmt, B, calls, d_c, d_r, d_model, seed, rope=None, dt=torch.bfl
     cfg = rope or api.rope()
     inv = O.rope_inv_freq(d_r, cfg.base, cfg.factor, cfg.orig_ctx, cfg.beta_fast, cfg.beta_slow)
     cache = api.DeviceCache(torch.from_numpy(pool).to(DEV),
-                            torch.from_numpy(scales).to(DEV) if fmt == O.FMT_FP8_E4M3 else None,
+                            torch.from_numpy(scales).to(DEV) if fmt in O.SCALED else None,
                             KV[fmt], d_c, d_r)
     o_pool, o_scales = pool.copy(), scales.copy()
     bt_dev = torch.from_numpy(bt).to(DEV)
@@ -72,7 +73,9 @@ def _run_appends(fmt, B, calls, d_c, d_r, d_model, seed, rope=None, dt=torch.bfl
             for i in range(ql):
                 p = int(pos[b]) + i
                 blk, sl = bt[b, p // BLK], p % BLK
-                if fmt == O.FMT_FP8_E4M3:
+                if fmt == O.FMT_FP8_E4M3_ROW:
+                    mask[blk, :(sl + 1) * (d_c + d_r)] = True   # earlier codes may be re-encoded
+                elif fmt in O.FP8_SPLIT:
                     mask[blk, :(sl + 1) * d_c] = True     # earlier codes may be re-encoded
                     off = BLK * d_c + sl * 2 * d_r
                     mask[blk, off:off + 2 * d_r] = True
@@ -81,7 +84,7 @@ def _run_appends(fmt, B, calls, d_c, d_r, d_model, seed, rope=None, dt=torch.bfl
                     mask[blk, sl * rb:(sl + 1) * rb] = True
         pos += ql
     torch.cuda.synchronize()
-    g_scales = cache.block_scales.cpu().numpy() if fmt == O.FMT_FP8_E4M3 else None
+    g_scales = cache.block_scales.cpu().numpy() if fmt in O.SCALED else None
     return cache.pool.cpu().numpy(), g_scales, o_pool, o_scales, pool0, mask
 
 
@@ -89,7 +92,7 @@ def _check_16bit_rows(got, want, mask, what):
     """bf16 / f32 payloads: at most one unit in the last place apart (the GPU
     sums in fp32, the oracle in fp64), mostly identical."""
     g, w = got[mask], want[mask]
-    if what == "bf16":
+    if what in ("bf16", "f16"):
         gi = g.view(np.int16).astype(np.int32)
         wi = w.view(np.int16).astype(np.int32)
     else:
@@ -97,13 +100,17 @@ def _check_16bit_rows(got, want, mask, what):
         wi = w.view(np.int32).astype(np.int64)
     d = np.abs(gi - wi)
     say(f"  {what}: {d.size} values, {np.count_nonzero(d)} differ by one ulp, max {d.max()}")
-    if what == "bf16":
+    if what in ("bf16", "f16"):
         # one ulp, except near zero: a sum that cancels to a small value keeps
         # the fp32 accumulation's absolute error (~1e-6 of the row scale)
-        dec = lambda x: (x.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        if what == "bf16":
+            dec = lambda x: (x.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        else:
+            dec = lambda x: x.view(np.float16).astype(np.float64)
         gv, wv = dec(g), dec(w)
         scale = np.sqrt(np.mean(wv[np.isfinite(wv)] ** 2))
-        ok = (d <= 1) | (np.abs(gv - wv) <= 2.0 ** -8 * np.abs(wv) + 1e-4 * scale)
+        ok = (d <= 1) | (np.abs(gv - wv) <= (2.0 ** -8 if what == "bf16" else 2.0 ** -11) * np.abs(wv)
+                         + 1e-4 * scale)
         assert ok.all()
         assert np.count_nonzero(d) <= max(2, d.size // 200)
     else:
@@ -139,34 +146,38 @@ def test_append_bf16_yarn():
     _check_16bit_rows(got, want, mask, "bf16")
 
 
-def test_append_fp8_scale_growth():
+@pytest.mark.parametrize("fmt", [O.FMT_FP8_E4M3, O.FMT_FP8_E5M2, O.FMT_FP8_E4M3_ROW])
+def test_append_fp8_scale_growth(fmt):
     """Calls of 1, 3 and 70 tokens (fresh blocks, partial blocks, a block
     crossing) where later tokens are larger: scales grow and earlier codes
     are re-encoded.  Codes may differ by one step where the fp32 and fp64
     products fall on opposite sides of a rounding point."""
     B, d_c, d_r, dm = 4, 512, 64, 128
-    got, g_sc, want, w_sc, pool0, mask = _run_appends(O.FMT_FP8_E4M3, B, [1, 3, 70, 1], d_c, d_r, dm,
+    got, g_sc, want, w_sc, pool0, mask = _run_appends(fmt, B, [1, 3, 70, 1], d_c, d_r, dm,
                                                       seed=23, start=0, h_scale=[0.1, 1.0, 3.0, 10.0])
     assert np.array_equal(got[~mask], pool0[~mask])
     touched = np.unique(np.nonzero(mask)[0])
     np.testing.assert_allclose(g_sc[touched], w_sc[touched], rtol=1e-6)
     other = np.setdiff1d(np.arange(len(g_sc)), touched)
     assert np.array_equal(g_sc[other], w_sc[other])
+    W = d_c + d_r if fmt == O.FMT_FP8_E4M3_ROW else d_c
     codes = np.zeros(mask.shape, bool)
-    codes[:, :BLK * d_c] = True
+    codes[:, :BLK * W] = True
     cm = mask & codes
     g, w = got[cm], want[cm]
-    # one e4m3 step apart at most: compare the decoded magnitudes' code order
-    gv, wv = O.e4m3_to_f64(g), O.e4m3_to_f64(w)
+    # one code step apart at most
+    gv, wv = O.fp8_decode(fmt, g), O.fp8_decode(fmt, w)
     diff = np.count_nonzero(g != w)
     say(f"  fp8 codes: {g.size}, {diff} differ")
     assert diff <= max(4, g.size // 500)
-    step = np.maximum(np.abs(wv) * 2.0 ** -3, 2.0 ** -9)
+    step = (np.maximum(np.abs(wv) * 2.0 ** -3, 2.0 ** -9) if fmt != O.FMT_FP8_E5M2
+            else np.maximum(np.abs(wv) * 2.0 ** -2, 2.0 ** -16))
     nan = np.isnan(wv)
     assert np.array_equal(np.isnan(gv), nan)
     assert np.all(np.abs(gv - wv)[~nan] <= step[~nan] * 1.0001)
-    rm = mask & ~codes
-    _check_16bit_rows(got[:, BLK * d_c:], want[:, BLK * d_c:], rm[:, BLK * d_c:], "bf16")
+    if fmt != O.FMT_FP8_E4M3_ROW:
+        rm = mask & ~codes
+        _check_16bit_rows(got[:, BLK * d_c:], want[:, BLK * d_c:], rm[:, BLK * d_c:], "bf16")
 
 
 def test_append_full_size_decode_step():
@@ -239,3 +250,10 @@ def test_project_q_generic_f32():
     e2 = row_rel_err(q_rope.cpu().numpy(), ref_rope)
     say(f"  f32: q_lat {e1:.3e}  q_rope {e2:.3e}")
     assert e1 <= TOL["f32"] and e2 <= TOL["f32"]
+
+
+def test_append_f16_rows():
+    B, d_c, d_r, dm = 5, 512, 64, 256
+    got, _, want, _, pool0, mask = _run_appends(O.FMT_F16, B, [3, 1, 70], d_c, d_r, dm, seed=27)
+    assert np.array_equal(got[~mask], pool0[~mask])
+    _check_16bit_rows(got, want, mask, "f16")
