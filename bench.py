@@ -43,8 +43,14 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak
 COPY_BYTES = 256 << 20          # calibration copy size
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_mfma_bf16_traffic.json")
-DECODE_KERNEL = "decode_mfma_kernel<false>"      # bf16 cache
-DECODE_KERNEL_FP8 = "decode_mfma_kernel<true>"   # fp8 cache, converted to bf16 in LDS
+DECODE_KERNEL = "decode_mfma_kernel<mla::kv::Bf16>"       # bf16 cache
+DECODE_KERNEL_FP8 = "decode_mfma_kernel<mla::kv::E4m3>"   # fp8 cache, converted to bf16 in LDS
+MFMA_KERNELS = {"bf16": DECODE_KERNEL, "fp8_e4m3": DECODE_KERNEL_FP8,
+                "f16": "decode_mfma_kernel<mla::kv::F16>",
+                "fp8_e5m2": "decode_mfma_kernel<mla::kv::E5m2>",
+                "fp8_e4m3_row": "decode_mfma_kernel<mla::kv::E4m3Row>"}
+KV_DTYPE_LABEL = {"bf16": "bf16", "f32": "f32", "f16": "f16", "fp8_e4m3": "fp8_e4m3+bf16",
+                  "fp8_e5m2": "fp8_e5m2+bf16", "fp8_e4m3_row": "fp8_e4m3"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -57,7 +63,8 @@ def parse():
                     help="cache pool replicas rotated per call (default: enough for >= 512 MB)")
     ap.add_argument("--workload", default="v2_decode_b32_s4096_bf16",
                     choices=["v2_decode_b32_s4096_bf16", "long_ctx_b4_s64k_128k_bf16",
-                             "fp8_cache_spec2_b64", "full_layer_b128_bf16", "decode_step_b128_bf16"],
+                             "fp8_cache_spec2_b64", "full_layer_b128_bf16", "decode_step_b128_bf16",
+                             "f16_decode_b32_s4096", "fp8_e5m2_spec2_b64", "fp8_e4m3_row_spec2_b64"],
                     help="the measured batch (default) or one of the other parity workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -123,7 +130,8 @@ def cpu_baseline(d, cache_bytes, max_rows=4096):
     import oracle as O
 
     wl = d.wl
-    fmt = {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "fp8_e4m3": O.FMT_FP8_E4M3}[wl.kv_dtype]
+    fmt = {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "fp8_e4m3": O.FMT_FP8_E4M3, "f16": O.FMT_F16,
+           "fp8_e5m2": O.FMT_FP8_E5M2, "fp8_e4m3_row": O.FMT_FP8_E4M3_ROW}[wl.kv_dtype]
     n_rows = wl.B * wl.q_len * wl.n_h
     rows = np.arange(n_rows, dtype=np.int64)
     if n_rows > max_rows:
@@ -168,6 +176,8 @@ def main():
         # the full-layer shapes, from hidden states: query production and the
         # cache append take the place of the drawn queries
         out = run_layer(args, I.C5, producers=True)
+    elif args.workload in I.FORMAT_WORKLOADS:
+        out = run_decode(args, I.FORMAT_WORKLOADS[args.workload])
     elif I.WORKLOADS[args.workload].d_model:
         out = run_layer(args, I.WORKLOADS[args.workload])
     else:
@@ -248,11 +258,8 @@ def copy_calibration(torch, timer, dev):
 
 def decode_kernel_name(wl) -> str:
     """The decode kernel libmla launches for this shape."""
-    if wl.q_dtype == "bf16" and wl.d_c == 512 and wl.d_r == 64:
-        if wl.kv_dtype == "bf16":
-            return DECODE_KERNEL
-        if wl.kv_dtype == "fp8_e4m3":
-            return DECODE_KERNEL_FP8
+    if wl.q_dtype == "bf16" and wl.d_c == 512 and wl.d_r == 64 and wl.kv_dtype in MFMA_KERNELS:
+        return MFMA_KERNELS[wl.kv_dtype]
     return "decode_generic_kernel"
 
 
@@ -260,10 +267,11 @@ def roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic):
     """Roofline of the decode kernel.  Bound: HBM when the workload's FLOP per
     cache byte is below the ridge of the kernel's contraction (bf16 MFMA 2.5
     PFLOP/s, or fp32 vector ALU 157.3 TFLOP/s for the generic kernel, against
-    8 TB/s), else the compute unit."""
+    8 TB/s), else the compute unit.  (fp16 caches run fp16 MFMAs, whose
+    dense peak equals bf16's.)"""
     gbs = cache_bytes / (dec_ms * 1e-3) / 1e9
     tfl = flops / (dec_ms * 1e-3) / 1e12
-    if kernel in (DECODE_KERNEL, DECODE_KERNEL_FP8):
+    if kernel in MFMA_KERNELS.values():
         cpeak, cbound = BF16_MFMA_PEAK_TFLOPS, "mfma"
     else:
         cpeak, cbound = FP32_VALU_PEAK_TFLOPS, "alu"
@@ -361,7 +369,7 @@ def run_decode(args, wl):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.kv_dtype == "bf16" else ("fp8_e4m3+bf16" if wl.kv_dtype == "fp8_e4m3" else "f32"),
+        "dtype": KV_DTYPE_LABEL[wl.kv_dtype],
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "seq_len": S[0] if len(set(S)) == 1 else [min(S), max(S)],
                    "q_len": wl.q_len, "n_h": wl.n_h, "d_c": wl.d_c, "d_r": wl.d_r,

@@ -30,7 +30,7 @@ import torch
 
 BLOCK = 64
 
-__all__ = ["Workload", "C1", "C2", "C3", "C4", "C5", "WORKLOADS", "PagedCache",
+__all__ = ["Workload", "C1", "C2", "C3", "C4", "C5", "WORKLOADS", "FORMAT_WORKLOADS", "PagedCache",
            "DecodeInputs", "draw_seq_lens", "draw_layer_weights", "draw_hidden",
            "draw_cache_rows", "draw_heavy_mask", "page_cache", "make_decode_inputs",
            "make_layer_inputs", "block_bytes"]
@@ -85,6 +85,15 @@ C5 = Workload("full_layer_b128_bf16", 1005, "bf16", "bf16", B=128, q_len=1, n_h=
               q_lora=1536)
 
 WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5)}
+
+# The other cache formats at the measured shapes: fp16 rows at the
+# 32 x 4096 batch, e5m2 latent codes and whole-row e4m3 at the speculative
+# fp8 batch (own seeds).
+FORMAT_WORKLOADS = {w.name: w for w in (
+    C2.scaled(name="f16_decode_b32_s4096", seed=1012, kv_dtype="f16"),
+    C4.scaled(name="fp8_e5m2_spec2_b64", seed=1014, kv_dtype="fp8_e5m2"),
+    C4.scaled(name="fp8_e4m3_row_spec2_b64", seed=1024, kv_dtype="fp8_e4m3_row"),
+)}
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 # fp8 cache formats: torch code type, largest finite value, whether k^R is coded too
