@@ -155,7 +155,7 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
  *
  * q_lat  [T][n_h][d_c], q_rope [T][n_h][d_r] in q_dtype (F32 or BF16); the
  *        pages pass q as the pair (q_nope_absorbed, q_pe) — here two pointers.
- * cache  see mla_cache_desc_t.  Fast paths: kv BF16 or FP8_E4M3 with q BF16,
+ * cache  see mla_cache_desc_t.  Fast paths: every kv dtype but F32 with q BF16,
  *        d_c = 512, d_r = 64 (MFMA); every other supported combination runs a
  *        generic kernel (d_c <= 1024, d_r <= 256, d_c and d_r multiples of 4).
  * block_table [B][bt_stride] int32 pool block ids; entries past
