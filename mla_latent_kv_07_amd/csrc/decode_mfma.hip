@@ -436,20 +436,36 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         else
             return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
     };
-    auto convert = [&](int st) {
-        const int valid = S - (p_first + st * HALF);
+    // latent codes of token t: [t][512] (split layout) or the first 512 of [t][576]
+    constexpr int CODE_PITCH = ROW ? DC + DR : DC;
+    // The staged bytes a thread converts, in five parts: part j < 4 is
+    // 16-byte chunk tid + 256 j of the 16 KiB of latent codes, part 4 a
+    // piece of the rotary part.
+    auto convert_load = [&](int st, int j) {
         const lds_u8 *src = smem + staging_off(st);
+        const int tid = opaque(threadIdx.x);
+        if (j < 4) {
+            const int i = tid + 256 * j;
+            const int t = i >> 5, c16 = i & 31;
+            return *(const uint4 *)(src + (ROW ? t * CODE_PITCH + c16 * 16 : i * 16));
+        }
+        const int t = tid >> 3, c = tid & 7;
+        if constexpr (ROW) {
+            const uint2 w = *(const uint2 *)(src + t * CODE_PITCH + DC + c * 8);   // rotary codes 8c..8c+7
+            return make_uint4(w.x, w.y, 0, 0);
+        } else {
+            return *(const uint4 *)(src + FP8_LAT + t * RB + c * 16);
+        }
+    };
+    auto convert_part = [&](int st, const uint4 &in, int j) {
+        const int valid = S - (p_first + st * HALF);
         lds_u8 *dst = smem + stage_off(st);
         const int tid = opaque(threadIdx.x);
-        // latent codes of token t: [t][512] (split layout) or the first 512 of [t][576]
-        constexpr int CODE_PITCH = ROW ? DC + DR : DC;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = tid + 256 * j;   // 16-byte chunk of the 16 KiB of latent codes
+        if (j < 4) {
+            const int i = tid + 256 * j;
             const int t = i >> 5, c16 = i & 31;
-            const uint4 v = *(const uint4 *)(src + (ROW ? t * CODE_PITCH + c16 * 16 : i * 16));
             uint32_t o[8];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const uint32_t w[4] = {in.x, in.y, in.z, in.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 o[2 * e] = cvt_lo(w[e]);
@@ -459,20 +475,20 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             uint4 *d = (uint4 *)(dst + t * LPITCH + c16 * 32);
             d[0] = live ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
             d[1] = live ? make_uint4(o[4], o[5], o[6], o[7]) : make_uint4(0, 0, 0, 0);
-        }
-        {
+        } else {
             const int t = tid >> 3, c = tid & 7;
-            uint4 v;
-            if constexpr (ROW) {
-                // rotary codes 8c..8c+7 of token t
-                const uint2 w = *(const uint2 *)(src + t * CODE_PITCH + DC + c * 8);
-                v = make_uint4(cvt_lo(w.x), cvt_hi(w.x), cvt_lo(w.y), cvt_hi(w.y));
-            } else {
-                v = *(const uint4 *)(src + FP8_LAT + t * RB + c * 16);
-            }
+            uint4 v = in;
+            if constexpr (ROW) v = make_uint4(cvt_lo(in.x), cvt_hi(in.x), cvt_lo(in.y), cvt_hi(in.y));
             *(uint4 *)(dst + LAT_BYTES + (t >> 3) * 1024 + c * 128 + (t & 7) * 16) =
                 t < valid ? v : make_uint4(0, 0, 0, 0);
         }
+    };
+    auto convert = [&](int st) {
+        uint4 in[5];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) in[j] = convert_load(st, j);
+#pragma unroll
+        for (int j = 0; j < 5; ++j) convert_part(st, in[j], j);
     };
 
     // ---- prologue: score of stage 0
@@ -620,6 +636,25 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         l_lane = l_lane * alpha + (FP8 ? psum / sig_cur : psum);
         m_run = m_new;
 
+        // fp8: stage st+2 is converted during the value MFMAs, into the
+        // buffer of stage st-1 (free since the barrier at the top).  Every
+        // wave waits for its copy of stage st+2 (stage st+3's may still be in
+        // flight); the barrier makes all copies visible; the staged bytes are
+        // converted in five parts between them, each part read one slot
+        // ahead; the next iteration's barrier publishes the result.
+        const bool conv = FP8 && st + 2 < nst_live;
+        uint4 cin[2];
+        if constexpr (FP8) {
+            if (conv) {
+                if (st + 3 < nst_live)
+                    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();   // every wave's copy of stage st+2 has landed
+                cin[0] = convert_load(st + 2, 0);
+            }
+        }
+
         // value MFMAs: O^T[512 x 32] += V^T[512 x 32 tok] . P^T[32 tok x 32]
         // as two 16-token k-steps, V fragments PF MFMAs ahead
         const uint32_t vbs = vb0 + stage_off(st);
@@ -638,21 +673,19 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             if (i + PF < 2 * MBLOCKS) vb[i % PF] = vld(vbs, i + PF);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i + PF < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        if constexpr (FP8) {
-            // stage st+2: wait for this wave's copy (stage st+3's may still be
-            // in flight), then convert it into the buffer of stage st-1, free
-            // since the barrier above; the next iteration's barrier publishes it
-            if (st + 2 < nst_live) {
-                if (st + 3 < nst_live)
-                    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-                else
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                __syncthreads();   // every wave's copy of stage st+2 has landed
-                convert(st + 2);
+            if constexpr (FP8) {
+                if (i % 6 == 4) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (conv) {
+                        const int j = i / 6;
+                        if (j < 4) cin[(j + 1) & 1] = convert_load(st + 2, j + 1);
+                        convert_part(st + 2, cin[j & 1], j);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            sig_cur = sig_next;
         }
+        if constexpr (FP8) sig_cur = sig_next;
     };
 
     // two iterations per trip so that the score accumulators swap roles
