@@ -69,6 +69,7 @@ constexpr int MBLOCKS = DC / 32;                // 16 value M-blocks
 constexpr int O_PITCH = CB + 16;                // epilogue staging row pitch (bytes)
 constexpr int PF = 8;                           // value-fragment prefetch depth (MFMAs)
 constexpr int PFK = 3;                          // score-fragment prefetch depth (MFMAs)
+template <bool FP8> constexpr int copy_at() { return FP8 ? 0 : 2; }   // stage copies: 0 top, 1 score MFMAs, 2 value MFMAs
 // fp8 caches: each stage's e4m3 latent (32 x 512 B) and bf16 rotary rows
 // (32 x 128 B) land in one of two staging buffers, and are converted once per
 // workgroup into a bf16 stage buffer of the layout above (three of them).
@@ -77,16 +78,29 @@ constexpr int FP8_STAGE = FP8_LAT + HALF * RB;  // 20480
 constexpr int NSTAGE8 = 3;
 template <bool FP8>
 constexpr int lds_bytes() { return FP8 ? NSTAGE8 * STAGE_BYTES + 2 * FP8_STAGE : NSTAGE * STAGE_BYTES; }
-static_assert(lds_bytes<false>() <= 160 * 1024 && lds_bytes<true>() <= 160 * 1024, "stage buffers exceed LDS");
+// After the stage buffers: the pool ids of an item's first TAB_IDS blocks
+// (read once in the prologue, so that the stage loop issues no scalar memory
+// load), then for 8-bit caches a ring of 4 block-scale slots, one per stage in
+// flight, each filled by the stage's own copy.
+constexpr int TAB_IDS = 1024;
+template <bool FP8>
+constexpr int tab_off() { return lds_bytes<FP8>(); }
+template <bool FP8>
+constexpr int ring_off() { return tab_off<FP8>() + 4 * TAB_IDS; }
+template <bool FP8>
+constexpr int lds_total() { return ring_off<FP8>() + (FP8 ? 16 : 0); }
+static_assert(lds_total<false>() <= 160 * 1024 && lds_total<true>() <= 160 * 1024, "stage buffers exceed LDS");
 static_assert(4 * 18432 <= 2 * STAGE_BYTES, "query halves exceed stage buffers 0-1");
+static_assert(LAT_BYTES % 128 == 0 && STAGE_BYTES % 128 == 0, "rotary reads XOR bits 5-6 of their offsets");
 static_assert(2 * STAGE_BYTES <= NSTAGE8 * STAGE_BYTES, "fp8: query halves overlap the staging buffers");
 static_assert(4 * 32 * O_PITCH <= lds_bytes<true>() && 4 * 32 * O_PITCH <= lds_bytes<false>(),
               "epilogue staging exceeds the LDS allocation");
 
 // LDS layout of a stage (slot t = token t of the stage):
 //   latent rows  [32][1040 B]: bytes 0..1023 of slot t = c of token t;
-//   rotary part  [4][8 chunks][8 tokens][16 B]: chunk c of token t at
-//                LAT_BYTES + (t >> 3) * 1024 + c * 128 + (t & 7) * 16.
+//   rotary part  [32 tokens][8 slots][16 B], token-major: token t's 128 B at
+//                LAT_BYTES + (t >> 3) * 1024 + (t & 7) * 128, its 16-byte
+//                chunk c in slot c ^ rot_swz(t).
 // Row i of the score MFMA (A-operand lane i) reads slot tok_of(i), where
 // i = 8a + 4h + e  ->  16 (a >> 1) + 4 e + 2 (a & 1) + h.
 // With 64 four-byte banks (256 B per cycle), the 16-byte pitch step makes
@@ -97,6 +111,16 @@ static_assert(4 * 32 * O_PITCH <= lds_bytes<true>() && 4 * 32 * O_PITCH <= lds_b
 __device__ __forceinline__ constexpr int tok_of(int i) {
     return 16 * (i >> 4) + 4 * (i & 3) + 2 * ((i >> 3) & 1) + ((i >> 2) & 1);
 }
+// Chunk swizzle of the rotary part.  One 16-lane pass of a score read takes
+// chunk c of 16 tokens: t & 7 = 0..7 of two 8-token groups.  Token t's slot
+// lands in 16-byte bank group 8 (t & 1) + (c ^ rot_swz(t)); over the 4 tokens
+// of one parity in a group rot_swz takes 4 values that differ in bits 0-1, and
+// the two groups differ in bit 2, so the 16 reads hit 16 distinct bank groups.
+// The copy fills a token's 128 B from 8 consecutive lanes, so each 16-lane
+// quarter of a copy reads 2 cache lines; a chunk-major layout made every
+// quarter touch 8 lines and cost the copy four times the issue time of a
+// contiguous one.
+__device__ __forceinline__ constexpr int rot_swz(int t) { return ((t & 7) >> 1) ^ (((t >> 3) & 1) << 2); }
 
 // One asynchronous 1 KiB copy: global_load_lds_dwordx4 writes lane i's 16
 // bytes to LDS at M0 + 16 i.  Issued as inline asm so that the compiler's
@@ -111,45 +135,66 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const ui
                  : "memory", "m0");
 }
 
-constexpr int DMA_PER_STAGE = 9;   // per wave: 8 latent rows + 1 KiB of rotary parts
+// One asynchronous 4-byte copy by lane 0 only: to LDS at M0 (the block scale
+// of an 8-bit stage).  Same wait discipline as dma16.
+__device__ __forceinline__ void dma4_lane0(uint32_t lds_addr, const uint8_t *src, int lane) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    if (lane == 0)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                     :: "s"(m0), "v"(0u), "s"(src) : "memory", "m0");
+}
 
-// Copy one stage whose first token is at src0 (token row pointer in HBM).
-// Wave w copies latent rows 8w..8w+7 (one 1 KiB instruction each; lane i
-// reads bytes 16i..16i+15, voff = l16 = 16 i) and the rotary parts of the same
-// 8 tokens (one instruction; lane i = 8c + u reads chunk c of token 8w + u,
-// voff = rot_off).
-__device__ __forceinline__ void issue_stage(const uint8_t *src0, uint32_t stage_lds, int wave,
-                                            uint32_t l16, uint32_t rot_off) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
+// The copy of one stage is split into parts (one instruction each) so that
+// the stage loop can spread them over the score MFMAs.
+constexpr int DMA_PER_STAGE = 9;    // 16-bit rows, per wave: 8 latent rows + 1 KiB of rotary parts
+constexpr int DMA_PER_STAGE8 = 6;   // 8-bit codes, per wave: the block scale + 5 KiB
+
+// Part k of a 16-bit stage whose first token is at src0 (token row pointer in
+// HBM).  Wave w copies latent row 8w + k for k < 8 (one 1 KiB instruction;
+// lane i reads bytes 16i..16i+15, voff = l16 = 16 i) and, for k = 8, the
+// rotary parts of the same 8 tokens (lane i = 8u + p fills slot p of token
+// 8w + u, i.e. reads its chunk p ^ rot_swz(8w + u); voff = rot_off).
+__device__ __forceinline__ void stage_part(const uint8_t *src0, uint32_t stage_lds, int wave,
+                                           uint32_t l16, uint32_t rot_off, int k) {
+    if (k < 8) {
         const int t = wave * 8 + k;
         dma16(stage_lds + t * LPITCH, l16, src0 + t * ROW_BYTES);
+    } else {
+        dma16(stage_lds + LAT_BYTES + wave * 1024, rot_off, src0);
     }
-    dma16(stage_lds + LAT_BYTES + wave * 1024, rot_off, src0);
 }
 
-// fp8 cache: copy one stage (32 tokens) of a block into a staging buffer:
-// wave w copies latent bytes [4 KiB w, 4 KiB (w + 1)) (two 512-byte rows per
-// 1 KiB instruction) and the 8 rotary rows 8w..8w+7 (one instruction).
-__device__ __forceinline__ void issue_stage_fp8(const uint8_t *codes0, const uint8_t *rope0,
-                                                uint32_t staging_lds, int wave, uint32_t l16) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dma16(staging_lds + (4 * wave + k) * 1024, l16, codes0 + (4 * wave + k) * 1024);
-    dma16(staging_lds + FP8_LAT + wave * 1024, l16, rope0 + wave * 1024);
+// Part k of an 8-bit stage (32 tokens of a block) into a staging buffer:
+// k = 0 the block scale (lane 0 of every wave, into the stage's ring slot);
+// e4m3 / e5m2 latent: k = 1..4 latent bytes 4 KiB w + 1 KiB (k - 1) (two
+// 512-byte rows per instruction), k = 5 the 8 rotary rows 8w..8w+7.
+__device__ __forceinline__ void stage_part_fp8(const uint8_t *codes0, const uint8_t *rope0, const uint8_t *scale,
+                                               uint32_t staging_lds, uint32_t ring_lds, int wave, int lane, int k) {
+    const uint32_t l16 = (uint32_t)lane << 4;
+    if (k == 0)
+        dma4_lane0(ring_lds, scale, lane);
+    else if (k < 5)
+        dma16(staging_lds + (4 * wave + k - 1) * 1024, l16, codes0 + (4 * wave + k - 1) * 1024);
+    else
+        dma16(staging_lds + FP8_LAT + wave * 1024, l16, rope0 + wave * 1024);
 }
 
-// whole-row e4m3 cache: one stage is 32 contiguous rows of 576 codes (18 KiB)
-// of the block's [64][576]; wave w copies KiB 4w..4w+3 and KiB 16 + (w & 1)
-// (waves 2 and 3 repeat the copies of waves 0 and 1: same bytes, same place),
-// so every wave issues as many copies as for the split layout.
-__device__ __forceinline__ void issue_stage_row(const uint8_t *rows0, uint32_t staging_lds, int wave, uint32_t l16) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dma16(staging_lds + (4 * wave + k) * 1024, l16, rows0 + (4 * wave + k) * 1024);
-    dma16(staging_lds + (16 + (wave & 1)) * 1024, l16, rows0 + (16 + (wave & 1)) * 1024);
+// Whole-row e4m3 cache: one stage is 32 contiguous rows of 576 codes (18 KiB)
+// of the block's [64][576]; after the scale (k = 0), wave w copies KiB
+// 4w + k - 1 for k = 1..4 and KiB 16 + (w & 1) for k = 5 (waves 2 and 3
+// repeat the last copies of waves 0 and 1: same bytes, same place), so every
+// wave issues as many copies as for the split layout.
+__device__ __forceinline__ void stage_part_row(const uint8_t *rows0, const uint8_t *scale, uint32_t staging_lds,
+                                               uint32_t ring_lds, int wave, int lane, int k) {
+    const uint32_t l16 = (uint32_t)lane << 4;
+    if (k == 0) {
+        dma4_lane0(ring_lds, scale, lane);
+    } else {
+        const int kib = k < 5 ? 4 * wave + k - 1 : 16 + (wave & 1);
+        dma16(staging_lds + kib * 1024, l16, rows0 + kib * 1024);
+    }
 }
 static_assert(HALF * (DC + DR) <= 18 * 1024 && 18 * 1024 <= FP8_STAGE, "row stage copy");
-
-constexpr int DMA_PER_STAGE8 = 5;
 
 // Loads of wave-uniform values (plan, block table, lengths) through the
 // constant address space become scalar loads, which never wait on the
@@ -183,7 +228,8 @@ __device__ __forceinline__ int opaque(int v) {
 template <typename KV>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     constexpr bool FP8 = KV::fp8, ROW = KV::row, H16 = KV::half;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem_[lds_bytes<FP8>()];
+    constexpr int COPY_AT = copy_at<FP8>();
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_[lds_total<FP8>()];
     lds_u8 *smem = (lds_u8 *)smem_;
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
@@ -225,12 +271,21 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         int64_t id = sload(a.block_table, bt_row + blk0 + (st >> 1));
         return id < 0 ? 0 : (id >= num_blocks ? num_blocks - 1 : id);
     };
-    auto stage_src = [&](int st) {   // HBM row of the stage's first token (bf16 layout)
-        return pool + blk_id(st) * (int64_t)(kBlock * ROW_BYTES) + (st & 1) * HALF * ROW_BYTES;
+    // pool id of the block holding stage st, from the LDS table once the
+    // prologue has filled it (a scalar load for blocks past its end)
+    const int ntab = min(blk1 - blk0, TAB_IDS);
+    const __attribute__((address_space(3))) int32_t *tab =
+        (const __attribute__((address_space(3))) int32_t *)(smem + tab_off<FP8>());
+    // (raw: the table entry of stage st as read into a VGPR, tab_raw(st))
+    auto tab_raw = [&](int st) { return tab[min(st >> 1, TAB_IDS - 1)]; };
+    auto blk_id_tab = [&](int st, int raw) -> int64_t {
+        if ((st >> 1) < ntab) return __builtin_amdgcn_readfirstlane(raw);
+        return blk_id(st);
     };
-    // block scale of a stage (fp8)
+    // block scale of stage st (8-bit caches): its ring slot, filled by the
+    // stage's copy
     auto sigma = [&](int st) {
-        return __int_as_float(sload((const int32_t *)a.block_scales, blk_id(st)));
+        return *(const __attribute__((address_space(3))) float *)(smem + ring_off<FP8>() + 4 * (st & 3));
     };
     auto stage_off = [&](int st) {
         // bf16: stage st in buffer (st + 2) mod 4 (buffers 0-1 hold the queries
@@ -239,27 +294,39 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     };
     auto staging_off = [&](int st) { return (uint32_t)(NSTAGE8 * STAGE_BYTES + (st & 1) * FP8_STAGE); };
     const uint32_t l16 = lane << 4;
-    const uint32_t rot_off = FP8 ? 0u : (uint32_t)((wave * 8 + (lane & 7)) * ROW_BYTES + CB + 16 * (lane >> 3));
-    auto issue = [&](int st) {
-        if constexpr (ROW) {
-            const uint8_t *blk = pool + blk_id(st) * a.block_bytes;
-            issue_stage_row(blk + (st & 1) * HALF * (DC + DR), smem_addr + staging_off(st), wave,
-                            (uint32_t)opaque(lane) << 4);
-        } else if constexpr (FP8) {
-            const uint8_t *blk = pool + blk_id(st) * a.block_bytes;
-            issue_stage_fp8(blk + (st & 1) * FP8_LAT, blk + kBlock * DC + (st & 1) * HALF * RB,
-                            smem_addr + staging_off(st), wave, (uint32_t)opaque(lane) << 4);
+    auto rot_voff = [&](int ln_) {
+        const int t = wave * 8 + (ln_ >> 3);
+        return (uint32_t)(t * ROW_BYTES + CB + 16 * ((ln_ & 7) ^ rot_swz(t)));
+    };
+    const uint32_t rot_off = FP8 ? 0u : rot_voff(lane);
+    // part k of the copy of stage st, held by pool block id
+    constexpr int NPARTS = FP8 ? DMA_PER_STAGE8 : DMA_PER_STAGE;
+    auto issue_part = [&](int st, int64_t id, int k) {
+        if constexpr (FP8) {
+            const uint8_t *blk = pool + id * a.block_bytes;
+            const uint8_t *scale = (const uint8_t *)a.block_scales + 4 * id;
+            const uint32_t ring = smem_addr + ring_off<FP8>() + 4 * (st & 3);
+            if constexpr (ROW)
+                stage_part_row(blk + (st & 1) * HALF * (DC + DR), scale, smem_addr + staging_off(st), ring, wave,
+                               opaque(lane), k);
+            else
+                stage_part_fp8(blk + (st & 1) * FP8_LAT, blk + kBlock * DC + (st & 1) * HALF * RB, scale,
+                               smem_addr + staging_off(st), ring, wave, opaque(lane), k);
         } else {
+            const uint8_t *src0 = pool + id * (int64_t)(kBlock * ROW_BYTES) + (st & 1) * HALF * ROW_BYTES;
             if constexpr (H16) {
                 // the fp16 variant's register allocation spills these two
                 // offsets; recomputed where they are used instead
                 const int ol = opaque(lane);
-                issue_stage(stage_src(st), smem_addr + stage_off(st), wave, (uint32_t)ol << 4,
-                            (uint32_t)((wave * 8 + (ol & 7)) * ROW_BYTES + CB + 16 * (ol >> 3)));
+                stage_part(src0, smem_addr + stage_off(st), wave, (uint32_t)ol << 4, rot_voff(ol), k);
             } else {
-                issue_stage(stage_src(st), smem_addr + stage_off(st), wave, l16, rot_off);
+                stage_part(src0, smem_addr + stage_off(st), wave, l16, rot_off, k);
             }
         }
+    };
+    auto issue = [&](int st, int64_t id) {
+#pragma unroll
+        for (int k = 0; k < NPARTS; ++k) issue_part(st, id, k);
     };
 
     // ---- queries -> VGPRs (MFMA B fragments: lane (ln, g) holds, for k-step
@@ -304,21 +371,41 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             for (int j = 0; j < DR / 16; ++j)
                 qf[KC + j] = *(const bf16x8 *)(qw + 16 * CB + (lr >> 3) * 1024 + (2 * j + g) * 128 + (lr & 7) * 16);
         };
+        // the block-id table: plain loads issued before any copy (so the
+        // wait the compiler places before the table writes, after every copy
+        // has landed, holds nothing back)
+        int tv[TAB_IDS / 256];
+#pragma unroll
+        for (int k = 0; k < TAB_IDS / 256; ++k) {
+            const int j = (int)threadIdx.x + 256 * k;
+            tv[k] = j < ntab ? a.block_table[bt_row + blk0 + j] : 0;
+        }
         copy_half(0);
-        issue(0);
-        if (nst_live > 1) issue(1);
+        issue(0, blk_id(0));
+        if (nst_live > 1) issue(1, blk_id(1));
         // the first half has landed when at most the stage copies are in flight
         if (nst_live > 1) {
-            if constexpr (FP8) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            if constexpr (FP8) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
             else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
         } else {
-            if constexpr (FP8) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+            if constexpr (FP8) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
             else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
         }
         if (ln < 16) read_half();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the region is refilled
         copy_half(1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // second half, stages 0 and 1
+        {
+            __attribute__((address_space(3))) int32_t *tw =
+                (__attribute__((address_space(3))) int32_t *)(smem + tab_off<FP8>());
+#pragma unroll
+            for (int k = 0; k < TAB_IDS / 256; ++k) {
+                // every entry is written (0 past the item's blocks), so that
+                // no load stays outstanding for the compiler past this point
+                const int j = (int)threadIdx.x + 256 * k;
+                tw[j] = tv[k] < 0 ? 0 : (tv[k] >= num_blocks ? (int)(num_blocks - 1) : tv[k]);
+            }
+        }
         if (ln >= 16) read_half();
         if constexpr (H16) {
             // fp16 cache: the queries as fp16 (saturating)
@@ -343,7 +430,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     // Per-lane LDS read bases (a stage offset is added once per stage; every
     // read adds a compile-time offset).
     //  score, latent k-step ks: slot tok_of(ln), chunk 2 ks + g -> kb0 + 32 ks
-    //  score, rotary k-step KC + j: chunk 2 j + g of slot tok_of(ln) -> rb0 + 256 j
+    //  score, rotary k-step KC + j: chunk 2 j + g of token tq = tok_of(ln), in
+    //  slot (2 j + g) ^ rot_swz(tq) = 2 j ^ (g ^ rot_swz(tq)): rb0 holds the
+    //  token's base + 16 (g ^ rot_swz(tq)) (a stage offset keeps bits 0-6
+    //  clear), the k-step applies ^ 32 j
     //  value (ds_read_b64_tr_b16: lane i of each 16-lane group receives element
     //  i % 4 of the 8 bytes read by lane 4s + i/4, s = 0..3): k-step s2 needs,
     //  for lane half g, the tokens tok_of(8 s2 + 4 g + e) = 4 e + 2 s2 + g and,
@@ -352,13 +442,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     //  -> vb0 + 2 LPITCH s2 + 64 mb (+ 16 LPITCH).
     const int tq = tok_of(ln);
     const uint32_t kb0 = tq * LPITCH + 16 * g;
-    const uint32_t rb0 = LAT_BYTES + (tq >> 3) * 1024 + 128 * g + (tq & 7) * 16;
+    const uint32_t rb0 = LAT_BYTES + (tq >> 3) * 1024 + (tq & 7) * 128 + 16 * (g ^ rot_swz(tq));
     const int grp16 = lane >> 4, w16 = lane & 15;
     const uint32_t vb0 = (4 * (w16 >> 2) + (grp16 >> 1)) * LPITCH + 32 * (grp16 & 1) + 8 * (w16 & 3);
 
     auto kld = [&](uint32_t kbs, uint32_t rbs, int ks) {
         return ks < KC ? *(const bf16x8 *)(smem + kbs + 32 * ks)
-                       : *(const bf16x8 *)(smem + rbs + 256 * (ks - KC));
+                       : *(const bf16x8 *)(smem + (rbs ^ (uint32_t)(32 * (ks - KC))));
     };
     auto vld = [&](uint32_t vbs, int i) {
         const int s2 = i / MBLOCKS, mb = i % MBLOCKS;
@@ -416,7 +506,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
                 *(uint4 *)(stg + (valid + (idx >> 6)) * LPITCH + (idx & 63) * 16) = make_uint4(0, 0, 0, 0);
             for (int idx = threadIdx.x; idx < (HALF - valid) * 8; idx += 256) {
                 const int t = valid + (idx >> 3), c = idx & 7;
-                *(uint4 *)(stg + LAT_BYTES + (t >> 3) * 1024 + c * 128 + (t & 7) * 16) = make_uint4(0, 0, 0, 0);
+                *(uint4 *)(stg + LAT_BYTES + (t >> 3) * 1024 + (t & 7) * 128 + c * 16) = make_uint4(0, 0, 0, 0);
             }
         }
     };
@@ -479,7 +569,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             const int t = tid >> 3, c = tid & 7;
             uint4 v = in;
             if constexpr (ROW) v = make_uint4(cvt_lo(in.x), cvt_hi(in.x), cvt_lo(in.y), cvt_hi(in.y));
-            *(uint4 *)(dst + LAT_BYTES + (t >> 3) * 1024 + c * 128 + (t & 7) * 16) =
+            *(uint4 *)(dst + LAT_BYTES + (t >> 3) * 1024 + (t & 7) * 128 + (c ^ rot_swz(t)) * 16) =
                 t < valid ? v : make_uint4(0, 0, 0, 0);
         }
     };
@@ -499,10 +589,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         convert(0);
         if (nst_live > 1) convert(1);
         __syncthreads();
-        if (nst_live > 2) issue(2);
+        if (nst_live > 2) issue(2, blk_id_tab(2, tab_raw(2)));
         sig_cur = sigma(0);
     } else {
-        if (nst_live > 2) issue(2);
+        if (nst_live > 2) issue(2, blk_id_tab(2, tab_raw(2)));
         zero_tail(0);
     }
     f32x16 sA, sB;
@@ -523,14 +613,27 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     // ---- one pipelined iteration: scores of stage st (cur, complete) become
     // probabilities while stage st+1's score MFMAs fill nxt; then stage st's
     // value MFMAs.
-    auto iteration = [&](int st, f32x16 &cur, f32x16 &nxt) {
+    // raw: on entry the table entry of stage st+3 (read one iteration ahead,
+    // so its LDS latency is hidden); on exit that of stage st+4
+    auto iteration = [&](int st, f32x16 &cur, f32x16 &nxt, int &raw) {
         const bool has_next = st + 1 < nst_live;
+        // stage st+3 is copied in parts spread over this iteration's score
+        // MFMAs
+        const bool iss = st + 3 < nst_live;
+        const int64_t id3 = iss ? blk_id_tab(st + 3, raw) : 0;
+        auto copy_slot = [&](int i, int n) {   // slot i of n MFMAs: one copy part
+            const int spread = n / NPARTS;
+            if (i % spread == 1 && i / spread < NPARTS) {
+                if (iss) issue_part(st + 3, id3, i / spread);
+            }
+        };
         if constexpr (FP8) {
-            // stage st+1 was converted at the end of iteration st-1 (or in the
+            // stage st+1 was converted during iteration st-1 (or in the
             // prologue); every wave has finished iteration st-1, so the
-            // staging buffer of stage st+1 may be refilled with stage st+3
+            // staging buffer and scale slot of stage st+1 may be refilled
+            // with stage st+3
             __syncthreads();
-            if (st + 3 < nst_live) issue(st + 3);
+            if constexpr (COPY_AT == 0) { if (iss) issue(st + 3, id3); }
             if (has_next) sig_next = sigma(st + 1);
         } else {
             if (has_next) {
@@ -543,7 +646,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             // every wave's copy of stage st+1 is visible, and every wave has
             // finished iteration st-1, so stage st-1's buffer may be refilled
             __syncthreads();
-            if (st + 3 < nst_live) issue(st + 3);
+            if constexpr (COPY_AT == 0) { if (iss) issue(st + 3, id3); }
             if (has_next) zero_tail(st + 1);
         }
         const uint32_t kbs = kb0 + stage_off(st + 1), rbs = rb0 + stage_off(st + 1);
@@ -614,6 +717,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
                 if (i + PFK < KS) kb[i % PFK] = kld(kbs, rbs, kstep(i + PFK));
                 if (FP8 && !ROW && i == DR / 16 - 1) rope_to_latent_scale(nxt, 1.0f / sig_next);
                 softmax_slice(i);
+                if constexpr (COPY_AT == 1) copy_slot(i, KS);
                 __builtin_amdgcn_sched_barrier(0);
             }
             asm volatile("s_nop 15" : "+v"(nxt));
@@ -642,12 +746,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         // flight); the barrier makes all copies visible; the staged bytes are
         // converted in five parts between them, each part read one slot
         // ahead; the next iteration's barrier publishes the result.
+        raw = tab_raw(st + 4);
         const bool conv = FP8 && st + 2 < nst_live;
         uint4 cin[2];
         if constexpr (FP8) {
             if (conv) {
-                if (st + 3 < nst_live)
-                    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+                if (COPY_AT != 2 && st + 3 < nst_live)
+                    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();   // every wave's copy of stage st+2 has landed
@@ -673,6 +778,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             if (i + PF < 2 * MBLOCKS) vb[i % PF] = vld(vbs, i + PF);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i + PF < 2 * MBLOCKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if constexpr (COPY_AT == 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                copy_slot(i, 2 * MBLOCKS);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if constexpr (FP8) {
                 if (i % 6 == 4) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -690,9 +800,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
 
     // two iterations per trip so that the score accumulators swap roles
     // without register copies
+    int raw = tab_raw(3);
     for (int st = 0; st < nst_live; st += 2) {
-        iteration(st, sA, sB);
-        if (st + 1 < nst_live) iteration(st + 1, sB, sA);
+        iteration(st, sA, sB, raw);
+        if (st + 1 < nst_live) iteration(st + 1, sB, sA, raw);
     }
 
     // ---- epilogue: O / l as bf16 rows staged through LDS, then 1 KiB
