@@ -298,7 +298,6 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         const int t = wave * 8 + (ln_ >> 3);
         return (uint32_t)(t * ROW_BYTES + CB + 16 * ((ln_ & 7) ^ rot_swz(t)));
     };
-    const uint32_t rot_off = FP8 ? 0u : rot_voff(lane);
     // part k of the copy of stage st, held by pool block id
     constexpr int NPARTS = FP8 ? DMA_PER_STAGE8 : DMA_PER_STAGE;
     auto issue_part = [&](int st, int64_t id, int k) {
@@ -314,14 +313,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
                                smem_addr + staging_off(st), ring, wave, opaque(lane), k);
         } else {
             const uint8_t *src0 = pool + id * (int64_t)(kBlock * ROW_BYTES) + (st & 1) * HALF * ROW_BYTES;
-            if constexpr (H16) {
-                // the fp16 variant's register allocation spills these two
-                // offsets; recomputed where they are used instead
-                const int ol = opaque(lane);
-                stage_part(src0, smem_addr + stage_off(st), wave, (uint32_t)ol << 4, rot_voff(ol), k);
-            } else {
-                stage_part(src0, smem_addr + stage_off(st), wave, l16, rot_off, k);
-            }
+            // the two per-lane offsets are recomputed where they are used
+            // (held across the loop, they were spilled)
+            const int ol = opaque(lane);
+            stage_part(src0, smem_addr + stage_off(st), wave, (uint32_t)ol << 4, rot_voff(ol), k);
         }
     };
     auto issue = [&](int st, int64_t id) {
@@ -467,25 +462,38 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     // builtin an AGPR accumulator, and the 256 AGPRs are all taken by O^T.
     // Hazards the compiler cannot see are covered by hand: the chain
     // accumulates back to back into the same registers (no wait states
-    // needed); s_nop 1 before each MFMA covers a VALU write of an operand or
-    // of the accumulator; an s_nop 15 after a chain covers the MFMA-result ->
-    // VALU-read latency (>= 10 wait states for an 8-pass MFMA).
-    auto score_mfma = [&](f32x16 &acc, const bf16x8 &kf, int i) {
+    // needed); its operands come from LDS reads (waited by lgkmcnt) or stay
+    // resident, so inside the stage loop only a VALU write of the
+    // accumulator needs the 2 wait states of an s_nop 1 (the fp8 rescale
+    // after the rotary k-steps; the first MFMA takes one too).  The chain of
+    // stage 0 keeps a nop before every MFMA: the compiler may place the
+    // fp16 conversion of a query fragment right before its first use.  An
+    // s_nop 15 after a chain covers the MFMA-result -> VALU-read latency
+    // (>= 10 wait states for an 8-pass MFMA).  A nop before every MFMA cost
+    // ~130 cycles per stage of issue.
+    auto score_mfma = [&](f32x16 &acc, const bf16x8 &kf, int i, bool all_nops) {
+        const bool nop = all_nops || i == 0 || (FP8 && !ROW && i == DR / 16);
         // the first MFMA writes the accumulator while reading its operands:
         // early clobber keeps them apart
         if constexpr (H16) {
             if (i == 0)
                 asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0"
                              : "=&v"(acc) : "v"(kf), "v"(qf[kstep(0)]));
-            else
+            else if (nop)
                 asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                             : "+v"(acc) : "v"(kf), "v"(qf[kstep(i)]));
+            else
+                asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
                              : "+v"(acc) : "v"(kf), "v"(qf[kstep(i)]));
         } else {
             if (i == 0)
                 asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
                              : "=&v"(acc) : "v"(kf), "v"(qf[kstep(0)]));
-            else
+            else if (nop)
                 asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+v"(acc) : "v"(kf), "v"(qf[kstep(i)]));
+            else
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                              : "+v"(acc) : "v"(kf), "v"(qf[kstep(i)]));
         }
     };
@@ -603,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         for (int j = 0; j < PFK; ++j) kb[j] = kld(kbs, rbs, kstep(j));
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-            score_mfma(sA, kb[i % PFK], i);
+            score_mfma(sA, kb[i % PFK], i, true);
             if (i + PFK < KS) kb[i % PFK] = kld(kbs, rbs, kstep(i + PFK));
             if (FP8 && !ROW && i == DR / 16 - 1) rope_to_latent_scale(sA, 1.0f / sig_cur);
         }
@@ -713,7 +721,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         if (has_next) {
 #pragma unroll
             for (int i = 0; i < KS; ++i) {
-                score_mfma(nxt, kb[i % PFK], i);
+                score_mfma(nxt, kb[i % PFK], i, false);
                 if (i + PFK < KS) kb[i % PFK] = kld(kbs, rbs, kstep(i + PFK));
                 if (FP8 && !ROW && i == DR / 16 - 1) rope_to_latent_scale(nxt, 1.0f / sig_next);
                 softmax_slice(i);

@@ -1,0 +1,119 @@
+"""Wait states around the hand-written MFMAs of the decode kernels.
+
+The score chain of the MFMA decode is inline asm, so the compiler's hazard
+recognizer does not see it as an MFMA.  gfx950 needs 2 wait states between a
+VALU write of a VGPR and an MFMA that reads it (A, B or C operand); the kernel
+places an ``s_nop 1`` only where such a write can precede the chain.  This
+test compiles the kernels to gfx950 assembly and checks every inline-asm MFMA
+against the instructions before it: within 2 wait states (an ``s_nop N``
+counts N + 1, any other instruction 1) no VALU instruction may write one of
+its source registers, and no label may start the window (a jump into it could
+bring a VALU write the scan does not see) unless the MFMA has a nop.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "mla_latent_kv_07_amd", "csrc", "decode_mfma.hip")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+WINDOW = 2
+_REG = re.compile(r"v\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def regs(text):
+    out = set()
+    for m in _REG.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def instr(line):
+    """(mnemonic, operand text) of an instruction line, or None."""
+    t = line.split(";")[0].strip()
+    if not t or t.startswith(".") or t.endswith(":"):
+        return None
+    parts = t.split(None, 1)
+    return parts[0], (parts[1] if len(parts) > 1 else "")
+
+
+def check_asm(lines):
+    """Violations: (line number, mfma text, offending text)."""
+    bad = []
+    in_asm = False
+    for n, line in enumerate(lines):
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        ins = instr(line)
+        if not (in_asm and ins and ins[0].startswith("v_mfma")):
+            continue
+        ops = [o.strip() for o in ins[1].split(",")]
+        srcs = set()
+        for o in ops[1:]:
+            srcs |= regs(o)
+        waits = 0
+        k = n - 1
+        while k >= 0 and waits < WINDOW:
+            prev = lines[k]
+            ps = prev.strip()
+            if re.match(r"^[.\w]+:", ps):                 # a label: another path may enter here
+                bad.append((n + 1, s, "label " + ps.split(":")[0]))
+                break
+            p = instr(prev)
+            k -= 1
+            if p is None:
+                continue
+            mn, args = p
+            if mn == "s_nop":
+                waits += int(args.strip(), 0) + 1
+                continue
+            if mn.startswith("v_") and not mn.startswith("v_mfma"):
+                dst = args.split(",")[0]
+                if regs(dst) & srcs:
+                    bad.append((n + 1, s, ps))
+            waits += 1
+    return bad
+
+
+@pytest.fixture(scope="module")
+def decode_asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not found")
+    out = tmp_path_factory.mktemp("asm") / "decode_mfma.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.dirname(SRC), "-o", str(out), SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return open(out).read().split("\n")
+
+
+def test_checker_flags_a_planted_hazard():
+    planted = ["\tv_mul_f32_e32 v20, v1, v2", ";;#ASMSTART",
+               "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], v[0:15]", ";;#ASMEND"]
+    assert check_asm(planted)
+    covered = ["\tv_mul_f32_e32 v20, v1, v2", ";;#ASMSTART", "\ts_nop 1",
+               "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], v[0:15]", ";;#ASMEND"]
+    assert not check_asm(covered)
+    acc = ["\tv_mul_f32_e32 v3, v1, v2", "\ts_waitcnt lgkmcnt(0)", ";;#ASMSTART",
+           "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], v[0:15]", ";;#ASMEND"]
+    assert check_asm(acc)
+
+
+def test_score_chain_wait_states(decode_asm):
+    n_mfma = sum(1 for l in decode_asm if re.match(r"\s+v_mfma", l))
+    assert n_mfma > 100
+    bad = check_asm(decode_asm)
+    assert not bad, "\n".join(f"line {a}: {b} <- {c}" for a, b, c in bad[:20])
