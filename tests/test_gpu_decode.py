@@ -52,6 +52,17 @@ def test_decode_bf16_heavy_rows_and_nan_tails():
     compare_decode(d, o, lse)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8_e4m3", "fp8_e5m2", "fp8_e4m3_row"])
+def test_decode_reference_raise_every_format(kv):
+    # rows scaled x8 in later stages lift a row's stage max far above the
+    # reference taken from its first stage: the kernel recomputes those
+    # stages' scores and rescales the value sum (the rare path of the lazy
+    # max); few CUs give long items with many stages each
+    d = small(kv, seq=(900, 1300, 40), seed=21, heavy=0.03)
+    o, lse, _ = run_decode(d, cus=4)
+    compare_decode(d, o, lse)
+
+
 def test_decode_bf16_spec_pair_causal():
     # q_len = 2: 256 rows per sequence -> two row chunks per work item
     d = small("bf16", seq=(2, 3, 64, 65, 500), q_len=2, seed=10)
