@@ -101,36 +101,46 @@ typedef struct {
  */
 typedef struct {
     int32_t B, q_len, n_h, d_c;
-    int32_t num_items;      /* work items (workgroups per row chunk) */
-    int32_t row_chunks;     /* query-row chunks per sequence (128 rows each on the MFMA path) */
-    int32_t num_partials;   /* partial-result slots (sequences with >1 split) */
+    int32_t num_items;      /* work items: block ranges of one (sequence, row chunk) */
+    int32_t row_chunks;     /* query-row chunks per sequence (128 rows each) */
+    int32_t num_partials;   /* partial-result slots (items of split segments) */
     int32_t needs_combine;  /* 1 if mla_decode launches the LSE combine */
-    int32_t max_splits;     /* largest split count of any sequence */
-    int32_t blocks_per_item;/* target blocks per work item */
+    int32_t max_splits;     /* largest item count of any (sequence, row chunk) */
+    int32_t blocks_per_item;/* largest block count of any item */
     int32_t partial_dtype;  /* element type of the partial outputs in the workspace:
                                BF16 for the MFMA shapes (d_c 512, d_r 64, bf16/fp8
                                cache), F32 otherwise */
     int64_t plan_ints;      /* int32 entries of the device plan */
     int64_t workspace_bytes;/* partial-result workspace mla_decode needs */
+    int32_t grid_wgs;       /* workgroups of the MFMA decode launch (dispatch-table entries) */
 } mla_plan_t;
 
 /*
  * mla_decode_plan — host only, pure, makes no HIP call.
  *
- * Splits every sequence's ceil(seq_len/64) blocks into contiguous ranges so
- * that the total work fills `num_cus` compute units (per-item share
- * ceil(total_blocks * row_chunks / num_cus) blocks, at least 1), and lists
- * one work item {b, blk_begin, blk_end, slot} per range.
+ * Cuts the work, every (sequence, row chunk) segment of ceil(seq_len/64)
+ * blocks, into work items (contiguous block ranges) for `num_cus` compute
+ * units: the segments, in order, are packed into at most num_cus bins so
+ * that the largest bin cost is minimal (cost of an item = its 32-token
+ * stages + 6 for its prologue and epilogue; a bin takes whole segments while
+ * they fit, then whole blocks of the next), and the pieces of that packing
+ * are the items.  Items run one per workgroup; a dispatch table orders them
+ * longest first per XCD (workgroup k runs on XCD k % 8), by simulating
+ * list scheduling on num_cus/8 compute units per XCD.
  *
  * seq_lens_host [B]: tokens per sequence, counting the q_len query tokens
  *                    (each query token's own row is already in the cache).
  * plan_host:         int32 array of plan_capacity entries, or NULL to only
  *                    size the plan (info is filled either way).
- * Layout written: [num_items, B, row_chunks, num_partials],
- *                 items[num_items][4] = {b, blk_begin, blk_end, slot (-1 = final)},
- *                 split_off[B + 1] (partial slots of sequence b are
- *                 split_off[b] .. split_off[b+1]-1),
- *                 seq_flags[B] (1 = decode writes the final output directly).
+ * Layout written (int32): header[8] = {num_items, B, row_chunks,
+ *                 num_partials, grid_wgs, 0, 0, 0},
+ *                 items[num_items][4] = {b * row_chunks + chunk, blk_begin,
+ *                 blk_end, slot (-1 = final)},
+ *                 wg_item[grid_wgs] (item of each decode workgroup, -1 = none),
+ *                 split_off[B * row_chunks + 1] (partial slots of segment
+ *                 s = b * row_chunks + chunk are split_off[s] .. split_off[s+1]-1),
+ *                 seq_flags[B * row_chunks] (1 = decode writes the segment's
+ *                 final output directly).
  * The caller copies plan_host to device memory (plan_ints int32 entries)
  * and passes it to mla_decode with the same seq_lens.
  * Errors: INVALID_ARG for B < 1, q_len < 1, n_h < 1, negative lengths,

@@ -38,6 +38,7 @@ class Plan(ctypes.Structure):
         ("num_items", c_int32), ("row_chunks", c_int32), ("num_partials", c_int32),
         ("needs_combine", c_int32), ("max_splits", c_int32), ("blocks_per_item", c_int32),
         ("partial_dtype", c_int32), ("plan_ints", c_int64), ("workspace_bytes", c_int64),
+        ("grid_wgs", c_int32),
     ]
 
     def as_dict(self):

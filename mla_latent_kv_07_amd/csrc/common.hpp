@@ -28,26 +28,35 @@ struct DecodeArgs {
     int64_t num_pool_blocks;   // block ids are clamped to [0, num_pool_blocks)
     int32_t bt_stride, B, q_len, n_h, d_c, d_r;
     int32_t rows;              // q_len * n_h
-    int32_t num_items, row_chunks;
+    int32_t num_items, row_chunks, grid_wgs;
     float scale_log2;          // scale * log2(e)
     mla_dtype_t q_dtype, kv_dtype, partial_dtype;
 };
 
-// Plan layout offsets (int32 entries).
-__host__ __device__ inline int64_t plan_items_off() { return 4; }
-__host__ __device__ inline int64_t plan_split_off(int32_t num_items) { return 4 + 4 * (int64_t)num_items; }
-__host__ __device__ inline int64_t plan_flags_off(int32_t num_items, int32_t B) {
-    return plan_split_off(num_items) + B + 1;
+// Plan layout (int32 entries): header[8] = {num_items, B, row_chunks,
+// num_partials, grid_wgs, 0, 0, 0}; items[num_items][4] = {b * row_chunks +
+// chunk, blk_begin, blk_end, slot}; wg_item[grid_wgs] (the item of each MFMA
+// decode workgroup, -1 for none); split_off[B * row_chunks + 1];
+// seq_flags[B * row_chunks].
+constexpr int kPlanHeader = 8;
+__host__ __device__ inline int64_t plan_items_off() { return kPlanHeader; }
+__host__ __device__ inline int64_t plan_wg_off(int32_t num_items) { return kPlanHeader + 4 * (int64_t)num_items; }
+__host__ __device__ inline int64_t plan_split_off(int32_t num_items, int32_t grid_wgs) {
+    return plan_wg_off(num_items) + grid_wgs;
+}
+__host__ __device__ inline int64_t plan_flags_off(int32_t num_items, int32_t grid_wgs, int32_t num_seg) {
+    return plan_split_off(num_items, grid_wgs) + num_seg + 1;
 }
 
 hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 // MFMA decode of the DeepSeek-V2 shape (d_c 512, d_r 64, bf16 queries) for
 // every 16-bit and 8-bit cache format
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
+// split_off / seq_flags are indexed by b * ceil(rows / chunk_rows) + r / chunk_rows
 hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *lse_part,
                           const int32_t *split_off, const int32_t *seq_flags, int32_t B,
-                          int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dt, float *lse,
-                          hipStream_t s);
+                          int32_t rows, int32_t chunk_rows, int32_t d_c, void *o_lat,
+                          mla_dtype_t out_dt, float *lse, hipStream_t s);
 hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int32_t c_bytes,
                          int32_t r_bytes, bool split_rows, const int32_t *bt, int32_t bt_stride,
                          const int32_t *seq_lens, int32_t B, int32_t max_tokens, uint8_t *out,

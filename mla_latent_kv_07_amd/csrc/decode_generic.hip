@@ -90,11 +90,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 template <int KV, typename QT>
 __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
-    const int item = blockIdx.x / a.row_chunks;
-    const int chunk = blockIdx.x % a.row_chunks;
+    // one workgroup per work item: {sequence * row_chunks + chunk, blocks, slot}
+    const int item = blockIdx.x;
     if (item >= a.num_items) return;
     const int32_t *it = a.plan + plan_items_off() + 4 * item;
-    const int b = it[0], blk0 = it[1], blk1 = it[2], slot = it[3];
+    const int b = it[0] / a.row_chunks, chunk = it[0] % a.row_chunks;
+    const int blk0 = it[1], blk1 = it[2], slot = it[3];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int S = a.seq_lens[b];
     const QT *ql = (const QT *)a.q_lat;
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
 
 template <int KV>
 hipError_t launch_kv(const DecodeArgs &a, hipStream_t s) {
-    dim3 grid((unsigned)a.num_items * a.row_chunks);
+    dim3 grid((unsigned)a.num_items);
     if (a.q_dtype == MLA_DT_BF16)
         hipLaunchKernelGGL((decode_generic_kernel<KV, uint16_t>), grid, dim3(256), 0, s, a);
     else

@@ -233,19 +233,15 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     lds_u8 *smem = (lds_u8 *)smem_;
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
-    // workgroup -> (item, row chunk).  Workgroups are dealt to the 8 XCDs
-    // round robin (XCD = blockIdx % 8); XCD x takes the contiguous run
-    // x*G .. x*G+G-1 of the (item, chunk) units, so the splits of a sequence
-    // and the row chunks of an item share one L2: the queries of a sequence
-    // and each streamed block are fetched from HBM once.
-    const int rc = a.row_chunks;
-    const int G = gridDim.x / 8;
-    const int unit = (blockIdx.x & 7) * G + (blockIdx.x >> 3);
-    const int item = unit / rc, chunk = unit % rc;
-    if (item >= a.num_items) return;
+    // workgroup -> work item {sequence * row_chunks + chunk, blocks, slot},
+    // from the plan's dispatch table (longest items first on each XCD; -1
+    // pads the grid)
+    const int item = sload(a.plan, plan_wg_off(a.num_items) + blockIdx.x);
+    if (item < 0) return;
     const int64_t io = plan_items_off() + 4 * item;
-    const int b = sload(a.plan, io), blk0 = sload(a.plan, io + 1), blk1 = sload(a.plan, io + 2),
-              slot = sload(a.plan, io + 3);
+    const int sc = sload(a.plan, io);
+    const int b = sc / a.row_chunks, chunk = sc - b * a.row_chunks;
+    const int blk0 = sload(a.plan, io + 1), blk1 = sload(a.plan, io + 2), slot = sload(a.plan, io + 3);
     const int S = sload(a.seq_lens, b);
     const int nst = 2 * (blk1 - blk0);   // 32-token stages in this item
     // a stage holds tokens only if its first position is < S (the plan covers
@@ -857,9 +853,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
-    // a multiple of 8 workgroups, one per (item, row chunk) plus padding
-    const int units = a.num_items * a.row_chunks;
-    dim3 grid((unsigned)((units + 7) / 8) * 8);
+    // one workgroup per dispatch-table entry (a multiple of 8)
+    dim3 grid((unsigned)a.grid_wgs);
     switch (a.kv_dtype) {
     case MLA_DT_BF16: hipLaunchKernelGGL(decode_mfma_kernel<kv::Bf16>, grid, dim3(256), 0, s, a); break;
     case MLA_DT_F16: hipLaunchKernelGGL(decode_mfma_kernel<kv::F16>, grid, dim3(256), 0, s, a); break;

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <queue>
 #include <vector>
 
 #include "common.hpp"
@@ -113,46 +114,119 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     if (rows > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "q_len*n_h too large");
     int32_t row_chunks = (int32_t)((rows + kRowsPerChunk - 1) / kRowsPerChunk);
 
-    int64_t total_blocks = 0;
-    for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < B; ++b)
         if (seq_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %d < 0", b, seq_lens_host[b]);
-        total_blocks += (seq_lens_host[b] + kBlock - 1) / kBlock;
-    }
-    // Per-item share: spread all (block, row-chunk) work over the compute
-    // units.  The balanced share ceil(total / CUs) can leave more work units
-    // than compute units on ragged batches (each sequence rounds its split
-    // count up), which costs a second round of workgroups; take instead the
-    // smallest share whose units fit in one round, when one exists.
-    int64_t max_nb = 0;
-    for (int b = 0; b < B; ++b) max_nb = std::max<int64_t>(max_nb, (seq_lens_host[b] + kBlock - 1) / kBlock);
-    auto units_for = [&](int64_t sh) {
-        int64_t u = 0;
-        for (int b = 0; b < B; ++b) u += (seq_lens_host[b] + kBlock - 1) / kBlock / sh +
-                                         (((seq_lens_host[b] + kBlock - 1) / kBlock) % sh != 0);
-        return u * row_chunks;
-    };
-    int64_t share = std::max<int64_t>(1, (total_blocks * row_chunks + num_cus - 1) / num_cus);
-    if (max_nb > 0 && units_for(share) > num_cus && units_for(max_nb) <= num_cus) {
-        int64_t lo = share, hi = max_nb;   // units_for(hi) fits, units_for(lo) does not
-        while (hi - lo > 1) {
-            const int64_t mid = (lo + hi) / 2;
-            (units_for(mid) <= num_cus ? hi : lo) = mid;
-        }
-        share = hi;
-    }
 
-    int64_t num_items = 0, num_partials = 0;
-    int32_t max_splits = 0;
+    // Work list: every (sequence, row chunk) segment with at least one block,
+    // in order.  A work item is a block range of one segment, run by one
+    // workgroup.  Item sizes: pack the list into at most num_cus bins
+    // minimising the largest bin cost, each item costing its 32-token stages
+    // plus kItemCost for its query prologue and output epilogue (binary
+    // search on the budget M, greedy fill: a bin takes whole segments while
+    // they fit, then as many whole blocks of the next as fit); the pieces cut
+    // this way are the items.  Uniform batches get the even split (the
+    // measured 32 x 4096 batch: 8 items of 8 blocks per sequence); ragged
+    // ones get pieces sized so that short sequences fill the gaps left by
+    // long ones, instead of every compute unit waiting for the longest split.
+    struct Seg { int32_t sc; int64_t nb, st; };
+    std::vector<Seg> segs;
     bool any_empty = false;
     for (int b = 0; b < B; ++b) {
-        int64_t nb = (seq_lens_host[b] + kBlock - 1) / kBlock;
+        const int64_t nb = (seq_lens_host[b] + kBlock - 1) / kBlock;
+        const int64_t st = (seq_lens_host[b] + 31) / 32;
         if (nb == 0) { any_empty = true; continue; }
-        int64_t splits = (nb + share - 1) / share;
-        num_items += splits;
-        if (splits > 1) num_partials += splits;
-        max_splits = std::max<int32_t>(max_splits, (int32_t)splits);
+        for (int c = 0; c < row_chunks; ++c) segs.push_back({b * row_chunks + c, nb, st});
     }
+    constexpr int64_t kItemCost = 6;
+    auto piece_stages = [](const Seg &g, int64_t k0, int64_t k1) {
+        return std::min<int64_t>(2 * (k1 - k0), g.st - 2 * k0);
+    };
+    struct Piece { int32_t seg; int64_t k0, k1; };
+    // bins used at budget M (stops counting past `limit` unless pieces are wanted)
+    auto fill = [&](int64_t M, int64_t limit, std::vector<Piece> *out) {
+        int64_t bins = 0, load = 0;
+        bool open = false;
+        for (size_t i = 0; i < segs.size(); ++i) {
+            const Seg &g = segs[i];
+            int64_t k = 0;
+            while (k < g.nb) {
+                if (!open) {
+                    if (++bins > limit && !out) return bins;
+                    load = 0;
+                    open = true;
+                }
+                const int64_t rest = piece_stages(g, k, g.nb);
+                int64_t kk;
+                if (load + rest + kItemCost <= M) {
+                    kk = g.nb;
+                } else {
+                    kk = std::min<int64_t>(g.nb, k + std::max<int64_t>(0, (M - load - kItemCost) / 2));
+                    open = false;   // full after this piece
+                }
+                if (kk > k) {
+                    if (out) out->push_back({(int32_t)i, k, kk});
+                    load += piece_stages(g, k, kk) + kItemCost;
+                    k = kk;
+                }
+            }
+        }
+        return bins;
+    };
+    std::vector<Piece> pieces;
+    if (!segs.empty()) {
+        int64_t total = 0;
+        for (const Seg &g : segs) total += g.st + kItemCost;
+        int64_t lo = kItemCost + 1, hi = std::max<int64_t>(total, kItemCost + 2);   // fill(hi) uses one bin
+        while (hi - lo > 1) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            (fill(mid, num_cus, nullptr) <= num_cus ? hi : lo) = mid;
+        }
+        fill(hi, num_cus, &pieces);
+    }
+    const int64_t num_items = (int64_t)pieces.size();
+    const int64_t nseg = (int64_t)B * row_chunks;
     if (num_items > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "too many work items");
+
+    // Dispatch order of the MFMA decode.  Workgroup k runs on XCD k % 8, and
+    // each XCD starts its workgroups in order on whichever of its compute
+    // units frees first.  Simulate longest-first list scheduling of the
+    // items over the num_cus compute units (numbered XCD-major, ties to the
+    // lowest number, so that equal pieces of one sequence share an XCD and
+    // its L2) and give each XCD its items in simulated start order.
+    constexpr int kXcds = 8;
+    const int64_t per_x = (num_cus + kXcds - 1) / kXcds;
+    std::vector<std::vector<int32_t>> queue(kXcds);
+    {
+        std::vector<int64_t> cost(num_items);
+        for (int64_t i = 0; i < num_items; ++i)
+            cost[i] = piece_stages(segs[pieces[i].seg], pieces[i].k0, pieces[i].k1) + kItemCost;
+        std::vector<int32_t> order(num_items);
+        for (int64_t i = 0; i < num_items; ++i) order[i] = (int32_t)i;
+        std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+        typedef std::pair<int64_t, int32_t> Slot;   // (free at, compute unit)
+        std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> free_at;
+        for (int32_t c = 0; c < num_cus; ++c) free_at.push({0, c});
+        for (int32_t i : order) {
+            const Slot u = free_at.top();
+            free_at.pop();
+            queue[u.second / per_x].push_back(i);
+            free_at.push({u.first + cost[i], u.second});
+        }
+    }
+    size_t longest = 0;
+    for (const auto &q : queue) longest = std::max(longest, q.size());
+    const int64_t grid_wgs = kXcds * (int64_t)longest;
+
+    // pieces per segment -> partial slots (segments split more than once)
+    std::vector<int32_t> count(segs.size(), 0);
+    for (const Piece &q : pieces) ++count[q.seg];
+    int64_t num_partials = 0, max_blocks = 0;
+    int32_t max_splits = 0;
+    for (size_t i = 0; i < segs.size(); ++i) {
+        if (count[i] > 1) num_partials += count[i];
+        max_splits = std::max(max_splits, count[i]);
+    }
+    for (const Piece &q : pieces) max_blocks = std::max<int64_t>(max_blocks, q.k1 - q.k0);
 
     info->B = B; info->q_len = q_len; info->n_h = n_h; info->d_c = d_c;
     info->num_items = (int32_t)num_items;
@@ -160,9 +234,10 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     info->num_partials = (int32_t)num_partials;
     info->needs_combine = (num_partials > 0 || any_empty) ? 1 : 0;
     info->max_splits = max_splits;
-    info->blocks_per_item = (int32_t)share;
+    info->blocks_per_item = (int32_t)max_blocks;
     info->partial_dtype = is_fast_shape(kv_dtype, d_c, d_r) ? MLA_DT_BF16 : MLA_DT_F32;
-    info->plan_ints = 4 + 4 * num_items + 2 * (int64_t)B + 1;
+    info->grid_wgs = (int32_t)grid_wgs;
+    info->plan_ints = plan_flags_off((int32_t)num_items, (int32_t)grid_wgs, (int32_t)nseg) + nseg;
     int64_t o_bytes = num_partials * rows * d_c * elem_bytes((mla_dtype_t)info->partial_dtype);
     int64_t o_bytes_al = (o_bytes + 255) / 256 * 256;
     info->workspace_bytes = num_partials ? o_bytes_al + num_partials * rows * 4 : 0;
@@ -172,28 +247,45 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
         return fail(MLA_ERR_INVALID_ARG, "plan capacity %lld < %lld", (long long)plan_capacity, (long long)info->plan_ints);
 
     int32_t *items = plan_host + plan_items_off();
-    int32_t *split_off = plan_host + plan_split_off((int32_t)num_items);
-    int32_t *flags = plan_host + plan_flags_off((int32_t)num_items, B);
+    int32_t *wg_item = plan_host + plan_wg_off((int32_t)num_items);
+    int32_t *split_off = plan_host + plan_split_off((int32_t)num_items, (int32_t)grid_wgs);
+    int32_t *flags = plan_host + plan_flags_off((int32_t)num_items, (int32_t)grid_wgs, (int32_t)nseg);
+    for (int k = 0; k < kPlanHeader; ++k) plan_host[k] = 0;
     plan_host[0] = (int32_t)num_items;
     plan_host[1] = B;
     plan_host[2] = row_chunks;
     plan_host[3] = (int32_t)num_partials;
-    int64_t it = 0, slot = 0;
-    for (int b = 0; b < B; ++b) {
-        int64_t nb = (seq_lens_host[b] + kBlock - 1) / kBlock;
-        split_off[b] = (int32_t)slot;
-        if (nb == 0) { flags[b] = 0; continue; }
-        int64_t splits = (nb + share - 1) / share;
-        flags[b] = splits == 1 ? 1 : 0;
-        for (int64_t k = 0; k < splits; ++k) {
-            items[4 * it + 0] = b;
-            items[4 * it + 1] = (int32_t)(k * nb / splits);
-            items[4 * it + 2] = (int32_t)((k + 1) * nb / splits);
-            items[4 * it + 3] = splits == 1 ? -1 : (int32_t)(slot++);
-            ++it;
+    plan_host[4] = (int32_t)grid_wgs;
+    // slots: the pieces of a split segment, in order
+    std::vector<int32_t> first_slot(segs.size(), -1);
+    {
+        int64_t slot = 0;
+        size_t i = 0;
+        for (int64_t sc = 0; sc < nseg; ++sc) {
+            split_off[sc] = (int32_t)slot;
+            flags[sc] = 0;
+            if (i < segs.size() && segs[i].sc == sc) {
+                if (count[i] == 1) flags[sc] = 1;
+                else { first_slot[i] = (int32_t)slot; slot += count[i]; }
+                ++i;
+            }
         }
+        split_off[nseg] = (int32_t)slot;
     }
-    split_off[B] = (int32_t)slot;
+    std::vector<int32_t> seen(segs.size(), 0);
+    for (int64_t it = 0; it < num_items; ++it) {
+        const Piece &q = pieces[it];
+        items[4 * it + 0] = segs[q.seg].sc;
+        items[4 * it + 1] = (int32_t)q.k0;
+        items[4 * it + 2] = (int32_t)q.k1;
+        items[4 * it + 3] = count[q.seg] == 1 ? -1 : first_slot[q.seg] + seen[q.seg];
+        ++seen[q.seg];
+    }
+    for (int64_t k = 0; k < grid_wgs; ++k) {
+        const auto &q = queue[k % kXcds];
+        const size_t j = (size_t)(k / kXcds);
+        wg_item[k] = j < q.size() ? q[j] : -1;
+    }
     return ok();
 }
 
@@ -244,7 +336,7 @@ mla_status_t prepare_decode(const void *q_lat, const void *q_rope, mla_dtype_t q
     a.num_pool_blocks = cache->num_blocks;
     a.bt_stride = bt_stride; a.B = B; a.q_len = q_len; a.n_h = n_h;
     a.d_c = cache->d_c; a.d_r = cache->d_r; a.rows = (int32_t)rows;
-    a.num_items = plan->num_items; a.row_chunks = plan->row_chunks;
+    a.num_items = plan->num_items; a.row_chunks = plan->row_chunks; a.grid_wgs = plan->grid_wgs;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q_dtype = q_dtype; a.kv_dtype = cache->kv_dtype;
     a.partial_dtype = (mla_dtype_t)plan->partial_dtype;
@@ -270,10 +362,11 @@ mla_status_t finish_decode(const mla_plan_t *plan, const int32_t *plan_dev, void
         o_part = workspace;
         lse_part = (float *)((char *)workspace + (o_bytes + 255) / 256 * 256);
     }
-    const int32_t *split_off = plan_dev + plan_split_off(plan->num_items);
-    const int32_t *flags = plan_dev + plan_flags_off(plan->num_items, plan->B);
+    const int32_t nseg = plan->B * plan->row_chunks;
+    const int32_t *split_off = plan_dev + plan_split_off(plan->num_items, plan->grid_wgs);
+    const int32_t *flags = plan_dev + plan_flags_off(plan->num_items, plan->grid_wgs, nseg);
     return hip_status(launch_combine(o_part, pdt, lse_part, split_off, flags, plan->B,
-                                     (int32_t)rows, plan->d_c, o_lat, out_dtype, lse, s),
+                                     (int32_t)rows, kRowsPerChunk, plan->d_c, o_lat, out_dtype, lse, s),
                       "combine launch");
 }
 
@@ -338,7 +431,7 @@ mla_status_t mla_combine_lse(const float *o_part, const float *lse_part,
     if (out_dtype != MLA_DT_F32 && out_dtype != MLA_DT_BF16)
         return fail(MLA_ERR_UNSUPPORTED, "out dtype %d unsupported", (int)out_dtype);
     return hip_status(launch_combine(o_part, MLA_DT_F32, lse_part, split_off, seq_flags, B, rows,
-                                     d_c, o_lat, out_dtype, lse, (hipStream_t)stream),
+                                     rows, d_c, o_lat, out_dtype, lse, (hipStream_t)stream),
                       "combine launch");
 }
 

@@ -70,15 +70,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const PartT *__restrict__ 
                                                       const float *__restrict__ lse_part,
                                                       const int32_t *__restrict__ split_off,
                                                       const int32_t *__restrict__ seq_flags,
-                                                      int32_t rows, int32_t d_c,
+                                                      int32_t rows, int32_t chunk_rows, int32_t d_c,
                                                       OutT *__restrict__ o_lat,
                                                       float *__restrict__ lse) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.y;
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
-    if (seq_flags && seq_flags[b] == 1) return;
-    const int k0 = split_off[b], n = split_off[b + 1] - k0;
+    // the split list of the row's (sequence, row chunk)
+    const int sc = b * ((rows + chunk_rows - 1) / chunk_rows) + r / chunk_rows;
+    if (seq_flags && seq_flags[sc] == 1) return;
+    const int k0 = split_off[sc], n = split_off[sc + 1] - k0;
     const int64_t out_row = (int64_t)b * rows + r;
     // running max over all splits (in chunks of 64 lanes)
     float m = -INFINITY;
@@ -149,15 +151,18 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
                                                          const float *__restrict__ lse_part,
                                                          const int32_t *__restrict__ split_off,
                                                          const int32_t *__restrict__ seq_flags,
-                                                         int32_t rows, OutT *__restrict__ o_lat,
+                                                         int32_t rows, int32_t chunk_rows,
+                                                         OutT *__restrict__ o_lat,
                                                          float *__restrict__ lse) {
     constexpr int U = 8;
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.y;
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
-    if (seq_flags && seq_flags[b] == 1) return;
-    const int k0 = split_off[b], n = split_off[b + 1] - k0;
+    // the split list of the row's (sequence, row chunk)
+    const int sc = b * ((rows + chunk_rows - 1) / chunk_rows) + r / chunk_rows;
+    if (seq_flags && seq_flags[sc] == 1) return;
+    const int k0 = split_off[sc], n = split_off[sc + 1] - k0;
     const int64_t out_row = (int64_t)b * rows + r;
     const uint16_t *src0 = o_part + ((int64_t)k0 * rows + r) * 512 + lane * 8;
     const int64_t split_stride = (int64_t)rows * 512;
@@ -232,35 +237,35 @@ hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int32_t c_byt
 
 hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *lse_part,
                           const int32_t *split_off, const int32_t *seq_flags, int32_t B,
-                          int32_t rows, int32_t d_c, void *o_lat, mla_dtype_t out_dt, float *lse,
-                          hipStream_t s) {
+                          int32_t rows, int32_t chunk_rows, int32_t d_c, void *o_lat,
+                          mla_dtype_t out_dt, float *lse, hipStream_t s) {
     dim3 grid((rows + 3) / 4, B);
     if (part_dt == MLA_DT_BF16 && d_c == 512) {
         if (out_dt == MLA_DT_BF16)
             hipLaunchKernelGGL(combine512_kernel<uint16_t>, grid, dim3(256), 0, s,
                                (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows,
-                               (uint16_t *)o_lat, lse);
+                               chunk_rows, (uint16_t *)o_lat, lse);
         else
             hipLaunchKernelGGL(combine512_kernel<float>, grid, dim3(256), 0, s,
                                (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows,
-                               (float *)o_lat, lse);
+                               chunk_rows, (float *)o_lat, lse);
     } else if (part_dt == MLA_DT_BF16) {
         if (out_dt == MLA_DT_BF16)
             hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s,
-                               (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, d_c,
+                               (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, chunk_rows, d_c,
                                (uint16_t *)o_lat, lse);
         else
             hipLaunchKernelGGL((combine_kernel<uint16_t, float>), grid, dim3(256), 0, s,
-                               (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, d_c,
+                               (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, chunk_rows, d_c,
                                (float *)o_lat, lse);
     } else {
         if (out_dt == MLA_DT_BF16)
             hipLaunchKernelGGL((combine_kernel<float, uint16_t>), grid, dim3(256), 0, s,
-                               (const float *)o_part, lse_part, split_off, seq_flags, rows, d_c,
+                               (const float *)o_part, lse_part, split_off, seq_flags, rows, chunk_rows, d_c,
                                (uint16_t *)o_lat, lse);
         else
             hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(256), 0, s,
-                               (const float *)o_part, lse_part, split_off, seq_flags, rows, d_c,
+                               (const float *)o_part, lse_part, split_off, seq_flags, rows, chunk_rows, d_c,
                                (float *)o_lat, lse);
     }
     return hipGetLastError();

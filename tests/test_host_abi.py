@@ -40,11 +40,36 @@ def plan(seq, q_len=1, n_h=128, d_c=512, d_r=64, kv=L.DT_BF16, cus=256):
 
 
 def parse(info, p):
-    n = info.num_items
-    items = p[4:4 + 4 * n].view(n, 4).tolist()
-    split_off = p[4 + 4 * n:4 + 4 * n + info.B + 1].tolist()
-    flags = p[4 + 4 * n + info.B + 1:].tolist()
-    return items, split_off, flags
+    n, g, nseg = info.num_items, info.grid_wgs, info.B * info.row_chunks
+    items = p[8:8 + 4 * n].view(n, 4).tolist()
+    wg = p[8 + 4 * n:8 + 4 * n + g].tolist()
+    split_off = p[8 + 4 * n + g:8 + 4 * n + g + nseg + 1].tolist()
+    flags = p[8 + 4 * n + g + nseg + 1:].tolist()
+    assert len(flags) == nseg
+    return items, wg, split_off, flags
+
+
+def item_cost(seq, rc, it):
+    """32-token stages of an item + 6 for its prologue and epilogue (the planner's model)"""
+    sc, lo, hi, _ = it
+    S = seq[sc // rc]
+    return min(2 * (hi - lo), (S - 64 * lo + 31) // 32) + 6
+
+
+def dispatch_makespan(seq, info, items, wg, cus=256):
+    """Workgroup k runs on XCD k % 8; each XCD starts its items in table order
+    on whichever of its cus/8 compute units frees first."""
+    import heapq
+    m = -(-cus // 8)
+    worst = 0
+    for x in range(8):
+        free = [0] * m
+        for k in range(x, len(wg), 8):
+            if wg[k] >= 0:
+                t = heapq.heappop(free)
+                heapq.heappush(free, t + item_cost(seq, info.row_chunks, items[wg[k]]))
+        worst = max(worst, max(free))
+    return worst
 
 
 @pytest.mark.parametrize("seq,q_len,cus", [
@@ -57,31 +82,41 @@ def parse(info, p):
 ])
 def test_plan_covers_each_block_once(seq, q_len, cus):
     info, p = plan(seq, q_len=q_len, cus=cus)
-    items, split_off, flags = parse(info, p)
-    assert p[0] == info.num_items and p[1] == len(seq) and p[2] == info.row_chunks
-    assert info.row_chunks == (q_len * 128 + 127) // 128
+    items, wg, split_off, flags = parse(info, p)
+    rc = info.row_chunks
+    assert p[0] == info.num_items and p[1] == len(seq) and p[2] == rc and p[4] == info.grid_wgs
+    assert rc == (q_len * 128 + 127) // 128
+    # every item appears once in the dispatch table; padding is -1
+    assert info.grid_wgs % 8 == 0
+    assert sorted(k for k in wg if k >= 0) == list(range(info.num_items))
+    assert all(k == -1 for k in wg if k < 0)
     seen = {}
     slots = set()
-    for b, lo, hi, slot in items:
+    for sc, lo, hi, slot in items:
+        b = sc // rc
+        assert 0 <= sc < len(seq) * rc
         assert 0 <= lo < hi <= (seq[b] + 63) // 64
         assert hi - lo <= info.blocks_per_item
         for blk in range(lo, hi):
-            assert (b, blk) not in seen
-            seen[(b, blk)] = slot
+            assert (sc, blk) not in seen
+            seen[(sc, blk)] = slot
         if slot >= 0:
-            assert split_off[b] <= slot < split_off[b + 1]
+            assert split_off[sc] <= slot < split_off[sc + 1]
             slots.add(slot)
     for b, S in enumerate(seq):
         nb = (S + 63) // 64
-        assert all((b, k) in seen for k in range(nb))
-        n_items = sum(1 for it in items if it[0] == b)
-        if nb == 0:
-            assert flags[b] == 0 and split_off[b + 1] == split_off[b]
-        elif n_items == 1:
-            assert flags[b] == 1 and split_off[b + 1] == split_off[b]
-        else:
-            assert flags[b] == 0 and split_off[b + 1] - split_off[b] == n_items
+        for c in range(rc):
+            sc = b * rc + c
+            assert all((sc, k) in seen for k in range(nb))
+            n_items = sum(1 for it in items if it[0] == sc)
+            if nb == 0:
+                assert flags[sc] == 0 and split_off[sc + 1] == split_off[sc]
+            elif n_items == 1:
+                assert flags[sc] == 1 and split_off[sc + 1] == split_off[sc]
+            else:
+                assert flags[sc] == 0 and split_off[sc + 1] - split_off[sc] == n_items
     assert slots == set(range(info.num_partials))
+    assert info.max_splits == max([sum(1 for it in items if it[0] == sc) for sc in range(len(seq) * rc)] + [0])
     assert info.needs_combine == int(info.num_partials > 0 or 0 in seq)
     rows = q_len * 128
     assert info.partial_dtype == L.DT_BF16          # MFMA shape: bf16 partials
@@ -190,21 +225,37 @@ def test_cache_bytes():
     assert lib().mla_cache_bytes(ctypes.byref(_desc(block_size=32))) == 0
 
 
-def test_plan_fits_one_round_on_ragged_batches():
-    """Ragged batches: the share is the smallest whose (item, row chunk) units
-    fit in one round of workgroups, so no compute unit runs two."""
+def test_plan_balances_ragged_batches():
+    """Ragged batches: with the dispatch table run as the hardware runs it
+    (workgroup k on XCD k % 8, each XCD starting its workgroups in order on
+    its first free compute unit), the busiest compute unit carries little
+    more than an even share of the stages plus one item's overhead, where
+    one item per sequence split evenly over the compute units would leave
+    many of them idle behind the longest split."""
     import numpy as np
     rng = np.random.default_rng(7)
     for B, lo, hi, q_len, cus in [(64, 1024, 8192, 2, 256), (128, 1, 32768, 1, 256), (4, 65536, 131072, 1, 256),
-                                  (7, 1, 5000, 1, 16)]:
+                                  (7, 1, 5000, 1, 16), (300, 1, 3000, 1, 256)]:
         seq = rng.integers(lo, hi + 1, size=B).tolist()
         info, p = plan(seq, q_len=q_len, cus=cus)
-        nb = [(S + 63) // 64 for S in seq]
-        units = lambda sh: sum(-(-n // sh) for n in nb) * info.row_chunks
-        assert info.num_items * info.row_chunks == units(info.blocks_per_item)
-        assert units(info.blocks_per_item) <= cus
-        if info.blocks_per_item > 1:
-            assert units(info.blocks_per_item - 1) > cus
+        items, wg, _, _ = parse(info, p)
+        rc = info.row_chunks
+        stages = sum((S + 31) // 32 for S in seq) * rc
+        even = stages / cus
+        mk = dispatch_makespan(seq, info, items, wg, cus)
+        assert mk <= 1.12 * even + 2 * 6 + 2, (B, mk, even)
+
+
+def test_plan_keeps_uniform_batches_whole():
+    """A uniform batch splits each sequence evenly, one item per compute unit,
+    and a sequence's pieces sit on one XCD (consecutive table entries of
+    one XCD's queue)."""
+    info, p = plan([4096] * 32)
+    items, wg, _, _ = parse(info, p)
+    assert info.num_items == 256 and info.grid_wgs == 256
+    for x in range(8):
+        seqs = {items[wg[k]][0] for k in range(x, 256, 8)}
+        assert len(seqs) == 4     # 32 pieces of 4 sequences
 
 
 def test_rope_freqs_match_the_oracle():
