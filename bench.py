@@ -146,9 +146,59 @@ def cpu_baseline(d, cache_bytes, max_rows=4096):
     run(rows)
     dt = time.perf_counter() - t0
     full = dt * n_rows / rows.size
-    return {"value": round(cache_bytes / full / 1e9, 4), "unit": "GB/s", "cores": O.threads(),
-            "kind": "oracle",
-            "sample": f"{rows.size} of {n_rows} query rows ({dt:.2f} s), scaled to the whole batch"}
+    out = {"value": round(cache_bytes / full / 1e9, 4), "unit": "GB/s", "cores": O.threads(),
+           "kind": "oracle",
+           "sample": f"{rows.size} of {n_rows} query rows ({dt:.2f} s), scaled to the whole batch",
+           "cpu_model": cpu_model()}
+    if wl.kv_dtype in ("bf16", "f16", "f32"):
+        out["fast_cpu_context"] = torch_cpu_context(d, cache_bytes, O)
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def torch_cpu_context(d, cache_bytes, O, max_seqs=8):
+    """Context line, not a baseline: the same decode in plain torch fp32 on
+    the host's cores (matmul, softmax, matmul per sequence over its gathered
+    latent rows), on the first max_seqs sequences, scaled to the batch."""
+    import numpy as np
+    import torch as T
+    wl = d.wl
+    fmt = {"f32": O.FMT_F32, "bf16": O.FMT_BF16, "f16": O.FMT_F16}[wl.kv_dtype]
+    nb = min(max_seqs, wl.B)
+    S_max = int(d.cache.seq_lens[:nb].max())
+    raw = O.gather(d.cache.pool, fmt, wl.d_c, wl.d_r, d.cache.block_table[:nb], d.cache.seq_lens[:nb], S_max)
+    dt_np = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16}[wl.kv_dtype]
+    rows = raw.view(dt_np).reshape(nb, S_max, wl.d_c + wl.d_r)
+    if wl.kv_dtype == "bf16":
+        kv = T.from_numpy(rows.astype(np.uint32) << 16).view(T.float32)
+    else:
+        kv = T.from_numpy(rows.astype(np.float32))
+    T.set_num_threads(O.threads())
+    q = T.cat([d.q_lat.float(), d.q_rope.float()], dim=-1).view(wl.B, wl.q_len * wl.n_h, -1)
+    def run():
+        for b in range(nb):
+            S = int(d.cache.seq_lens[b])
+            k = kv[b, :S]
+            s = (q[b] @ k.T) * d.scale
+            o = T.softmax(s, dim=-1) @ k[:, :wl.d_c]
+        return o
+    run()
+    t0 = time.perf_counter()
+    run()
+    dt = time.perf_counter() - t0
+    tokens = float(d.cache.seq_lens[:nb].sum())
+    full = dt * float(d.cache.seq_lens.sum()) / tokens
+    return {"value": round(cache_bytes / full / 1e9, 4), "unit": "GB/s", "kind": "torch fp32 matmul/softmax",
+            "sample": f"{nb} of {wl.B} sequences ({dt:.2f} s), scaled to the whole batch (no causal mask)"}
 
 
 def visible_flops(seq_lens, q_len, n_h, d_c, d_r) -> float:
