@@ -53,6 +53,7 @@ struct GemmArgs {
     int32_t M, N, K;     // K a multiple of 64; N a multiple of 8
     int32_t splits;      // z = b * splits + s; split s covers the 64-wide stages
                          // [s nk / splits, (s + 1) nk / splits) of the nk = K / 64
+    int32_t ntiles;      // column tiles per workgroup, in turn (blockIdx.x * ntiles + j)
 };
 
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const void *src) {
@@ -69,7 +70,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int z = blockIdx.z, b = z / g.splits, s = z % g.splits;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int m0 = blockIdx.y * BM;
+    for (int tj = 0; tj < g.ntiles; ++tj) {
+    const int n0 = (blockIdx.x * g.ntiles + tj) * BN;
+    if (n0 >= g.N) break;
+    if (tj > 0) __syncthreads();   // the previous tile's epilogue is done with the LDS
     const int nk_all = g.K / BK;
     const int st0 = (int)((int64_t)s * nk_all / g.splits), nk = (int)((int64_t)(s + 1) * nk_all / g.splits) - st0;
     const int64_t k_begin = (int64_t)st0 * BK;
@@ -214,6 +219,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs g) {
             *(uint4 *)((uint16_t *)g.C + off) = pk;
         }
     }
+    }   // column tiles
 }
 
 // out[m][n] = bf16(sum over splits of ws[s][m][n]), 8 consecutive n per thread
@@ -239,7 +245,8 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float *__restrict_
 
 template <bool B_KCONTIG, bool OUT_F32>
 hipError_t launch_gemm(const GemmArgs &g, int batch, hipStream_t st) {
-    dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)(batch * g.splits));
+    const int tiles = (g.N + BN - 1) / BN, nt = g.ntiles < 1 ? 1 : g.ntiles;
+    dim3 grid((unsigned)((tiles + nt - 1) / nt), (unsigned)((g.M + BM - 1) / BM), (unsigned)(batch * g.splits));
     hipLaunchKernelGGL((gemm_bf16_kernel<B_KCONTIG, OUT_F32>), grid, dim3(256), 0, st, g);
     return hipGetLastError();
 }
@@ -268,7 +275,7 @@ hipError_t launch_gemm_nn_f32(const void *A, int64_t lda, const void *B, int64_t
     g.A = (const uint16_t *)A; g.lda = lda; g.bsa = 0;
     g.B = (const uint16_t *)B; g.ldb = ldb; g.bsb = 0;
     g.C = ws; g.ldc = N; g.bsc = 0; g.css = (int64_t)M * N;
-    g.M = M; g.N = N; g.K = K; g.splits = splits;
+    g.M = M; g.N = N; g.K = K; g.splits = splits; g.ntiles = 1;
     return launch_gemm<false, true>(g, 1, s);
 }
 
@@ -279,7 +286,7 @@ hipError_t launch_gemm_nn_bf16(const void *A, int64_t lda, const void *B, int64_
     g.A = (const uint16_t *)A; g.lda = lda; g.bsa = 0;
     g.B = (const uint16_t *)B; g.ldb = ldb; g.bsb = 0;
     g.C = C; g.ldc = ldc; g.bsc = 0; g.css = 0;
-    g.M = M; g.N = N; g.K = K; g.splits = 1;
+    g.M = M; g.N = N; g.K = K; g.splits = 1; g.ntiles = 1;
     return launch_gemm<false, false>(g, 1, s);
 }
 
@@ -305,6 +312,11 @@ hipError_t launch_absorb_q_mfma(const void *q_nope, int64_t ld_q, const void *w_
     g.B = (const uint16_t *)w_uk;   g.ldb = d_nope; g.bsb = (int64_t)d_c * d_nope;
     g.C = q_lat; g.ldc = (int64_t)n_h * d_c; g.bsc = d_c; g.css = 0;
     g.M = T; g.N = d_c; g.K = d_nope; g.splits = 1;
+    // K = d_nope is two stages: one 128 x 128 tile per workgroup would take
+    // two rounds of short workgroups; two tiles each (the query tile
+    // re-read from L2) keep the heads within one round
+    const int tiles = (d_c + BN - 1) / BN;
+    g.ntiles = (int64_t)tiles * n_h > 256 && tiles > 1 ? 2 : 1;
     return launch_gemm<true, false>(g, n_h, s);
 }
 
@@ -326,7 +338,7 @@ hipError_t launch_absorb_out_mfma(const void *o_lat, const void *w_uv, const voi
     g1.A = (const uint16_t *)o_lat; g1.lda = (int64_t)n_h * d_c; g1.bsa = d_c;
     g1.B = (const uint16_t *)w_uv;  g1.ldb = d_v; g1.bsb = (int64_t)d_c * d_v;
     g1.C = u_ws; g1.ldc = (int64_t)n_h * d_v; g1.bsc = d_v; g1.css = 0;
-    g1.M = T; g1.N = d_v; g1.K = d_c; g1.splits = 1;
+    g1.M = T; g1.N = d_v; g1.K = d_c; g1.splits = 1; g1.ntiles = 1;
     hipError_t e = launch_gemm<false, false>(g1, n_h, s);
     if (e != hipSuccess) return e;
     // out = u . W_O over K = n_h d_v, split into fp32 partials, then summed
@@ -336,7 +348,7 @@ hipError_t launch_absorb_out_mfma(const void *o_lat, const void *w_uv, const voi
     g2.A = (const uint16_t *)u_ws; g2.lda = K; g2.bsa = 0;
     g2.B = (const uint16_t *)w_o;  g2.ldb = d_model; g2.bsb = 0;
     g2.C = ws; g2.ldc = d_model; g2.bsc = 0; g2.css = (int64_t)T * d_model;
-    g2.M = T; g2.N = d_model; g2.K = K; g2.splits = sp;
+    g2.M = T; g2.N = d_model; g2.K = K; g2.splits = sp; g2.ntiles = 1;
     e = launch_gemm<false, true>(g2, 1, s);
     if (e != hipSuccess) return e;
     const int64_t n8 = (int64_t)T * d_model / 8;
