@@ -63,6 +63,25 @@ def test_decode_reference_raise_every_format(kv):
     compare_decode(d, o, lse)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_decode_many_ragged_sequences_dispatch_table(kv):
+    # 300 sequences of 1-700 tokens with q_len 2 (two row chunks each): the
+    # plan holds far more items than compute units, mixes split and whole
+    # (sequence, row chunk) segments, and the dispatch table gives every XCD
+    # a long queue; empty sequences and one-token ones included
+    import numpy as np
+    rng = np.random.default_rng(31)
+    seq = rng.integers(1, 701, size=300)
+    seq[[5, 77, 200]] = 0
+    seq[[6, 78]] = 1
+    d = small(kv, seq=tuple(int(x) for x in seq), q_len=2, seed=32)
+    o, lse, dec = run_decode(d)
+    assert dec.info.num_items > 256 and dec.info.grid_wgs > 256 and dec.info.row_chunks == 2
+    say(f"  items {dec.info.num_items}, grid {dec.info.grid_wgs}, partial slots {dec.info.num_partials}")
+    rows = np.sort(np.random.default_rng(33).choice(300 * 256, size=3000, replace=False))
+    compare_decode(d, o, lse, rows=rows)
+
+
 def test_decode_bf16_spec_pair_causal():
     # q_len = 2: 256 rows per sequence -> two row chunks per work item
     d = small("bf16", seq=(2, 3, 64, 65, 500), q_len=2, seed=10)
