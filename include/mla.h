@@ -83,7 +83,27 @@ typedef enum {
  * Blocks are 256-byte aligned when base is (block bytes are multiples of 256
  * for the instantiated dims).  Rows past a sequence's length may hold
  * anything, including NaN: no result depends on them.
+ *
+ * flags (0 or MLA_CACHE_FP8_EXACT) choose the arithmetic of mla_decode over
+ * an FP8_E4M3 cache at d_c = 512, d_r = 64 with BF16 queries.  The pages fix
+ * the fp8 storage, not this arithmetic.
+ *   0 (default): the codes go into 8-bit MFMAs as stored.  Each query row
+ *     becomes two e4m3 terms, q~ ~= sigma_q (h + l/16) with
+ *     sigma_q = max|q~| / 448.  The probabilities become two e4m3 terms of
+ *     y = p 2^5 mant(|block scale|), y ~= h + l/16; the exponent of the block
+ *     scale rides on the value MFMA's E8M0 operand scale.  The rotary part
+ *     stays on bf16.
+ *   MLA_CACHE_FP8_EXACT: codes are decoded exactly to bf16, and bf16 MFMAs
+ *     run the 16-bit pipeline (probabilities rounded to bf16).
+ * Both keep the error within a few 1e-3 of each output row's norm on N(0,1)
+ * data (two e4m3 terms carry q~ and P to ~2^-8).  The 8-bit path's score
+ * error grows with the logits: a block whose scale dwarfs its data's
+ * absmax / 448 (logits far beyond the rest) is better decoded exactly.
+ * Block scales must be finite (any sign; zero allowed).  Every other format
+ * and shape ignores flags.
  */
+#define MLA_CACHE_FP8_EXACT 1
+
 typedef struct {
     const void *base;
     const float *block_scales;  /* FP8_E4M3 only, else NULL */
@@ -92,6 +112,7 @@ typedef struct {
     int32_t d_c;                /* latent width */
     int32_t d_r;                /* rotary key width */
     mla_dtype_t kv_dtype;
+    int32_t flags;              /* 0 or MLA_CACHE_FP8_EXACT (see above) */
 } mla_cache_desc_t;
 
 /*

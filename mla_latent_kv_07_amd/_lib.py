@@ -16,6 +16,7 @@ MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR_WORKSPA
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGN", 4: "WORKSPACE", 5: "HIP"}
 DT_F32, DT_BF16, DT_FP8_E4M3, DT_F16, DT_FP8_E5M2, DT_FP8_E4M3_ROW = 0, 1, 2, 3, 4, 5
 BLOCK_SIZE = 64
+CACHE_FP8_EXACT = 1   # mla_cache_desc_t.flags: exact fp8 decode on 16-bit MFMAs
 
 c_int32, c_int64, c_void_p, c_float = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
 
@@ -29,6 +30,7 @@ class CacheDesc(ctypes.Structure):
         ("d_c", c_int32),
         ("d_r", c_int32),
         ("kv_dtype", c_int32),
+        ("flags", c_int32),
     ]
 
 

@@ -40,6 +40,9 @@ class DeviceCache:
     kv_dtype: str
     d_c: int
     d_r: int
+    # e4m3 latents: decode the codes exactly on 16-bit MFMAs instead of the
+    # 8-bit MFMA path (mla_cache_desc_t.flags)
+    fp8_exact: bool = False
 
     @property
     def num_blocks(self) -> int:
@@ -48,7 +51,8 @@ class DeviceCache:
     def desc(self) -> L.CacheDesc:
         return L.CacheDesc(self.pool.data_ptr(),
                            None if self.block_scales is None else self.block_scales.data_ptr(),
-                           self.num_blocks, L.BLOCK_SIZE, self.d_c, self.d_r, _KV[self.kv_dtype])
+                           self.num_blocks, L.BLOCK_SIZE, self.d_c, self.d_r, _KV[self.kv_dtype],
+                           L.CACHE_FP8_EXACT if self.fp8_exact else 0)
 
     @staticmethod
     def from_host(cache, device) -> "DeviceCache":

@@ -31,6 +31,7 @@ struct DecodeArgs {
     int32_t num_items, row_chunks, grid_wgs;
     float scale_log2;          // scale * log2(e)
     mla_dtype_t q_dtype, kv_dtype, partial_dtype;
+    int32_t cache_flags;       // mla_cache_desc_t::flags
 };
 
 // Plan layout (int32 entries): header[8] = {num_items, B, row_chunks,
@@ -52,6 +53,8 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 // MFMA decode of the DeepSeek-V2 shape (d_c 512, d_r 64, bf16 queries) for
 // every 16-bit and 8-bit cache format
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
+// the same shape over an e4m3 latent cache on the 8-bit matrix cores
+hipError_t launch_decode_f8mma(const DecodeArgs &a, hipStream_t s);
 // split_off / seq_flags are indexed by b * ceil(rows / chunk_rows) + r / chunk_rows
 hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *lse_part,
                           const int32_t *split_off, const int32_t *seq_flags, int32_t B,

@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "lds_copy.hpp"
 
 namespace mla {
 
@@ -122,28 +123,6 @@ __device__ __forceinline__ constexpr int tok_of(int i) {
 // contiguous one.
 __device__ __forceinline__ constexpr int rot_swz(int t) { return ((t & 7) >> 1) ^ (((t >> 3) & 1) << 2); }
 
-// One asynchronous 1 KiB copy: global_load_lds_dwordx4 writes lane i's 16
-// bytes to LDS at M0 + 16 i.  Issued as inline asm so that the compiler's
-// wait-count pass does not see an LDS writer in flight (it would otherwise
-// drain every LDS read with lgkmcnt(0)); completion is awaited explicitly
-// (vmcnt + barrier) before a stage is read.  VMEM loads complete in order, so
-// the compiler's own vmcnt waits stay correct: unseen extra loads can only
-// make them over-wait.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const uint8_t *src) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(src)
-                 : "memory", "m0");
-}
-
-// One asynchronous 4-byte copy by lane 0 only: to LDS at M0 (the block scale
-// of an 8-bit stage).  Same wait discipline as dma16.
-__device__ __forceinline__ void dma4_lane0(uint32_t lds_addr, const uint8_t *src, int lane) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-    if (lane == 0)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                     :: "s"(m0), "v"(0u), "s"(src) : "memory", "m0");
-}
-
 // The copy of one stage is split into parts (one instruction each) so that
 // the stage loop can spread them over the score MFMAs.
 constexpr int DMA_PER_STAGE = 9;    // 16-bit rows, per wave: 8 latent rows + 1 KiB of rotary parts
@@ -195,22 +174,6 @@ __device__ __forceinline__ void stage_part_row(const uint8_t *rows0, const uint8
     }
 }
 static_assert(HALF * (DC + DR) <= 18 * 1024 && 18 * 1024 <= FP8_STAGE, "row stage copy");
-
-// Loads of wave-uniform values (plan, block table, lengths) through the
-// constant address space become scalar loads, which never wait on the
-// vector-memory counter of the asynchronous stage copies.
-__device__ __forceinline__ int32_t sload(const int32_t *p, int64_t i) {
-    return ((const __attribute__((address_space(4))) int32_t *)p)[i];
-}
-
-// An opaque copy of a per-lane value: offsets derived from it are computed
-// where they are used and die there, instead of being held in registers
-// across the stage loop (the fp8 copies and conversion use it).
-__device__ __forceinline__ int opaque(int v) {
-    asm volatile("" : "+v"(v));
-    return v;
-}
-
 
 // FP8: the cache stores e4m3 (or e5m2) latents with one fp32 scale per
 // 64-token block and bf16 rotary keys.  Codes are converted exactly to bf16

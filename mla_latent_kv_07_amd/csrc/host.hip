@@ -82,6 +82,7 @@ mla_status_t check_cache(const mla_cache_desc_t *c) {
                     c->d_c, c->d_r);
     if (is_fp8_kv(c->kv_dtype) && !c->block_scales)
         return fail(MLA_ERR_INVALID_ARG, "fp8 cache needs block_scales");
+    if (c->flags & ~MLA_CACHE_FP8_EXACT) return fail(MLA_ERR_INVALID_ARG, "unknown cache flags %d", c->flags);
     if (!aligned(c->base, 16)) return fail(MLA_ERR_ALIGN, "cache base not 16-byte aligned");
     return MLA_OK;
 }
@@ -340,13 +341,17 @@ mla_status_t prepare_decode(const void *q_lat, const void *q_rope, mla_dtype_t q
     a.scale_log2 = scale * 1.4426950408889634f;
     a.q_dtype = q_dtype; a.kv_dtype = cache->kv_dtype;
     a.partial_dtype = (mla_dtype_t)plan->partial_dtype;
+    a.cache_flags = cache->flags;
     *out = a;
     return MLA_OK;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     if (a.num_items == 0) return hipSuccess;
-    if (is_fast_shape(a.kv_dtype, a.d_c, a.d_r) && a.q_dtype == MLA_DT_BF16) return launch_decode_mfma(a, s);
+    if (is_fast_shape(a.kv_dtype, a.d_c, a.d_r) && a.q_dtype == MLA_DT_BF16) {
+        if (a.kv_dtype == MLA_DT_FP8_E4M3 && !(a.cache_flags & MLA_CACHE_FP8_EXACT)) return launch_decode_f8mma(a, s);
+        return launch_decode_mfma(a, s);
+    }
     return launch_decode_generic(a, s);
 }
 

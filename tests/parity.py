@@ -54,9 +54,12 @@ def to_device(d: I.DecodeInputs):
             d.q_lat.to(DEV), d.q_rope.to(DEV))
 
 
-def run_decode(d: I.DecodeInputs, cus=None):
+def run_decode(d: I.DecodeInputs, cus=None, fp8_exact=False):
+    """fp8_exact: an e4m3 latent cache decoded exactly on 16-bit MFMAs instead
+    of the default 8-bit MFMA path (mla_cache_desc_t.flags)."""
     wl = d.wl
     cache, bt, sl, ql, qr = to_device(d)
+    cache.fp8_exact = fp8_exact
     dec = api.Decoder(d.cache.seq_lens, wl.q_len, wl.n_h, wl.d_c, wl.d_r, wl.kv_dtype, DEV, cus=cus)
     o, lse = dec(ql, qr, cache, bt, sl, d.scale)
     torch.cuda.synchronize()

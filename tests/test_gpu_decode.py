@@ -112,9 +112,50 @@ def test_decode_generic_paths():
     compare_decode(d, o, lse)
 
 
-def test_decode_fp8_cache():
+@pytest.mark.parametrize("exact", [False, True], ids=["fp8_mfma", "exact_bf16"])
+def test_decode_fp8_cache(exact):
     d = small("fp8_e4m3", seq=(2, 150, 300), q_len=2, seed=14)
-    o, lse, _ = run_decode(d, cus=8)
+    o, lse, _ = run_decode(d, cus=8, fp8_exact=exact)
+    compare_decode(d, o, lse)
+
+
+def test_decode_fp8_mfma_path_tracks_exact_path():
+    # the two arithmetics over one e4m3 cache: the 8-bit MFMA path (two-term
+    # e4m3 query and probabilities) against the exact decode, row by row, and
+    # both against the oracle.  The rows scaled x8 here carry 8x larger
+    # logits, so the query's residual rounding (~2^-8) moves their weights
+    # most: the paths differ by up to ~2 % (a few 1e-3 on N(0,1) rows)
+    d = small("fp8_e4m3", seq=(700, 1, 64, 65, 1300), q_len=2, seed=41, heavy=0.02)
+    o8, l8, _ = run_decode(d, cus=6)
+    ox, lx, _ = run_decode(d, cus=6, fp8_exact=True)
+    a8 = o8.float().cpu().numpy().reshape(-1, 512)
+    ax = ox.float().cpu().numpy().reshape(-1, 512)
+    nz = np.linalg.norm(ax, axis=1) > 0
+    rel = np.linalg.norm(a8 - ax, axis=1)[nz] / np.linalg.norm(ax, axis=1)[nz]
+    say(f"  8-bit vs exact path: max row rel diff {rel.max():.3e}")
+    assert rel.max() < 3e-2
+    assert np.array_equal(np.isinf(l8.cpu().numpy()), np.isinf(lx.cpu().numpy()))
+    compare_decode(d, o8, l8)
+    compare_decode(d, ox, lx)
+
+
+def test_decode_fp8_mfma_block_scale_edges():
+    # block scales the 8-bit path splits into mantissa (in the P codes) and
+    # E8M0 exponent (on the value MFMA): zero (the block's latent term
+    # vanishes), below the E8M0 range (2^-126: exponent clamped, mantissa
+    # shrinks), an odd mantissa (x 1.37) and a negative scale (the codes
+    # change sign); the oracle decodes code * scale exactly.  (A scale far
+    # above the data's absmax / 448 inflates that block's logits, and with
+    # them the score error of the two-term query: the exact path serves such
+    # caches.)
+    d = small("fp8_e4m3", seq=(640, 300), seed=43)
+    sc = d.cache.block_scales
+    blocks = d.cache.block_table[0, :10].tolist()
+    sc[blocks[1]] = 0.0
+    sc[blocks[2]] = 2.0 ** -126
+    sc[blocks[3]] = sc[blocks[3]] * 1.37
+    sc[blocks[5]] = -sc[blocks[5]]
+    o, lse, _ = run_decode(d, cus=4)
     compare_decode(d, o, lse)
 
 

@@ -152,10 +152,11 @@ A = 1 << 20
 
 
 def _desc(**kw):
-    d = dict(base=A, block_scales=None, num_blocks=10, block_size=64, d_c=512, d_r=64, kv_dtype=L.DT_BF16)
+    d = dict(base=A, block_scales=None, num_blocks=10, block_size=64, d_c=512, d_r=64, kv_dtype=L.DT_BF16,
+             flags=0)
     d.update(kw)
     return L.CacheDesc(d["base"], d["block_scales"], d["num_blocks"], d["block_size"], d["d_c"],
-                       d["d_r"], d["kv_dtype"])
+                       d["d_r"], d["kv_dtype"], d["flags"])
 
 
 def _decode(desc=None, q=A, qr=A, qdt=L.DT_BF16, bt=A, stride=64, sl=A, B=2, q_len=1, n_h=128,
@@ -175,6 +176,8 @@ def _decode(desc=None, q=A, qr=A, qdt=L.DT_BF16, bt=A, stride=64, sl=A, B=2, q_l
     (dict(desc=_desc(d_c=2048)), L.MLA_ERR_UNSUPPORTED),
     (dict(desc=_desc(d_r=6)), L.MLA_ERR_UNSUPPORTED),
     (dict(desc=_desc(kv_dtype=L.DT_FP8_E4M3)), L.MLA_ERR_INVALID_ARG),   # no block scales
+    (dict(desc=_desc(flags=2)), L.MLA_ERR_INVALID_ARG),                  # unknown cache flag
+    (dict(desc=_desc(flags=-1)), L.MLA_ERR_INVALID_ARG),
     (dict(q=None), L.MLA_ERR_INVALID_ARG),
     (dict(qr=None), L.MLA_ERR_INVALID_ARG),
     (dict(o=None), L.MLA_ERR_INVALID_ARG),
