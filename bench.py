@@ -40,11 +40,12 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA peak
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak
 COPY_BYTES = 256 << 20          # calibration copy size
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_mfma_bf16_traffic.json")
 DECODE_KERNEL = "decode_mfma_kernel<mla::kv::Bf16>"       # bf16 cache
-DECODE_KERNEL_FP8 = "decode_mfma_kernel<mla::kv::E4m3>"   # fp8 cache, converted to bf16 in LDS
+DECODE_KERNEL_FP8 = "decode_f8mma_kernel"   # e4m3 cache on the 8-bit MFMAs
 MFMA_KERNELS = {"bf16": DECODE_KERNEL, "fp8_e4m3": DECODE_KERNEL_FP8,
                 "f16": "decode_mfma_kernel<mla::kv::F16>",
                 "fp8_e5m2": "decode_mfma_kernel<mla::kv::E5m2>",
@@ -318,10 +319,14 @@ def roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic):
     cache byte is below the ridge of the kernel's contraction (bf16 MFMA 2.5
     PFLOP/s, or fp32 vector ALU 157.3 TFLOP/s for the generic kernel, against
     8 TB/s), else the compute unit.  (fp16 caches run fp16 MFMAs, whose
-    dense peak equals bf16's.)"""
+    dense peak equals bf16's; the e4m3 kernel runs the latent score and the
+    value sum, 94 % of its FLOPs, on 8-bit MFMAs and is priced at the fp8
+    dense peak of 5.0 PFLOP/s.)"""
     gbs = cache_bytes / (dec_ms * 1e-3) / 1e9
     tfl = flops / (dec_ms * 1e-3) / 1e12
-    if kernel in MFMA_KERNELS.values():
+    if kernel == DECODE_KERNEL_FP8:
+        cpeak, cbound = FP8_MFMA_PEAK_TFLOPS, "mfma"
+    elif kernel in MFMA_KERNELS.values():
         cpeak, cbound = BF16_MFMA_PEAK_TFLOPS, "mfma"
     else:
         cpeak, cbound = FP32_VALU_PEAK_TFLOPS, "alu"
