@@ -90,7 +90,7 @@ typedef enum {
  *   0 (default): the codes go into 8-bit MFMAs as stored.  Each query row
  *     becomes two e4m3 terms, q~ ~= sigma_q (h + l/16) with
  *     sigma_q = max|q~| / 448.  The probabilities become two e4m3 terms of
- *     y = p 2^5 mant(|block scale|), y ~= h + l/16; the exponent of the block
+ *     y = p 2^5 mant(|block scale|), y ~= h + l (l the residual); the exponent of the block
  *     scale rides on the value MFMA's E8M0 operand scale.  The rotary part
  *     stays on bf16.
  *   MLA_CACHE_FP8_EXACT: codes are decoded exactly to bf16, and bf16 MFMAs

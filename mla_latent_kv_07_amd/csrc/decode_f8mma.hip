@@ -9,7 +9,8 @@
 //   q8  the absorbed query of a row as two e4m3 terms, q~ ~= sigma_q (h + l/16),
 //       sigma_q = max|q~| / 448 over the row (h alone leaves ~8 % error in
 //       o_lat on N(0,1) data, h + l/16 about 2.5 %);
-//   P8  p 2^5 mant(sigma_blk) as two e4m3 terms, P ~= P_h + P_l / 16, with
+//   P8  y = p 2^5 mant(sigma_blk) as two e4m3 terms, y ~= P_h + P_l (P_l the
+//       unscaled residual y - P_h, within 2^-10 of it), with
 //       sigma_blk = mant 2^e, mant in [1, 2): the value MFMA applies 2^(e-5)
 //       through its E8M0 A-operand scale, so O gathers sum_p p c_p up to the
 //       rounding of P (one term alone leaves ~4 % error in o_lat on N(0,1)
@@ -75,7 +76,7 @@ constexpr int LIM_OFF = RING_OFF + 4 * RING_SLOT;
 constexpr int LDS_BYTES = LIM_OFF + 4 * 128 > 128 * O_PITCH ? LIM_OFF + 4 * 128 : 128 * O_PITCH;
 constexpr int COPIES = 11;                   // per wave and stage: 8 latent KiB, 2 rotary KiB, the scale
 constexpr int E8M0_ONE = 127;                // E8M0 scale 2^0
-constexpr int E8M0_16TH = 123;               // 2^-4: the l terms of the query and of P
+constexpr int E8M0_16TH = 123;               // 2^-4: the l term of the query
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 static_assert(COPIES <= 2 * KC, "two copy parts per score k-chunk");
 static_assert(STAGE % 8192 == 0, "stage offsets leave the XOR-ed address bits 4-8 clear");
@@ -430,8 +431,7 @@ __global__ __launch_bounds__(256, 1) void decode_f8mma_kernel(DecodeArgs a) {
             ph[w] = pk8x4(sv[q], sv[q + 1], sv[q + 2], sv[q + 3]);
             const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(ph[w], false);
             const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(ph[w], true);
-            pl[w] = pk8x4((sv[q] - h01[0]) * 16.0f, (sv[q + 1] - h01[1]) * 16.0f, (sv[q + 2] - h23[0]) * 16.0f,
-                          (sv[q + 3] - h23[1]) * 16.0f);
+            pl[w] = pk8x4(sv[q] - h01[0], sv[q + 1] - h01[1], sv[q + 2] - h23[0], sv[q + 3] - h23[1]);
         }
         if (__ballot(raise && m_run != -INFINITY)) {
             // rare: the value sum so far moves to the new reference max;
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void decode_f8mma_kernel(DecodeArgs a) {
             oacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[mb % PFV], ph, oacc[mb], 0, 0, 0, sa, 0,
                                                                         E8M0_ONE);
             oacc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[mb % PFV], pl, oacc[mb], 0, 0, 0, sa, 0,
-                                                                        E8M0_16TH);
+                                                                        E8M0_ONE);
             if (mb + PFV < MBLK) vf[mb % PFV] = vld(mb + PFV);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             if (mb + PFV < MBLK) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
