@@ -302,10 +302,10 @@ __global__ __launch_bounds__(256, 1) void decode_f8mma_kernel(DecodeArgs a) {
         // this iteration's score MFMAs (issued in one burst, the copies held
         // the wave at the memory pipeline while the matrix core idled; among
         // the value MFMAs they pushed the queries out of registers).  Past the
-        // item's last stage the parts copy pool block 0 into that free
-        // buffer, which is never read again, so that the score loop needs no
-        // branch.
-        const int64_t id2 = st + 2 < nst_live ? blk_id(st + 2) : 0;
+        // item's last stage the parts copy this stage's own block (just read,
+        // so served from L2) into that free buffer, which is never read
+        // again, so that the score loop needs no branch.
+        const int64_t id2 = blk_id(st + 2 < nst_live ? st + 2 : st);
         const uint32_t so = stage_off(st);
         // positions past the sequence end: zero codes and keys, so that P = 0
         // never meets NaN or stale data in the value MFMA
