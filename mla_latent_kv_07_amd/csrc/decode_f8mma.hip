@@ -8,7 +8,7 @@
 // with
 //   q8  the absorbed query of a row as two e4m3 terms, q~ ~= sigma_q (h + l/16),
 //       sigma_q = max|q~| / 448 over the row (h alone leaves ~8 % error in
-//       o_lat on N(0,1) data, h + l/16 about 2.5 %);
+//       o_lat on N(0,1) data; with h + l/16 the query adds ~0.2 %);
 //   P8  y = p 2^5 mant(sigma_blk) as two e4m3 terms, y ~= P_h + P_l (P_l the
 //       unscaled residual y - P_h, within 2^-10 of it), with
 //       sigma_blk = mant 2^e, mant in [1, 2): the value MFMA applies 2^(e-5)
@@ -79,6 +79,7 @@ constexpr int E8M0_ONE = 127;                // E8M0 scale 2^0
 constexpr int E8M0_16TH = 123;               // 2^-4: the l term of the query
 static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 static_assert(COPIES <= 2 * KC, "two copy parts per score k-chunk");
+static_assert(COPIES == 11, "the stage loop waits with vmcnt(11): one stage's copies per wave");
 static_assert(STAGE % 8192 == 0, "stage offsets leave the XOR-ed address bits 4-8 clear");
 
 // LDS layout of a stage (token t = 0..63 of the block):
