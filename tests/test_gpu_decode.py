@@ -139,6 +139,19 @@ def test_decode_fp8_mfma_path_tracks_exact_path():
     compare_decode(d, ox, lx)
 
 
+@pytest.mark.parametrize("exact", [False, True], ids=["fp8_mfma", "exact_bf16"])
+def test_decode_fp8_few_heads_and_empty_rows(exact):
+    # n_h = 16 with a query pair: 32 rows per sequence, so three of the four
+    # waves hold only rows past the end; sequences shorter than the pair and
+    # empty ones leave rows with no visible position (o = 0, lse = -inf)
+    d = small("fp8_e4m3", seq=(1, 0, 2, 77, 300), q_len=2, n_h=16, seed=45)
+    o, lse, _ = run_decode(d, cus=4, fp8_exact=exact)
+    compare_decode(d, o, lse)
+    lse_c = lse.cpu().reshape(5, 2, 16)
+    assert torch.isinf(lse_c[0, 0]).all() and torch.isinf(lse_c[1]).all()
+    assert torch.isfinite(lse_c[0, 1]).all() and torch.isfinite(lse_c[3]).all()
+
+
 def test_decode_fp8_mfma_block_scale_edges():
     # block scales the 8-bit path splits into mantissa (in the P codes) and
     # E8M0 exponent (on the value MFMA): zero (the block's latent term
