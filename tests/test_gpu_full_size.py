@@ -35,13 +35,15 @@ def test_long_context_full_size_sampled():
     compare_decode(d, o, lse, rows=rows)
 
 
-def test_fp8_spec_pair_full_size_sampled():
+@pytest.mark.parametrize("exact", [False, True], ids=["fp8_mfma", "exact_bf16"])
+def test_fp8_spec_pair_full_size_sampled(exact):
     """64 sequences of 1K-8K tokens, e4m3 latent with one scale per block,
-    bf16 rotary keys, two causal query tokens per sequence."""
+    bf16 rotary keys, two causal query tokens per sequence; the default 8-bit
+    MFMA decode and the exact one."""
     t0 = time.time()
     d = I.make_decode_inputs(I.C4)
     say(f"  inputs {time.time() - t0:.1f} s")
-    o, lse, _ = run_decode(d)
+    o, lse, _ = run_decode(d, fp8_exact=exact)
     rows = _sample_rows(d.wl.B * d.wl.q_len * d.wl.n_h, 128, 4)
     compare_decode(d, o, lse, rows=rows)
 
