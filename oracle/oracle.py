@@ -77,7 +77,14 @@ PIN_STATUS = {
                     "(bf16, f32) over ragged call sizes; bytes outside written slots unchanged; fp8 "
                     "whole-block scale = amax/448 with codes within half an e4m3 step; scale growth "
                     "re-encodes earlier rows within two roundings; all-zero block takes scale 1",
-    "project_queries_lowrank": "pinned: equals the one-matrix projection with merged per-head weights",
+    "project_kv": "pinned: one-hot hidden states select weight rows exactly (c = first d_c columns, "
+                  "k^R = the rest, unrotated at position 0) and each rotary pair equals an explicit 2x2 "
+                  "rotation by p * 10000^(-2j/d_R) at the token's own position; linear in h",
+    "project_queries_direct": "pinned: one-hot hidden states select head blocks [q^C_i | q^R_i] of W_Q "
+                              "exactly, q^R turned by an explicit 2x2 rotation at each token's position",
+    "project_queries_lowrank": "pinned: equals the one-matrix projection with merged per-head weights; "
+                               "with W^DQ = I one-hot rows select W^UQ / W^QR head columns, q^R turned "
+                               "by an explicit 2x2 rotation",
     "project_queries_absorbed": "pinned: absorbed scores equal scores against explicitly reconstructed keys",
     "absorb_q": "pinned: absorbed score equals score against explicitly reconstructed keys",
     "absorb_out": "pinned: equals explicit per-head value reconstruction followed by W^O",
@@ -499,6 +506,10 @@ def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, 
         code' = fp8(value(code) * scale / scale');
       - the new codes are fp8(value / scale').
     Scales are kept as float32; the codes use the stored float32 value.
+    A token whose position has no table entry (p < 0 or p >= 64 * table
+    width), or whose entry is not a pool block id (an unallocated slot such as
+    -1), is not written: the pages leave such tokens undefined, and skipping
+    them keeps every other block intact.
     pool: uint8 [num_blocks][block_bytes]; block_scales: float32 [num_blocks]
     (fp8 only).  Both are modified."""
     pool = np.asarray(pool)
@@ -520,8 +531,11 @@ def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, 
         rb = enc.shape[1]
         for t in range(T):
             b, p = t // q_len, int(pos[t])
+            if p < 0 or p // BLOCK >= bt.shape[1]:
+                continue                     # no table entry: not written
             blk = int(bt[b, p // BLOCK])
-            assert 0 <= blk < nblk_pool
+            if not 0 <= blk < nblk_pool:
+                continue                     # unallocated table slot: not written
             pool[blk, (p % BLOCK) * rb:(p % BLOCK + 1) * rb] = enc[t]
         return
     assert fmt in SCALED
@@ -536,10 +550,13 @@ def cache_append(pool, block_scales, fmt: int, d_c: int, d_r: int, block_table, 
         groups: dict[int, list[int]] = {}
         for i in range(q_len):
             p = int(pos[b * q_len + i])
+            if p < 0 or p // BLOCK >= bt.shape[1]:
+                continue                     # no table entry: not written
             groups.setdefault(p // BLOCK, []).append(i)
         for lb, idx in groups.items():
             blk = int(bt[b, lb])
-            assert 0 <= blk < nblk_pool
+            if not 0 <= blk < nblk_pool:
+                continue                     # unallocated table slot: not written
             toks = [b * q_len + i for i in idx]
             slots = [int(pos[t]) % BLOCK for t in toks]
             amax = float(np.max(np.abs(vals[toks])))

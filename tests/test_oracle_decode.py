@@ -45,9 +45,12 @@ def _rounded_rows(wl, rows):
     return rows.to(torch.float64)
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16", "f16"])
-def test_decode_matches_sdpa_fp64(kv):
-    wl = _small(kv)
+@pytest.mark.parametrize("kv,d_c,d_r", [("f32", 64, 16), ("bf16", 64, 16), ("f16", 64, 16),
+                                        ("bf16", 512, 64)])
+def test_decode_matches_sdpa_fp64(kv, d_c, d_r):
+    # one KV head of width D_qk = d_c + d_r with D_v = d_c: small dims, and
+    # the DeepSeek-V2 dims (576 / 512)
+    wl = _small(kv, d_c=d_c, d_r=d_r)
     g = _gen(11)
     rows = I.draw_cache_rows(wl, g, torch.tensor(wl.seq_lens))
     T = wl.B
