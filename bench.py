@@ -272,6 +272,30 @@ class Timer:
         check(st)
         return wall * 1e3 / K, e0.elapsed_time(e1) / K
 
+    def split_steps(self, phases, K, check):
+        """K steps, each the given phases (callables taking the step index)
+        in order, with an event before, between and after them: returns
+        (wall ms per step, event ms per step, [mean event ms of each phase]).
+        The phases of a step run back to back, so the phase means add up to
+        the step time."""
+        n = len(phases)
+        evs = [[self.ev() for _ in range(n + 1)] for _ in range(K)]
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st = 0
+        for i in range(K):
+            e = evs[i]
+            e[0].record(self.stream)
+            for j, ph in enumerate(phases):
+                st |= ph(i)
+                e[j + 1].record(self.stream)
+        self.torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        check(st)
+        per = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K for j in range(n)]
+        gpu = evs[0][0].elapsed_time(evs[K - 1][n]) / K
+        return wall * 1e3 / K, gpu, per
+
     def per_call(self, step, n, check):
         pairs = [(self.ev(), self.ev()) for _ in range(n)]
         st = 0
@@ -292,6 +316,26 @@ def replicas_for(args, pool_bytes) -> int:
     if args.replicas:
         return args.replicas
     return max(2, -(-(512 << 20) // pool_bytes))
+
+
+def shader_clock_mhz(torch, timer, lib, step, n=8, iters=2000):
+    """Shader clock under matrix-core load: a short MFMA-chain probe on every
+    compute unit right after each of n steps of the workload (s_memtime
+    cycles over s_memrealtime 100 MHz ticks, mla_clock_probe); the median over
+    the probes, and their range."""
+    from mla_latent_kv_07_amd import _lib as L
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros((n, wgs, 2), dtype=torch.int64, device="cuda:0")
+    for i in range(n):
+        L.check(step(i))
+        L.check(lib.mla_clock_probe(ctypes.c_void_p(out[i].data_ptr()), wgs, iters,
+                                    ctypes.c_void_p(timer.stream.cuda_stream)))
+    torch.cuda.synchronize()
+    o = out.cpu().double()
+    mhz = sorted((o[i, :, 0].sum() / o[i, :, 1].sum() * 100.0).item() for i in range(n))
+    return {"median": round(mhz[n // 2], 1), "min": round(mhz[0], 1), "max": round(mhz[-1], 1),
+            "how": "s_memtime / s_memrealtime (100 MHz) over a bf16 MFMA chain on every CU, after each of "
+                   f"{n} steps"}
 
 
 def copy_calibration(torch, timer, dev):
@@ -343,6 +387,16 @@ def roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic):
               "hbm_gbs": round(gbs, 1), "tflops": round(tfl, 1),
               "compute_frac": round(tfl / cpeak, 4)})
     return r
+
+
+def mfma_util_at_clock(kernel, flops, dec_ms, mhz):
+    """Algorithmic FLOPs per second over the dense peak of the kernel's MFMAs
+    at the measured shader clock (the published peaks assume 2.4 GHz)."""
+    if kernel not in MFMA_KERNELS.values():
+        return None
+    peak = FP8_MFMA_PEAK_TFLOPS if kernel == DECODE_KERNEL_FP8 else BF16_MFMA_PEAK_TFLOPS
+    tfl = flops / (dec_ms * 1e-3) / 1e12
+    return round(tfl / (peak * mhz / 2400.0), 4)
 
 
 def traffic_for(kernel, workload):
@@ -402,11 +456,19 @@ def run_decode(args, wl):
         L.check(step(i))
     torch.cuda.synchronize()
     K = args.steps
-    ms_per_step, gpu_ms = timer.steps(step, K, L.check)
+    # the timed steps: mla_decode as its two launches (calling both in order
+    # is exactly mla_decode), with HIP events before, between and after them
+    # on the launch stream, so that decode + combine = the step by
+    # construction
+    phases = [lambda i: part(*call_args[i % R])]
+    if dec.info.needs_combine:
+        phases.append(lambda i: fin(*fin_args))
+    ms_per_step, gpu_ms, per = timer.split_steps(phases, K, L.check)
+    dec_ms = per[0]
+    comb_ms = per[1] if dec.info.needs_combine else 0.0
     n_leg = max(K, 50)
-    dec_ms = timer.legs(part, call_args, n_leg, L.check)
-    comb_ms = timer.legs(fin, [fin_args], n_leg, L.check) if dec.info.needs_combine else 0.0
     call_us = timer.per_call(step, n_leg, L.check)
+    clock = shader_clock_mhz(torch, timer, lib, step)
     copy_gbs = copy_calibration(torch, timer, dev) if args.copy_calibration else None
 
     kernel = decode_kernel_name(wl)
@@ -436,9 +498,11 @@ def run_decode(args, wl):
         "call_us": call_us,
         "decode_kernel_us": round(dec_ms * 1e3, 2),
         "combine_kernel_us": round(comb_ms * 1e3, 2),
+        "shader_clock_mhz": clock,
         "roofline": roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic_for(kernel, wl.name)),
         "cpu_baseline": None,
     }
+    out["roofline"]["mfma_util_at_clock"] = mfma_util_at_clock(kernel, flops, dec_ms, clock["median"])
     if copy_gbs is not None:
         out["copy_calibration_gbs"] = copy_gbs
     if not args.no_cpu_baseline:

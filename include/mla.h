@@ -99,8 +99,13 @@ typedef enum {
  * data (two e4m3 terms carry q~ and P to ~2^-8).  The 8-bit path's score
  * error grows with the logits: a block whose scale dwarfs its data's
  * absmax / 448 (logits far beyond the rest) is better decoded exactly.
- * Block scales must be finite (any sign; zero allowed).  Every other format
- * and shape ignores flags.
+ * Block scales must be finite (any sign; zero allowed).  Both arithmetics
+ * bound tiny scales to keep their fp32 intermediates in range: the 8-bit
+ * path clamps the exponent at -122 (the mantissa then shrinks), the exact
+ * path (and the e5m2 / whole-row formats, which always take it) raises
+ * magnitudes below 2^-64 to 2^-64 — a block with such a scale holds latent
+ * values below 448 * 2^-64, negligible next to any block of ordinary scale.
+ * Every other format and shape ignores flags.
  */
 #define MLA_CACHE_FP8_EXACT 1
 
@@ -134,6 +139,10 @@ typedef struct {
     int64_t plan_ints;      /* int32 entries of the device plan */
     int64_t workspace_bytes;/* partial-result workspace mla_decode needs */
     int32_t grid_wgs;       /* workgroups of the MFMA decode launch (dispatch-table entries) */
+    int32_t kv_dtype;       /* cache format the plan was built for (mla_dtype_t) */
+    int32_t d_r;            /* rotary width the plan was built for */
+    int32_t max_seq_blocks; /* largest ceil(seq_lens[b] / 64): mla_decode needs
+                               bt_stride >= this */
 } mla_plan_t;
 
 /*
@@ -190,15 +199,21 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
  *        d_c = 512, d_r = 64 (MFMA); every other supported combination runs a
  *        generic kernel (d_c <= 1024, d_r <= 256, d_c and d_r multiples of 4).
  * block_table [B][bt_stride] int32 pool block ids; entries past
- *        ceil(seq_lens[b]/64) are never read.
- * seq_lens [B] int32 (device), the same values the plan was built from.
+ *        ceil(seq_lens[b]/64) are never read.  bt_stride must cover the
+ *        longest planned sequence (bt_stride >= plan->max_seq_blocks).  Ids
+ *        outside [0, num_blocks) are clamped into it (no fault; a correct
+ *        table holds none).
+ * seq_lens [B] int32 (device), the same values the plan was built from
+ *        (the kernels read at most the planned blocks of each sequence).
  * scale  softmax scale; the pages give none — the absorbed score keeps the
  *        un-absorbed logits, so pass 1/sqrt(d_nope + d_r) for those.
  * plan / plan_dev  from mla_decode_plan (host struct, device copy).
  * workspace  >= plan->workspace_bytes (may be NULL if that is 0), 256-B aligned.
  * o_lat  [T][n_h][d_c] in q_dtype; lse [T][n_h] fp32.
- * Errors: INVALID_ARG (nulls, sizes, plan mismatch, num_blocks < 1),
- * UNSUPPORTED (block_size != 64, dims/dtypes), ALIGN, WORKSPACE, HIP.
+ * Errors: INVALID_ARG (nulls, sizes, num_blocks < 1, a plan built for
+ * another B / q_len / n_h / d_c / d_r / kv dtype, bt_stride below
+ * plan->max_seq_blocks), UNSUPPORTED (block_size != 64, dims/dtypes), ALIGN,
+ * WORKSPACE, HIP.
  */
 mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
                         const mla_cache_desc_t *cache, const int32_t *block_table,
@@ -206,6 +221,31 @@ mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dty
                         int32_t n_h, float scale, const mla_plan_t *plan,
                         const int32_t *plan_dev, void *workspace, int64_t workspace_bytes,
                         void *o_lat, float *lse, mla_stream_t stream);
+
+/*
+ * mla_decode_noalloc — mla_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, kernels and results, with the
+ * split partials in a scratch array the library holds in device memory
+ * instead of a caller workspace.  It calls no hipMalloc / hipFree and no
+ * allocating routine.  Limit: plan->workspace_bytes <=
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB: every configuration of 256 work items
+ * of up to 256 query rows), else MLA_ERR_WORKSPACE before any HIP call.
+ * Each GPU the library runs on holds one scratch array (64 MiB) until the
+ * process ends; its address is looked up once per device on the first call
+ * there (with that device current).  Every call on a GPU shares that GPU's
+ * scratch, which keeps the last call's contents (nothing in it has to start
+ * at zero): calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.  Arguments and other errors
+ * are those of mla_decode without workspace / workspace_bytes.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64 << 20)
+mla_status_t mla_decode_noalloc(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
+                                const mla_cache_desc_t *cache, const int32_t *block_table,
+                                int32_t bt_stride, const int32_t *seq_lens, int32_t B,
+                                int32_t q_len, int32_t n_h, float scale, const mla_plan_t *plan,
+                                const int32_t *plan_dev, void *o_lat, float *lse,
+                                mla_stream_t stream);
 
 /*
  * mla_decode_partial / mla_decode_finish — mla_decode in its two launches.
@@ -284,7 +324,9 @@ mla_status_t mla_absorb_out(const void *o_lat, const void *w_uv, const void *w_o
  * (block bt[b][p/64], slot p%64).  Row bytes: (d_c + d_r) * elem for F32 /
  * BF16; for FP8_E4M3 the d_c code bytes followed by the 2*d_r bytes of the
  * bf16 rotary key.  out is [B][max_tokens][row bytes]; rows past seq_lens[b]
- * are not written.  Bit-exact byte copy.
+ * are not written.  Bit-exact byte copy.  max_tokens must not exceed
+ * 64 * bt_stride (INVALID_ARG); block ids outside [0, num_blocks) are
+ * clamped into it.
  */
 mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *block_table,
                               int32_t bt_stride, const int32_t *seq_lens, int32_t B,
@@ -330,9 +372,10 @@ mla_status_t mla_rope_freqs(const mla_rope_t *rope, int32_t d_r, double *theta_h
  *   slot p % 64 of block block_table[b][p / 64].
  * h [T][d_model], w_kv [d_model][d_c + d_r] (W^DKV then W^KR columns), both
  * dt (F32 or BF16); accumulation in fp32; pos0 [B] int32 (device).  The block
- * table must already hold blocks for every written position; ids outside
- * [0, num_blocks) are clamped, and tokens at p < 0 or p >= 64 bt_stride
- * are not written.  Storage: F32 / BF16 rows rounded once to
+ * table must already hold blocks for every written position; a token whose
+ * table entry lies outside [0, num_blocks) (an unallocated slot such as -1)
+ * is not written, nor is a token at p < 0 or p >= 64 bt_stride, so no other
+ * block is touched.  Storage: F32 / BF16 rows rounded once to
  * nearest even.  FP8_E4M3 (huny §6 FP8 item: a dynamic scale per block; the
  * pages give no update rule — the reading here): a block whose slot 0 is
  * written by this call takes scale amax|c| / 448 over the tokens written
@@ -377,6 +420,17 @@ mla_status_t mla_project_q(const void *h, const void *w_dq, const void *w_uq, co
                            int32_t d_c, int32_t d_r, const mla_rope_t *rope, void *q_lat,
                            void *q_rope, void *workspace, int64_t workspace_bytes,
                            mla_stream_t stream);
+
+/*
+ * mla_clock_probe — measurement helper, not a step of the path: `wgs`
+ * workgroups of 4 waves each run a dependent chain of `iters` bf16
+ * 32x32x16 MFMAs, and out[2k], out[2k+1] (int64, device) receive the shader
+ * cycles (s_memtime) and 100 MHz real-time ticks (s_memrealtime) workgroup k
+ * spent in it, so that out[2k] / out[2k+1] * 100 MHz is the shader clock
+ * under matrix-core load.  INVALID_ARG for NULL out, wgs outside [1, 65536]
+ * or iters outside [1, 2^24]; ALIGN for an out not 8-byte aligned.
+ */
+mla_status_t mla_clock_probe(int64_t *out, int32_t wgs, int32_t iters, mla_stream_t stream);
 
 /* Bytes of the whole pool described by `cache` (0 on bad arguments). */
 int64_t mla_cache_bytes(const mla_cache_desc_t *cache);

@@ -17,6 +17,7 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGN", 4: "WOR
 DT_F32, DT_BF16, DT_FP8_E4M3, DT_F16, DT_FP8_E5M2, DT_FP8_E4M3_ROW = 0, 1, 2, 3, 4, 5
 BLOCK_SIZE = 64
 CACHE_FP8_EXACT = 1   # mla_cache_desc_t.flags: exact fp8 decode on 16-bit MFMAs
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES
 
 c_int32, c_int64, c_void_p, c_float = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
 
@@ -40,7 +41,7 @@ class Plan(ctypes.Structure):
         ("num_items", c_int32), ("row_chunks", c_int32), ("num_partials", c_int32),
         ("needs_combine", c_int32), ("max_splits", c_int32), ("blocks_per_item", c_int32),
         ("partial_dtype", c_int32), ("plan_ints", c_int64), ("workspace_bytes", c_int64),
-        ("grid_wgs", c_int32),
+        ("grid_wgs", c_int32), ("kv_dtype", c_int32), ("d_r", c_int32), ("max_seq_blocks", c_int32),
     ]
 
     def as_dict(self):
@@ -79,6 +80,9 @@ def load() -> ctypes.CDLL:
                              c_int32, c_int32, c_float, ctypes.POINTER(Plan), P, P, c_int64, P,
                              P, P]
     L.mla_decode_partial.argtypes = L.mla_decode.argtypes
+    L.mla_decode_noalloc.argtypes = [P, P, c_int32, ctypes.POINTER(CacheDesc), P, c_int32, P, c_int32,
+                                     c_int32, c_int32, c_float, ctypes.POINTER(Plan), P, P, P, P]
+    L.mla_decode_noalloc.restype = c_int32
     L.mla_decode_finish.argtypes = [ctypes.POINTER(Plan), P, P, c_int64, c_int32, P, P, P]
     L.mla_combine_lse.argtypes = [P, P, P, P, c_int32, c_int32, c_int32, P, c_int32, P, P]
     L.mla_absorb_q.argtypes = [P, c_int64, P, P, c_int32, c_int32, c_int32, c_int32, c_int32, P]
@@ -98,6 +102,8 @@ def load() -> ctypes.CDLL:
     L.mla_project_q_workspace.restype = c_int64
     L.mla_project_q.argtypes = [P, P, P, P, P, c_int32, P, c_int32, c_int32, c_int32, c_int32,
                                 c_int32, c_int32, c_int32, ctypes.POINTER(Rope), P, P, P, c_int64, P]
+    L.mla_clock_probe.argtypes = [P, c_int32, c_int32, P]
+    L.mla_clock_probe.restype = c_int32
     L.mla_last_error.restype = ctypes.c_char_p
     L.mla_version.restype = ctypes.c_char_p
     for name in ("mla_decode_plan", "mla_decode", "mla_decode_partial", "mla_decode_finish",

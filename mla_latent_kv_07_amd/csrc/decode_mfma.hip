@@ -246,6 +246,17 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     auto sigma = [&](int st) {
         return *(const __attribute__((address_space(3))) float *)(smem + ring_off<FP8>() + 4 * (st & 3));
     };
+    // The arithmetic takes the magnitude of a block scale: its sign and a
+    // zero are applied to the codes when they are converted (negated, or
+    // zeroed with magnitude 1).  Magnitudes below 2^-64 are raised to 2^-64:
+    // the rotary partial sum is divided by the scale and the probabilities
+    // carry it, and this keeps both inside fp32's range (such a block's
+    // latent values are below 448 * 2^-64 either way).
+    auto sig_mag = [](float s) { return s == 0.f ? 1.f : __builtin_fmaxf(__builtin_fabsf(s), 0x1p-64f); };
+    // xor mask (sign flip of both bf16 halves) and zero flag of stage st's
+    // converted codes
+    auto code_xor = [&](int st) { return sigma(st) < 0.f ? 0x80008000u : 0u; };
+    auto code_zero = [&](int st) { return sigma(st) == 0.f; };
     auto stage_off = [&](int st) {
         // bf16: stage st in buffer (st + 2) mod 4 (buffers 0-1 hold the queries
         // while stages 0-1 are copied)
@@ -514,7 +525,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             return *(const uint4 *)(src + FP8_LAT + t * RB + c * 16);
         }
     };
-    auto convert_part = [&](int st, const uint4 &in, int j) {
+    // xr / zr: the stage's code_xor / code_zero (a negative scale negates
+    // the converted codes, a zero scale zeroes them; the rotary part of the
+    // split layout is bf16 and carries no scale)
+    auto convert_part = [&](int st, const uint4 &in, int j, uint32_t xr, bool zr) {
         const int valid = S - (p_first + st * HALF);
         lds_u8 *dst = smem + stage_off(st);
         const int tid = opaque(threadIdx.x);
@@ -525,27 +539,33 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             const uint32_t w[4] = {in.x, in.y, in.z, in.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                o[2 * e] = cvt_lo(w[e]);
-                o[2 * e + 1] = cvt_hi(w[e]);
+                o[2 * e] = cvt_lo(w[e]) ^ xr;
+                o[2 * e + 1] = cvt_hi(w[e]) ^ xr;
             }
-            const bool live = t < valid;
+            const bool live = t < valid && !zr;
             uint4 *d = (uint4 *)(dst + t * LPITCH + c16 * 32);
             d[0] = live ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
             d[1] = live ? make_uint4(o[4], o[5], o[6], o[7]) : make_uint4(0, 0, 0, 0);
         } else {
             const int t = tid >> 3, c = tid & 7;
             uint4 v = in;
-            if constexpr (ROW) v = make_uint4(cvt_lo(in.x), cvt_hi(in.x), cvt_lo(in.y), cvt_hi(in.y));
+            bool live = t < valid;
+            if constexpr (ROW) {
+                v = make_uint4(cvt_lo(in.x) ^ xr, cvt_hi(in.x) ^ xr, cvt_lo(in.y) ^ xr, cvt_hi(in.y) ^ xr);
+                live = live && !zr;
+            }
             *(uint4 *)(dst + LAT_BYTES + (t >> 3) * 1024 + (t & 7) * 128 + (c ^ rot_swz(t)) * 16) =
-                t < valid ? v : make_uint4(0, 0, 0, 0);
+                live ? v : make_uint4(0, 0, 0, 0);
         }
     };
     auto convert = [&](int st) {
+        const uint32_t xr = code_xor(st);
+        const bool zr = code_zero(st);
         uint4 in[5];
 #pragma unroll
         for (int j = 0; j < 5; ++j) in[j] = convert_load(st, j);
 #pragma unroll
-        for (int j = 0; j < 5; ++j) convert_part(st, in[j], j);
+        for (int j = 0; j < 5; ++j) convert_part(st, in[j], j, xr, zr);
     };
 
     // ---- prologue: score of stage 0
@@ -557,7 +577,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         if (nst_live > 1) convert(1);
         __syncthreads();
         if (nst_live > 2) issue(2, blk_id_tab(2, tab_raw(2)));
-        sig_cur = sigma(0);
+        sig_cur = sig_mag(sigma(0));
     } else {
         if (nst_live > 2) issue(2, blk_id_tab(2, tab_raw(2)));
         zero_tail(0);
@@ -601,7 +621,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             // with stage st+3
             __syncthreads();
             if constexpr (COPY_AT == 0) { if (iss) issue(st + 3, id3); }
-            if (has_next) sig_next = sigma(st + 1);
+            if (has_next) sig_next = sig_mag(sigma(st + 1));
         } else {
             if (has_next) {
                 // stage st+1 landed for this wave (stage st+2 may be in flight)
@@ -716,6 +736,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
         raw = tab_raw(st + 4);
         const bool conv = FP8 && st + 2 < nst_live;
         uint4 cin[2];
+        uint32_t cxr = 0;
+        bool czr = false;
         if constexpr (FP8) {
             if (conv) {
                 if (COPY_AT != 2 && st + 3 < nst_live)
@@ -724,6 +746,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();   // every wave's copy of stage st+2 has landed
                 cin[0] = convert_load(st + 2, 0);
+                cxr = code_xor(st + 2);
+                czr = code_zero(st + 2);
             }
         }
 
@@ -756,7 +780,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
                     if (conv) {
                         const int j = i / 6;
                         if (j < 4) cin[(j + 1) & 1] = convert_load(st + 2, j + 1);
-                        convert_part(st + 2, cin[j & 1], j);
+                        convert_part(st + 2, cin[j & 1], j, cxr, czr);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <queue>
 #include <vector>
 
@@ -115,8 +116,11 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     if (rows > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "q_len*n_h too large");
     int32_t row_chunks = (int32_t)((rows + kRowsPerChunk - 1) / kRowsPerChunk);
 
-    for (int b = 0; b < B; ++b)
+    int64_t max_seq_blocks = 0;
+    for (int b = 0; b < B; ++b) {
         if (seq_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARG, "seq_lens[%d] = %d < 0", b, seq_lens_host[b]);
+        max_seq_blocks = std::max<int64_t>(max_seq_blocks, (seq_lens_host[b] + (int64_t)kBlock - 1) / kBlock);
+    }
 
     // Work list: every (sequence, row chunk) segment with at least one block,
     // in order.  A work item is a block range of one segment, run by one
@@ -238,6 +242,9 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     info->blocks_per_item = (int32_t)max_blocks;
     info->partial_dtype = is_fast_shape(kv_dtype, d_c, d_r) ? MLA_DT_BF16 : MLA_DT_F32;
     info->grid_wgs = (int32_t)grid_wgs;
+    info->kv_dtype = (int32_t)kv_dtype;
+    info->d_r = d_r;
+    info->max_seq_blocks = (int32_t)max_seq_blocks;
     info->plan_ints = plan_flags_off((int32_t)num_items, (int32_t)grid_wgs, (int32_t)nseg) + nseg;
     int64_t o_bytes = num_partials * rows * d_c * elem_bytes((mla_dtype_t)info->partial_dtype);
     int64_t o_bytes_al = (o_bytes + 255) / 256 * 256;
@@ -307,8 +314,17 @@ mla_status_t prepare_decode(const void *q_lat, const void *q_rope, mla_dtype_t q
     if (!plan || !plan_dev) return fail(MLA_ERR_INVALID_ARG, "missing decode plan");
     if (B < 1 || q_len < 1 || n_h < 1 || bt_stride < 1)
         return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d q_len=%d n_h=%d bt_stride=%d", B, q_len, n_h, bt_stride);
-    if (plan->B != B || plan->q_len != q_len || plan->n_h != n_h || plan->d_c != cache->d_c)
+    if (plan->B != B || plan->q_len != q_len || plan->n_h != n_h || plan->d_c != cache->d_c ||
+        plan->d_r != cache->d_r)
         return fail(MLA_ERR_INVALID_ARG, "plan was built for other sizes");
+    if (plan->kv_dtype != (int32_t)cache->kv_dtype)
+        return fail(MLA_ERR_INVALID_ARG, "plan was built for kv dtype %d, cache is %d", plan->kv_dtype,
+                    (int)cache->kv_dtype);
+    if (bt_stride < plan->max_seq_blocks)
+        return fail(MLA_ERR_INVALID_ARG, "bt_stride %d < %d blocks of the longest planned sequence", bt_stride,
+                    plan->max_seq_blocks);
+    if (plan->partial_dtype != (is_fast_shape(cache->kv_dtype, cache->d_c, cache->d_r) ? MLA_DT_BF16 : MLA_DT_F32))
+        return fail(MLA_ERR_INVALID_ARG, "plan partial dtype does not match the cache format");
     if (q_dtype != MLA_DT_F32 && q_dtype != MLA_DT_BF16)
         return fail(MLA_ERR_UNSUPPORTED, "q dtype %d unsupported", (int)q_dtype);
     if (!aligned(q_lat, 16) || !aligned(o_lat, 16) || (q_rope && !aligned(q_rope, 16)) || !aligned(lse, 4))
@@ -392,6 +408,71 @@ mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dty
     hipError_t e = launch_decode(a, s);
     if (e != hipSuccess) return hip_status(e, "decode launch");
     return finish_decode(plan, plan_dev, workspace, q_dtype, o_lat, lse, s);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of the entry point that allocates nothing (mla_decode_noalloc):
+// each GPU the library runs on holds one copy until the process ends.  In
+// host code `scratch` is only a stand-in for the symbol; its device address
+// comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+mla_status_t scratch_address(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_decode_noalloc(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
+                                const mla_cache_desc_t *cache, const int32_t *block_table,
+                                int32_t bt_stride, const int32_t *seq_lens, int32_t B,
+                                int32_t q_len, int32_t n_h, float scale, const mla_plan_t *plan,
+                                const int32_t *plan_dev, void *o_lat, float *lse,
+                                mla_stream_t stream) {
+    if (!plan) return fail(MLA_ERR_INVALID_ARG, "missing decode plan");
+    if (plan->workspace_bytes < 0 || plan->workspace_bytes > (int64_t)MLA_NOALLOC_SCRATCH_BYTES)
+        return fail(MLA_ERR_WORKSPACE, "plan needs %lld workspace bytes, beyond the %lld-byte scratch of "
+                    "mla_decode_noalloc", (long long)plan->workspace_bytes, (long long)MLA_NOALLOC_SCRATCH_BYTES);
+    // every argument check first (the scratch address is only a stand-in
+    // here: a non-NULL, 256-byte aligned placeholder), then the one HIP call
+    // that resolves it
+    DecodeArgs a;
+    mla_status_t st = prepare_decode(q_lat, q_rope, q_dtype, cache, block_table, bt_stride, seq_lens, B, q_len,
+                                     n_h, scale, plan, plan_dev, (void *)(uintptr_t)256,
+                                     MLA_NOALLOC_SCRATCH_BYTES, o_lat, lse, &a);
+    if (st != MLA_OK) return st;
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != MLA_OK) return st;
+    st = prepare_decode(q_lat, q_rope, q_dtype, cache, block_table, bt_stride, seq_lens, B, q_len, n_h, scale,
+                        plan, plan_dev, ws, MLA_NOALLOC_SCRATCH_BYTES, o_lat, lse, &a);
+    if (st != MLA_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_decode(a, s);
+    if (e != hipSuccess) return hip_status(e, "decode launch");
+    return finish_decode(plan, plan_dev, ws, q_dtype, o_lat, lse, s);
 }
 
 mla_status_t mla_decode_partial(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
@@ -578,6 +659,9 @@ mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *bloc
     if (!block_table || !seq_lens || !out) return fail(MLA_ERR_INVALID_ARG, "NULL block_table/seq_lens/out");
     if (B < 1 || max_tokens < 1 || bt_stride < 1)
         return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d max_tokens=%d bt_stride=%d", B, max_tokens, bt_stride);
+    if ((int64_t)max_tokens > (int64_t)kBlock * bt_stride)
+        return fail(MLA_ERR_INVALID_ARG, "max_tokens %d > %d positions of a block-table row", max_tokens,
+                    kBlock * bt_stride);
     if (!aligned(out, 16)) return fail(MLA_ERR_ALIGN, "out not 16-byte aligned");
     int eb = elem_bytes(cache->kv_dtype);
     bool split = cache->kv_dtype == MLA_DT_FP8_E4M3 || cache->kv_dtype == MLA_DT_FP8_E5M2;
@@ -585,9 +669,18 @@ mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *bloc
     int32_t r_bytes = split ? cache->d_r * 2 : 0;
     return hip_status(launch_gather((const uint8_t *)cache->base,
                                     block_bytes_of(cache->kv_dtype, cache->d_c, cache->d_r),
-                                    c_bytes, r_bytes, split, block_table, bt_stride, seq_lens, B,
+                                    cache->num_blocks, c_bytes, r_bytes, split, block_table, bt_stride,
+                                    seq_lens, B,
                                     max_tokens, (uint8_t *)out, (hipStream_t)stream),
                       "gather launch");
+}
+
+mla_status_t mla_clock_probe(int64_t *out, int32_t wgs, int32_t iters, mla_stream_t stream) {
+    if (!out) return fail(MLA_ERR_INVALID_ARG, "out is NULL");
+    if (wgs < 1 || wgs > (1 << 16) || iters < 1 || iters > (1 << 24))
+        return fail(MLA_ERR_INVALID_ARG, "bad probe size wgs=%d iters=%d", wgs, iters);
+    if (!aligned(out, 8)) return fail(MLA_ERR_ALIGN, "out not 8-byte aligned");
+    return hip_status(launch_clock_probe(out, wgs, iters, (hipStream_t)stream), "clock probe launch");
 }
 
 }  // extern "C"

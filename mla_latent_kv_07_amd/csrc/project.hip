@@ -135,7 +135,8 @@ struct AppendArgs {
 
 // fp8 caches (e4m3 or e5m2 latent + bf16 k^R, or the whole row in e4m3): one
 // workgroup per sequence, its q_len tokens in order (positions outside the
-// block table, p < 0 or p >= 64 bt_stride, are skipped).  The tokens that land
+// block table, p < 0 or p >= 64 bt_stride, or whose table entry is not a
+// pool block id, are skipped).  The tokens that land
 // in one block are handled together: the amax of their coded values sets or
 // raises the block scale, earlier slots are re-encoded when it grows, then
 // the codes are written.
@@ -152,10 +153,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab r
     const int N = a.d_c + a.d_r;
     const int p0 = a.pos0[b];
     auto xval = [&](int t, int f) { return split_sum(a.ws, a.split_stride, a.splits, (int64_t)t * N + f); };
-    auto block_of = [&](int p) {
-        int64_t id = a.bt[(int64_t)b * a.bt_stride + p / kBlock];
-        return id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
-    };
+    auto block_of = [&](int p) { return (int64_t)a.bt[(int64_t)b * a.bt_stride + p / kBlock]; };
     // rotary pair j of token t at position p: rotated, times mscale
     auto rot = [&](int t, int p, int j, float &y0, float &y1) {
         const float x0 = xval(t, a.d_c + 2 * j), x1 = xval(t, a.d_c + 2 * j + 1);
@@ -175,6 +173,10 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab r
             continue;
         }
         const int64_t blk = block_of(p);
+        if (blk < 0 || blk >= a.num_blocks) {        // unallocated table slot: not written
+            i = i_end;
+            continue;
+        }
         uint8_t *base = a.pool + blk * a.block_bytes;
         const int s0 = p % kBlock;
         // amax of the new latents in this block
@@ -245,8 +247,8 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab 
     const int t = (int)(idx / P2), k = (int)(idx % P2);
     const int b = t / a.q_len, p = a.pos0[b] + t % a.q_len;
     if (p < 0 || p / kBlock >= a.bt_stride) return;   // outside the table: not written
-    int64_t blk = a.bt[(int64_t)b * a.bt_stride + p / kBlock];
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    const int64_t blk = a.bt[(int64_t)b * a.bt_stride + p / kBlock];
+    if (blk < 0 || blk >= a.num_blocks) return;       // unallocated table slot: not written
     const int64_t o = (int64_t)t * N + 2 * k;
     float y0 = split_sum(a.ws, a.split_stride, a.splits, o);
     float y1 = split_sum(a.ws, a.split_stride, a.splits, o + 1);

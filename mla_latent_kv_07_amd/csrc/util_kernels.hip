@@ -13,12 +13,16 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t *__restrict__
                                                      const int32_t *__restrict__ bt,
                                                      int32_t bt_stride,
                                                      const int32_t *__restrict__ seq_lens,
-                                                     int32_t max_tokens, uint8_t *__restrict__ out) {
+                                                     int32_t max_tokens, int64_t num_blocks,
+                                                     uint8_t *__restrict__ out) {
     const int b = blockIdx.y;
     const int row_words = (c_bytes + r_bytes) >> 2;
+    // the host guarantees max_tokens <= 64 bt_stride, so p / 64 stays inside
+    // the table row; ids outside the pool are clamped into it
     const int n = min(seq_lens[b], max_tokens);
     for (int p = blockIdx.x * 16; p < min(n, (int)blockIdx.x * 16 + 16); ++p) {
-        const int64_t blk = bt[(int64_t)b * bt_stride + p / kBlock];
+        int64_t blk = bt[(int64_t)b * bt_stride + p / kBlock];
+        blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
         const int slot = p % kBlock;
         const uint8_t *base = pool + blk * block_bytes;
         uint32_t *dst = (uint32_t *)(out + ((int64_t)b * max_tokens + p) * (c_bytes + r_bytes));
@@ -225,13 +229,47 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
 
 }  // namespace
 
-hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int32_t c_bytes,
+// Shader-clock probe (a measurement helper, no step of the path): every wave
+// runs a dependent chain of `iters` bf16 32x32x16 MFMAs; lane 0 of each
+// workgroup records the shader cycles (s_memtime) and the 100 MHz real-time
+// ticks (s_memrealtime) the chain took.  The volatile asm fences keep the
+// chain between the two reads.
+__global__ __launch_bounds__(256) void clock_probe_kernel(int64_t *__restrict__ out, int32_t iters) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(float)((threadIdx.x + i) & 7);
+        b[i] = (__bf16)0.0f;
+    }
+    f32x16 acc = {};
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    asm volatile("" : "+v"(acc));
+    for (int i = 0; i < iters; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    asm volatile("s_nop 15" : "+v"(acc));
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = (int64_t)(t1 - t0);
+        out[2 * blockIdx.x + 1] = (int64_t)(r1 - r0);
+    }
+    if (iters < 0) out[0] = (int64_t)acc[threadIdx.x & 15];   // keeps the chain (never taken)
+}
+
+hipError_t launch_clock_probe(int64_t *out, int32_t wgs, int32_t iters, hipStream_t s) {
+    hipLaunchKernelGGL(clock_probe_kernel, dim3(wgs), dim3(256), 0, s, out, iters);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int64_t num_blocks, int32_t c_bytes,
                          int32_t r_bytes, bool split_rows, const int32_t *bt, int32_t bt_stride,
                          const int32_t *seq_lens, int32_t B, int32_t max_tokens, uint8_t *out,
                          hipStream_t s) {
     dim3 grid((max_tokens + 15) / 16, B);
     hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, pool, block_bytes, c_bytes, r_bytes,
-                       (int32_t)split_rows, bt, bt_stride, seq_lens, max_tokens, out);
+                       (int32_t)split_rows, bt, bt_stride, seq_lens, max_tokens, num_blocks, out);
     return hipGetLastError();
 }
 

@@ -162,37 +162,12 @@ def draw_seq_lens(wl: Workload, g: torch.Generator) -> torch.Tensor:
     return torch.tensor(wl.seq_lens, dtype=torch.int32)
 
 
-# Draws of more than this many values come from NumPy PCG64 streams seeded
+# Draws of more than this many values come from a NumPy PCG64 stream seeded
 # with one 63-bit integer drawn from the workload's torch generator (one draw
-# of the generator per tensor, as for small tensors).  The values are filled
-# in fixed chunks of _CHUNK, chunk i from the seeded stream jumped i times,
-# on a thread pool: the result does not depend on the thread count, and the
-# multi-gigabyte caches of the long-context and full-layer workloads take
-# seconds instead of minutes.
+# of the generator per tensor, as for small tensors, so the draw order is
+# kept), filled sequentially: the multi-gigabyte caches of the long-context
+# and full-layer workloads take seconds instead of minutes.
 _BIG_DRAW = 1 << 20
-_CHUNK = 1 << 24
-
-
-def _normal(shape, g, std=1.0):
-    n = math.prod(shape)
-    if n <= _BIG_DRAW:
-        return torch.randn(shape, generator=g, dtype=torch.float32) * std
-    import os
-    from concurrent.futures import ThreadPoolExecutor
-
-    import numpy as np
-    seed = int(torch.randint(0, 2 ** 63 - 1, (1,), generator=g, dtype=torch.int64))
-    out = np.empty(n, dtype=np.float32)
-    base = np.random.PCG64(seed)
-
-    def fill(i):
-        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
-        np.random.Generator(base.jumped(i)).standard_normal(out=out[lo:hi], dtype=np.float32)
-
-    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
-        list(ex.map(fill, range((n + _CHUNK - 1) // _CHUNK)))
-    t = torch.from_numpy(out).view(shape)
-    return t * std if std != 1.0 else t
 
 
 def _normal(shape, g, std=1.0):

@@ -48,8 +48,9 @@ def test_absorb_out(dt, T, n_h, d_c, d_v, d_model):
     eu = row_rel_err(u.float().cpu().numpy(), ref_u)
     # `out` takes u as the device rounded it (one more bf16 rounding than
     # the fp64 chain): compare against the oracle applied to the device's u
-    u_dev = u.float().cpu().double().numpy().reshape(T, -1)
-    ref_out_u = u_dev @ wo.double().numpy()
+    # (the oracle's absorb_out with W^UV = I per head applies W^O alone)
+    u_dev = u.float().cpu().double().numpy()
+    _, ref_out_u = O.absorb_out(u_dev, np.broadcast_to(np.eye(d_v), (n_h, d_v, d_v)), wo.double().numpy())
     eo = row_rel_err(out.float().cpu().numpy(), ref_out_u)
     eo_chain = row_rel_err(out.float().cpu().numpy(), ref_out)
     say(f"  absorb_out {dt} T={T}: u {eu:.3e} out {eo:.3e} chain {eo_chain:.3e}")

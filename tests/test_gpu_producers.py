@@ -257,3 +257,51 @@ def test_append_f16_rows():
     got, _, want, _, pool0, mask = _run_appends(O.FMT_F16, B, [3, 1, 70], d_c, d_r, dm, seed=27)
     assert np.array_equal(got[~mask], pool0[~mask])
     _check_16bit_rows(got, want, mask, "f16")
+
+
+@pytest.mark.parametrize("fmt", [O.FMT_BF16, O.FMT_FP8_E4M3])
+def test_append_skips_unallocated_table_slots(fmt):
+    """Table entries of -1 (blocks not yet allocated): the tokens that map to
+    them are not written and no other block changes; the rest of the call
+    is written as usual (sequence 2 crosses from an allocated block into an
+    unallocated one)."""
+    B, d_c, d_r, dm, ql = 3, 512, 64, 128, 5
+    rng, bt, pool, scales = _setup(fmt, B, 140, d_c, d_r, dm, seed=28)
+    bt[1, :] = -1
+    bt[2, 1] = -1
+    pos = np.array([10, 20, 62], np.int32)
+    pool0 = pool.copy()
+    w_dev = _bf16(rng.standard_normal((dm, d_c + d_r)) / math.sqrt(dm))
+    h_dev = _bf16(rng.standard_normal((B * ql, dm)))
+    cache = api.DeviceCache(torch.from_numpy(pool).to(DEV),
+                            torch.from_numpy(scales).to(DEV) if fmt in O.SCALED else None,
+                            KV[fmt], d_c, d_r)
+    api.cache_append(h_dev.to(DEV), w_dev.to(DEV), cache, torch.from_numpy(bt).to(DEV),
+                     torch.from_numpy(pos).to(DEV), ql, api.rope())
+    torch.cuda.synchronize()
+    got = cache.pool.cpu().numpy()
+    want, w_sc = pool.copy(), scales.copy()
+    O.cache_append(want, w_sc, fmt, d_c, d_r, bt, pos, ql, h_dev.double().numpy(), w_dev.double().numpy())
+    # bytes the call may write: blocks of sequence 0 and block 0 of sequence 2
+    touched = sorted({int(bt[0, 0]), int(bt[2, 0])})
+    other = np.setdiff1d(np.arange(pool.shape[0]), touched)
+    assert np.array_equal(got[other], pool0[other]), "a block outside the allocated slots changed"
+    assert np.array_equal(want[other], pool0[other])
+    if fmt == O.FMT_BF16:
+        mask = np.zeros(pool.shape, bool)
+        for b, n in ((0, ql), (2, 2)):
+            for i in range(n):
+                p = int(pos[b]) + i
+                sl = p % BLK
+                mask[bt[b, p // BLK], sl * 1152:(sl + 1) * 1152] = True
+        assert np.array_equal(got[~mask], pool0[~mask])
+        _check_16bit_rows(got, want, mask, "bf16")
+    else:
+        g_sc = cache.block_scales.cpu().numpy()
+        np.testing.assert_allclose(g_sc[touched], w_sc[touched], rtol=1e-6)
+        assert np.array_equal(g_sc[other], scales[other])
+        gv, wv = O.fp8_decode(fmt, got[touched, :BLK * d_c]), O.fp8_decode(fmt, want[touched, :BLK * d_c])
+        step = np.maximum(np.abs(wv) * 2.0 ** -3, 2.0 ** -9)
+        nan = np.isnan(wv)
+        assert np.array_equal(np.isnan(gv), nan)
+        assert np.all(np.abs(gv - wv)[~nan] <= step[~nan] * 1.0001)

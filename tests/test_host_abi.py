@@ -168,6 +168,13 @@ def _decode(desc=None, q=A, qr=A, qdt=L.DT_BF16, bt=A, stride=64, sl=A, B=2, q_l
                             ctypes.byref(plan_), plan_dev, ws, ws_bytes, o, lse, None)
 
 
+def test_plan_records_its_shape_and_table_width():
+    info, _ = plan([100, 200, 0, 64], kv=L.DT_FP8_E4M3, d_r=64)
+    assert (info.kv_dtype, info.d_r, info.max_seq_blocks) == (L.DT_FP8_E4M3, 64, 4)
+    info, _ = plan([4096] * 32)
+    assert info.max_seq_blocks == 64
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(desc=_desc(block_size=32)), L.MLA_ERR_UNSUPPORTED),
     (dict(desc=_desc(num_blocks=0)), L.MLA_ERR_INVALID_ARG),       # empty cache
@@ -185,6 +192,10 @@ def _decode(desc=None, q=A, qr=A, qdt=L.DT_BF16, bt=A, stride=64, sl=A, B=2, q_l
     (dict(B=3), L.MLA_ERR_INVALID_ARG),                             # plan mismatch
     (dict(n_h=64), L.MLA_ERR_INVALID_ARG),
     (dict(stride=0), L.MLA_ERR_INVALID_ARG),
+    (dict(stride=3), L.MLA_ERR_INVALID_ARG),                        # 200 tokens need 4 table entries
+    (dict(plan_=plan([100, 200], kv=L.DT_F16)[0]), L.MLA_ERR_INVALID_ARG),   # plan for another format
+    (dict(plan_=plan([100, 200], d_r=32)[0]), L.MLA_ERR_INVALID_ARG),        # plan for another d_r
+    (dict(plan_=plan([100, 200], d_c=256)[0]), L.MLA_ERR_INVALID_ARG),       # plan for another d_c
     (dict(qdt=L.DT_FP8_E4M3), L.MLA_ERR_UNSUPPORTED),
     (dict(q=A + 4), L.MLA_ERR_ALIGN),
     (dict(o=A + 2), L.MLA_ERR_ALIGN),
@@ -219,6 +230,9 @@ def test_other_entry_points_reject_bad_arguments():
     assert l.mla_gather_paged(ctypes.byref(d), A, 64, A, 0, 10, A, None) == L.MLA_ERR_INVALID_ARG
     assert l.mla_gather_paged(ctypes.byref(_desc(block_size=16)), A, 64, A, 2, 10, A, None) == L.MLA_ERR_UNSUPPORTED
     assert l.mla_gather_paged(ctypes.byref(d), A, 64, A, 2, 10, A + 1, None) == L.MLA_ERR_ALIGN
+    # more tokens than a table row of 2 entries maps
+    assert l.mla_gather_paged(ctypes.byref(d), A, 2, A, 2, 129, A, None) == L.MLA_ERR_INVALID_ARG
+    assert b"max_tokens" in l.mla_last_error()
 
 
 def test_cache_bytes():
@@ -299,3 +313,21 @@ def test_producers_reject_bad_arguments():
         a[i] = v
         assert l.mla_project_q(*a) == st, (i, v)
     assert l.mla_project_q_workspace(128, 5120, 1536, 128, 128, 512, 64, L.DT_BF16) > 0
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    # the entry point that allocates nothing refuses a plan whose partials
+    # exceed its fixed scratch, before any HIP call
+    info, _ = plan([100, 200], cus=4)
+    assert 0 < info.workspace_bytes <= L.NOALLOC_SCRATCH_BYTES
+    info.workspace_bytes = L.NOALLOC_SCRATCH_BYTES + 256
+    d = _desc()
+    st = lib().mla_decode_noalloc(A, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 2, 1, 128, 0.07,
+                                  ctypes.byref(info), A, A, A, None)
+    assert st == L.MLA_ERR_WORKSPACE and b"scratch" in lib().mla_last_error()
+    # argument errors are reported as by mla_decode, still before any HIP call
+    info, _ = plan([100, 200], cus=4)
+    assert lib().mla_decode_noalloc(A, A, L.DT_BF16, ctypes.byref(d), A, 3, A, 2, 1, 128, 0.07,
+                                    ctypes.byref(info), A, A, A, None) == L.MLA_ERR_INVALID_ARG
+    assert lib().mla_decode_noalloc(A, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 2, 1, 128, 0.07,
+                                    None, A, A, A, None) == L.MLA_ERR_INVALID_ARG
