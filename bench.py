@@ -8,8 +8,9 @@ this metadata once per batch, vLLM MLA page "MLA의 MQA 디코딩 경로").
 
 Prints one JSON line: latent-cache GB/s over the whole step, plus
   roofline      the decode kernel's algorithmic cache bytes per launch over
-                its average launch time (HIP events around back-to-back
-                launches on the launch stream), against MI355X's 8 TB/s HBM
+                its average launch time in the timed steps (start / stop
+                events stamped from the kernel's own dispatch on the launch
+                stream, mla_set_launch_events), against MI355X's 8 TB/s HBM
                 peak; "traffic" is the measured HBM bytes per launch from the
                 FETCH_SIZE / WRITE_SIZE counter summary, when that summary was
                 taken on the current kernel source;
@@ -272,29 +273,29 @@ class Timer:
         check(st)
         return wall * 1e3 / K, e0.elapsed_time(e1) / K
 
-    def split_steps(self, phases, K, check):
-        """K steps, each the given phases (callables taking the step index)
-        in order, with an event before, between and after them: returns
-        (wall ms per step, event ms per step, [mean event ms of each phase]).
-        The phases of a step run back to back, so the phase means add up to
-        the step time."""
-        n = len(phases)
-        evs = [[self.ev() for _ in range(n + 1)] for _ in range(K)]
+    def kernel_steps(self, lib, step, n_k, K, check):
+        """K steps between two events; before each step the next n_k kernel
+        launches of the library are given start / stop events stamped from
+        their own dispatch.  Returns (wall ms per step, event ms per step,
+        [mean ms of launch j of a step])."""
+        evs = [[self.ev() for _ in range(2 * n_k)] for _ in range(K)]
+        for e in (x for row in evs for x in row):   # create the HIP events
+            e.record(self.stream)
+        handles = [(ctypes.c_void_p * (2 * n_k))(*[e.cuda_event for e in row]) for row in evs]
+        e0, e1 = self.ev(), self.ev()
         self.torch.cuda.synchronize()
         t0 = time.perf_counter()
+        e0.record(self.stream)
         st = 0
         for i in range(K):
-            e = evs[i]
-            e[0].record(self.stream)
-            for j, ph in enumerate(phases):
-                st |= ph(i)
-                e[j + 1].record(self.stream)
+            st |= lib.mla_set_launch_events(handles[i], n_k)
+            st |= step(i)
+        e1.record(self.stream)
         self.torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         check(st)
-        per = [sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K for j in range(n)]
-        gpu = evs[0][0].elapsed_time(evs[K - 1][n]) / K
-        return wall * 1e3 / K, gpu, per
+        per = [sum(evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(K)) / K for j in range(n_k)]
+        return wall * 1e3 / K, e0.elapsed_time(e1) / K, per
 
     def per_call(self, step, n, check):
         pairs = [(self.ev(), self.ev()) for _ in range(n)]
@@ -456,16 +457,25 @@ def run_decode(args, wl):
         L.check(step(i))
     torch.cuda.synchronize()
     K = args.steps
-    # the timed steps: mla_decode as its two launches (calling both in order
-    # is exactly mla_decode), with HIP events before, between and after them
-    # on the launch stream, so that decode + combine = the step by
-    # construction
-    phases = [lambda i: part(*call_args[i % R])]
-    if dec.info.needs_combine:
-        phases.append(lambda i: fin(*fin_args))
-    ms_per_step, gpu_ms, per = timer.split_steps(phases, K, L.check)
+    # the timed steps: K back-to-back mla_decode calls between HIP events on
+    # the launch stream.  When the decode merges its own splits (the MFMA
+    # kernels with bf16 queries), a step is one launch and the decode
+    # kernel's average launch time is the step time by construction.
+    # Otherwise a second timed pass records events before, between and after
+    # the two launches of every step (decode, then combine) for the per-kernel
+    # split; those events lengthen the step, so the headline stays the plain
+    # pass.
+    # The headline: K plain mla_decode calls between two HIP events on the
+    # launch stream.  Then the same K calls again, each call's kernels
+    # stamping their own start and stop times (mla_set_launch_events, from
+    # the dispatch itself) for the per-kernel durations: the runtime follows
+    # such a stamped launch with a cache flush that lengthens the step, so
+    # that pass gives durations, not the step time.
+    n_k = 2 if dec.info.needs_combine else 1
+    ms_per_step, gpu_ms = timer.steps(step, K, L.check)
+    _, stamped_ms, per = timer.kernel_steps(lib, step, n_k, K, L.check)
     dec_ms = per[0]
-    comb_ms = per[1] if dec.info.needs_combine else 0.0
+    comb_ms = per[1] if n_k == 2 else 0.0
     n_leg = max(K, 50)
     call_us = timer.per_call(step, n_leg, L.check)
     clock = shader_clock_mhz(torch, timer, lib, step)
@@ -498,6 +508,9 @@ def run_decode(args, wl):
         "call_us": call_us,
         "decode_kernel_us": round(dec_ms * 1e3, 2),
         "combine_kernel_us": round(comb_ms * 1e3, 2),
+        "launches_per_step": n_k,
+        "kernel_us_sum": round(sum(per) * 1e3, 2),
+        "stamped_pass_us_per_step": round(stamped_ms * 1e3, 2),
         "shader_clock_mhz": clock,
         "roofline": roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic_for(kernel, wl.name)),
         "cpu_baseline": None,

@@ -165,7 +165,8 @@ typedef struct {
  * Layout written (int32): header[8] = {num_items, B, row_chunks,
  *                 num_partials, grid_wgs, 0, 0, 0},
  *                 items[num_items][4] = {b * row_chunks + chunk, blk_begin,
- *                 blk_end, slot (-1 = final)},
+ *                 blk_end, slot (-1 = final)} (a segment of an empty
+ *                 sequence has one item with blk_begin == blk_end),
  *                 wg_item[grid_wgs] (item of each decode workgroup, -1 = none),
  *                 split_off[B * row_chunks + 1] (partial slots of segment
  *                 s = b * row_chunks + chunk are split_off[s] .. split_off[s+1]-1),
@@ -431,6 +432,19 @@ mla_status_t mla_project_q(const void *h, const void *w_dq, const void *w_uq, co
  * or iters outside [1, 2^24]; ALIGN for an out not 8-byte aligned.
  */
 mla_status_t mla_clock_probe(int64_t *out, int32_t wgs, int32_t iters, mla_stream_t stream);
+
+/*
+ * mla_set_launch_events — measurement helper, not a step of the path: the
+ * next `pairs` kernel launches that the decode entry points make on the
+ * calling thread (the decode kernel, then the combine when one runs) record
+ * their own start and stop times into events[2k] and events[2k+1]
+ * (hipEvent_t created with timing; hipEventElapsedTime between the two gives
+ * the kernel's duration).  The timestamps come from the kernel's dispatch
+ * (hipExtLaunchKernel), so no marker enters the stream between launches.
+ * Pairs a call does not consume are dropped by the next call to this
+ * function.  INVALID_ARG for pairs outside [0, 4] or NULL events.
+ */
+mla_status_t mla_set_launch_events(void *const *events, int32_t pairs);
 
 /* Bytes of the whole pool described by `cache` (0 on bad arguments). */
 int64_t mla_cache_bytes(const mla_cache_desc_t *cache);

@@ -102,6 +102,8 @@ def load() -> ctypes.CDLL:
     L.mla_project_q_workspace.restype = c_int64
     L.mla_project_q.argtypes = [P, P, P, P, P, c_int32, P, c_int32, c_int32, c_int32, c_int32,
                                 c_int32, c_int32, c_int32, ctypes.POINTER(Rope), P, P, P, c_int64, P]
+    L.mla_set_launch_events.argtypes = [P, c_int32]
+    L.mla_set_launch_events.restype = c_int32
     L.mla_clock_probe.argtypes = [P, c_int32, c_int32, P]
     L.mla_clock_probe.restype = c_int32
     L.mla_last_error.restype = ctypes.c_char_p

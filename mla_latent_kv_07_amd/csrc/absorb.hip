@@ -106,11 +106,11 @@ hipError_t launch_absorb_q(const void *q_nope, int64_t ld_q, const void *w_uk, v
         return launch_absorb_q_mfma(q_nope, ld_q, w_uk, q_lat, T, n_h, d_nope, d_c, s);
     const unsigned grid = grid_for((int64_t)T * n_h * d_c);
     if (dt == MLA_DT_BF16)
-        hipLaunchKernelGGL(absorb_q_generic<uint16_t>, dim3(grid), dim3(256), 0, s,
+        launch_timed(absorb_q_generic<uint16_t>, dim3(grid), dim3(256), 0, s,
                            (const uint16_t *)q_nope, ld_q, (const uint16_t *)w_uk,
                            (uint16_t *)q_lat, T, n_h, d_nope, d_c);
     else
-        hipLaunchKernelGGL(absorb_q_generic<float>, dim3(grid), dim3(256), 0, s,
+        launch_timed(absorb_q_generic<float>, dim3(grid), dim3(256), 0, s,
                            (const float *)q_nope, ld_q, (const float *)w_uk, (float *)q_lat, T,
                            n_h, d_nope, d_c);
     return hipGetLastError();
@@ -131,17 +131,17 @@ hipError_t launch_absorb_out(const void *o_lat, const void *w_uv, const void *w_
     const unsigned g1 = grid_for((int64_t)T * n_h * d_v);
     const unsigned g2 = grid_for((int64_t)T * d_model);
     if (dt == MLA_DT_BF16) {
-        hipLaunchKernelGGL(absorb_uv_generic<uint16_t>, dim3(g1), dim3(256), 0, s,
+        launch_timed(absorb_uv_generic<uint16_t>, dim3(g1), dim3(256), 0, s,
                            (const uint16_t *)o_lat, (const uint16_t *)w_uv, (uint16_t *)u_ws, T,
                            n_h, d_c, d_v);
-        hipLaunchKernelGGL(absorb_o_generic<uint16_t>, dim3(g2), dim3(256), 0, s,
+        launch_timed(absorb_o_generic<uint16_t>, dim3(g2), dim3(256), 0, s,
                            (const uint16_t *)u_ws, (const uint16_t *)w_o, (uint16_t *)out, T,
                            n_h * d_v, d_model);
     } else {
-        hipLaunchKernelGGL(absorb_uv_generic<float>, dim3(g1), dim3(256), 0, s,
+        launch_timed(absorb_uv_generic<float>, dim3(g1), dim3(256), 0, s,
                            (const float *)o_lat, (const float *)w_uv, (float *)u_ws, T, n_h, d_c,
                            d_v);
-        hipLaunchKernelGGL(absorb_o_generic<float>, dim3(g2), dim3(256), 0, s, (const float *)u_ws,
+        launch_timed(absorb_o_generic<float>, dim3(g2), dim3(256), 0, s, (const float *)u_ws,
                            (const float *)w_o, (float *)out, T, n_h * d_v, d_model);
     }
     return hipGetLastError();

@@ -247,7 +247,7 @@ template <bool B_KCONTIG, bool OUT_F32>
 hipError_t launch_gemm(const GemmArgs &g, int batch, hipStream_t st) {
     const int tiles = (g.N + BN - 1) / BN, nt = g.ntiles < 1 ? 1 : g.ntiles;
     dim3 grid((unsigned)((tiles + nt - 1) / nt), (unsigned)((g.M + BM - 1) / BM), (unsigned)(batch * g.splits));
-    hipLaunchKernelGGL((gemm_bf16_kernel<B_KCONTIG, OUT_F32>), grid, dim3(256), 0, st, g);
+    launch_timed((gemm_bf16_kernel<B_KCONTIG, OUT_F32>), grid, dim3(256), 0, st, g);
     return hipGetLastError();
 }
 
@@ -295,7 +295,7 @@ hipError_t launch_split_sum_bf16(const float *ws, int splits, int64_t split_stri
                                  void *out, hipStream_t s) {
     const int64_t nb = (n8 + 255) / 256;
     const unsigned grid = (unsigned)(nb < 4096 ? (nb < 1 ? 1 : nb) : 4096);
-    hipLaunchKernelGGL(split_sum_kernel, dim3(grid), dim3(256), 0, s, ws, splits, split_stride, n8,
+    launch_timed(split_sum_kernel, dim3(grid), dim3(256), 0, s, ws, splits, split_stride, n8,
                        (uint16_t *)out);
     return hipGetLastError();
 }
@@ -354,7 +354,7 @@ hipError_t launch_absorb_out_mfma(const void *o_lat, const void *w_uv, const voi
     const int64_t n8 = (int64_t)T * d_model / 8;
     const int64_t nb = (n8 + 255) / 256;
     const unsigned grid = (unsigned)(nb < 4096 ? nb : 4096);
-    hipLaunchKernelGGL(split_sum_kernel, dim3(grid), dim3(256), 0, s, (const float *)ws, sp,
+    launch_timed(split_sum_kernel, dim3(grid), dim3(256), 0, s, (const float *)ws, sp,
                        (int64_t)T * d_model, n8, (uint16_t *)out);
     return hipGetLastError();
 }

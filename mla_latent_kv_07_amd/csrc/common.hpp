@@ -1,6 +1,7 @@
 // Internal declarations shared by the host layer and the kernels of libmla.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,6 +48,23 @@ __host__ __device__ inline int64_t plan_split_off(int32_t num_items, int32_t gri
 }
 __host__ __device__ inline int64_t plan_flags_off(int32_t num_items, int32_t grid_wgs, int32_t num_seg) {
     return plan_split_off(num_items, grid_wgs) + num_seg + 1;
+}
+
+// Measurement hook (mla_set_launch_events): the start / stop events the
+// next kernel launch on this thread records its own timestamps into (none:
+// nullptr), consumed in order by the launch sites below.
+struct LaunchTiming {
+    hipEvent_t start, stop;
+};
+LaunchTiming next_launch_timing();
+
+// A kernel launch that takes the next pair of measurement events, if any
+// (hipExtLaunchKernel stamps them from the kernel's own dispatch: no extra
+// packet enters the stream).
+template <typename F, typename... Args>
+inline void launch_timed(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+    const LaunchTiming t = next_launch_timing();
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, t.start, t.stop, 0u, args...);
 }
 
 hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);

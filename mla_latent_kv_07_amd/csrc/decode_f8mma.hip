@@ -525,7 +525,7 @@ hipError_t launch_decode_f8mma(const DecodeArgs &a, hipStream_t s) {
     if (a.kv_dtype != MLA_DT_FP8_E4M3 || a.d_c != DC || a.d_r != DR || a.q_dtype != MLA_DT_BF16 ||
         a.block_bytes != STAGE)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode_f8mma_kernel, dim3((unsigned)a.grid_wgs), dim3(256), 0, s, a);
+    launch_timed(decode_f8mma_kernel, dim3((unsigned)a.grid_wgs), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -188,9 +188,9 @@ template <int KV>
 hipError_t launch_kv(const DecodeArgs &a, hipStream_t s) {
     dim3 grid((unsigned)a.num_items);
     if (a.q_dtype == MLA_DT_BF16)
-        hipLaunchKernelGGL((decode_generic_kernel<KV, uint16_t>), grid, dim3(256), 0, s, a);
+        launch_timed((decode_generic_kernel<KV, uint16_t>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_generic_kernel<KV, float>), grid, dim3(256), 0, s, a);
+        launch_timed((decode_generic_kernel<KV, float>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -843,12 +843,12 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
     // one workgroup per dispatch-table entry (a multiple of 8)
     dim3 grid((unsigned)a.grid_wgs);
     switch (a.kv_dtype) {
-    case MLA_DT_BF16: hipLaunchKernelGGL(decode_mfma_kernel<kv::Bf16>, grid, dim3(256), 0, s, a); break;
-    case MLA_DT_F16: hipLaunchKernelGGL(decode_mfma_kernel<kv::F16>, grid, dim3(256), 0, s, a); break;
-    case MLA_DT_FP8_E4M3: hipLaunchKernelGGL(decode_mfma_kernel<kv::E4m3>, grid, dim3(256), 0, s, a); break;
-    case MLA_DT_FP8_E5M2: hipLaunchKernelGGL(decode_mfma_kernel<kv::E5m2>, grid, dim3(256), 0, s, a); break;
+    case MLA_DT_BF16: launch_timed(decode_mfma_kernel<kv::Bf16>, grid, dim3(256), 0, s, a); break;
+    case MLA_DT_F16: launch_timed(decode_mfma_kernel<kv::F16>, grid, dim3(256), 0, s, a); break;
+    case MLA_DT_FP8_E4M3: launch_timed(decode_mfma_kernel<kv::E4m3>, grid, dim3(256), 0, s, a); break;
+    case MLA_DT_FP8_E5M2: launch_timed(decode_mfma_kernel<kv::E5m2>, grid, dim3(256), 0, s, a); break;
     case MLA_DT_FP8_E4M3_ROW:
-        hipLaunchKernelGGL(decode_mfma_kernel<kv::E4m3Row>, grid, dim3(256), 0, s, a);
+        launch_timed(decode_mfma_kernel<kv::E4m3Row>, grid, dim3(256), 0, s, a);
         break;
     default: return hipErrorInvalidValue;
     }

@@ -17,6 +17,11 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// measurement events for the next kernel launches of this thread
+constexpr int kMaxTimedLaunches = 4;
+thread_local LaunchTiming g_timing[kMaxTimedLaunches];
+thread_local int g_timing_n = 0, g_timing_next = 0;
+
 mla_status_t fail(mla_status_t st, const char *fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
@@ -90,9 +95,29 @@ mla_status_t check_cache(const mla_cache_desc_t *c) {
 
 }  // namespace
 
+namespace mla {
+LaunchTiming next_launch_timing() {
+    if (g_timing_next >= g_timing_n) return LaunchTiming{nullptr, nullptr};
+    return g_timing[g_timing_next++];
+}
+}  // namespace mla
+
 extern "C" {
 
 const char *mla_last_error(void) { return g_err; }
+
+mla_status_t mla_set_launch_events(void *const *events, int32_t pairs) {
+    if (pairs < 0 || pairs > kMaxTimedLaunches)
+        return fail(MLA_ERR_INVALID_ARG, "pairs=%d outside [0, %d]", pairs, kMaxTimedLaunches);
+    if (pairs > 0 && !events) return fail(MLA_ERR_INVALID_ARG, "events is NULL");
+    for (int k = 0; k < pairs; ++k) {
+        if (!events[2 * k] || !events[2 * k + 1]) return fail(MLA_ERR_INVALID_ARG, "event %d is NULL", k);
+        g_timing[k] = LaunchTiming{(hipEvent_t)events[2 * k], (hipEvent_t)events[2 * k + 1]};
+    }
+    g_timing_n = pairs;
+    g_timing_next = 0;
+    return ok();
+}
 
 const char *mla_version(void) { return "mla-mi355x 0.1.0 (gfx950)"; }
 
@@ -133,13 +158,13 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     // measured 32 x 4096 batch: 8 items of 8 blocks per sequence); ragged
     // ones get pieces sized so that short sequences fill the gaps left by
     // long ones, instead of every compute unit waiting for the longest split.
+    // (segments of an empty sequence get one item of no blocks each, which
+    // writes their rows' o_lat = 0 and lse = -inf)
     struct Seg { int32_t sc; int64_t nb, st; };
     std::vector<Seg> segs;
-    bool any_empty = false;
     for (int b = 0; b < B; ++b) {
         const int64_t nb = (seq_lens_host[b] + kBlock - 1) / kBlock;
         const int64_t st = (seq_lens_host[b] + 31) / 32;
-        if (nb == 0) { any_empty = true; continue; }
         for (int c = 0; c < row_chunks; ++c) segs.push_back({b * row_chunks + c, nb, st});
     }
     constexpr int64_t kItemCost = 6;
@@ -187,6 +212,8 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
             (fill(mid, num_cus, nullptr) <= num_cus ? hi : lo) = mid;
         }
         fill(hi, num_cus, &pieces);
+        for (size_t i = 0; i < segs.size(); ++i)
+            if (segs[i].nb == 0) pieces.push_back({(int32_t)i, 0, 0});
     }
     const int64_t num_items = (int64_t)pieces.size();
     const int64_t nseg = (int64_t)B * row_chunks;
@@ -237,7 +264,7 @@ mla_status_t mla_decode_plan(const int32_t *seq_lens_host, int32_t B, int32_t q_
     info->num_items = (int32_t)num_items;
     info->row_chunks = row_chunks;
     info->num_partials = (int32_t)num_partials;
-    info->needs_combine = (num_partials > 0 || any_empty) ? 1 : 0;
+    info->needs_combine = num_partials > 0 ? 1 : 0;
     info->max_splits = max_splits;
     info->blocks_per_item = (int32_t)max_blocks;
     info->partial_dtype = is_fast_shape(kv_dtype, d_c, d_r) ? MLA_DT_BF16 : MLA_DT_F32;

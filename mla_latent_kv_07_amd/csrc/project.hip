@@ -336,7 +336,7 @@ template <typename TA, typename TB, typename TC>
 hipError_t gemm_generic(const TA *A, int64_t lda, int64_t bsa, const TB *B, int64_t sbk, int64_t sbn,
                         int64_t bsb, TC *C, int64_t ldc, int64_t bsc, int32_t M, int32_t N, int32_t K,
                         int32_t batch, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_generic_kernel<TA, TB, TC>), dim3(grid_of((int64_t)batch * M * N)), dim3(256),
+    launch_timed((gemm_generic_kernel<TA, TB, TC>), dim3(grid_of((int64_t)batch * M * N)), dim3(256),
                        0, s, A, lda, bsa, B, sbk, sbn, bsb, C, ldc, bsc, M, N, K, batch);
     return hipGetLastError();
 }
@@ -382,17 +382,17 @@ hipError_t launch_cache_append(const void *h, const void *w_kv, mla_dtype_t dt, 
     a.d_c = d_c; a.d_r = d_r;
     const unsigned rows_grid = (unsigned)(((int64_t)T * (N / 2) + 255) / 256);
     if (kv == MLA_DT_F32)
-        hipLaunchKernelGGL(append_rows_kernel<0>, dim3(rows_grid), dim3(256), 0, s, a, rt);
+        launch_timed(append_rows_kernel<0>, dim3(rows_grid), dim3(256), 0, s, a, rt);
     else if (kv == MLA_DT_BF16)
-        hipLaunchKernelGGL(append_rows_kernel<1>, dim3(rows_grid), dim3(256), 0, s, a, rt);
+        launch_timed(append_rows_kernel<1>, dim3(rows_grid), dim3(256), 0, s, a, rt);
     else if (kv == MLA_DT_F16)
-        hipLaunchKernelGGL(append_rows_kernel<2>, dim3(rows_grid), dim3(256), 0, s, a, rt);
+        launch_timed(append_rows_kernel<2>, dim3(rows_grid), dim3(256), 0, s, a, rt);
     else if (kv == MLA_DT_FP8_E4M3)
-        hipLaunchKernelGGL(append_fp8_kernel<0>, dim3(B), dim3(256), 0, s, a, rt);
+        launch_timed(append_fp8_kernel<0>, dim3(B), dim3(256), 0, s, a, rt);
     else if (kv == MLA_DT_FP8_E5M2)
-        hipLaunchKernelGGL(append_fp8_kernel<1>, dim3(B), dim3(256), 0, s, a, rt);
+        launch_timed(append_fp8_kernel<1>, dim3(B), dim3(256), 0, s, a, rt);
     else
-        hipLaunchKernelGGL(append_fp8_kernel<2>, dim3(B), dim3(256), 0, s, a, rt);
+        launch_timed(append_fp8_kernel<2>, dim3(B), dim3(256), 0, s, a, rt);
     return hipGetLastError();
 }
 
@@ -488,10 +488,10 @@ hipError_t launch_project_q(const void *h, const void *w_dq, const void *w_uq, c
     const float *w3 = (const float *)(w + q.off_w3);
     const unsigned rg = (unsigned)(((int64_t)T * n_h * (d_r / 2) + 255) / 256);
     if (dt == MLA_DT_BF16)
-        hipLaunchKernelGGL(rope_q_kernel<uint16_t>, dim3(rg), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
+        launch_timed(rope_q_kernel<uint16_t>, dim3(rg), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
                            T, n_h, d_r, (uint16_t *)q_rope, rt);
     else
-        hipLaunchKernelGGL(rope_q_kernel<float>, dim3(rg), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
+        launch_timed(rope_q_kernel<float>, dim3(rg), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
                            T, n_h, d_r, (float *)q_rope, rt);
     return hipGetLastError();
 }

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void clock_probe_kernel(int64_t *__restrict__ 
 }
 
 hipError_t launch_clock_probe(int64_t *out, int32_t wgs, int32_t iters, hipStream_t s) {
-    hipLaunchKernelGGL(clock_probe_kernel, dim3(wgs), dim3(256), 0, s, out, iters);
+    launch_timed(clock_probe_kernel, dim3(wgs), dim3(256), 0, s, out, iters);
     return hipGetLastError();
 }
 
@@ -268,7 +268,7 @@ hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int64_t num_b
                          const int32_t *seq_lens, int32_t B, int32_t max_tokens, uint8_t *out,
                          hipStream_t s) {
     dim3 grid((max_tokens + 15) / 16, B);
-    hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, pool, block_bytes, c_bytes, r_bytes,
+    launch_timed(gather_kernel, grid, dim3(256), 0, s, pool, block_bytes, c_bytes, r_bytes,
                        (int32_t)split_rows, bt, bt_stride, seq_lens, max_tokens, num_blocks, out);
     return hipGetLastError();
 }
@@ -280,29 +280,29 @@ hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *
     dim3 grid((rows + 3) / 4, B);
     if (part_dt == MLA_DT_BF16 && d_c == 512) {
         if (out_dt == MLA_DT_BF16)
-            hipLaunchKernelGGL(combine512_kernel<uint16_t>, grid, dim3(256), 0, s,
+            launch_timed(combine512_kernel<uint16_t>, grid, dim3(256), 0, s,
                                (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows,
                                chunk_rows, (uint16_t *)o_lat, lse);
         else
-            hipLaunchKernelGGL(combine512_kernel<float>, grid, dim3(256), 0, s,
+            launch_timed(combine512_kernel<float>, grid, dim3(256), 0, s,
                                (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows,
                                chunk_rows, (float *)o_lat, lse);
     } else if (part_dt == MLA_DT_BF16) {
         if (out_dt == MLA_DT_BF16)
-            hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s,
+            launch_timed((combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s,
                                (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, chunk_rows, d_c,
                                (uint16_t *)o_lat, lse);
         else
-            hipLaunchKernelGGL((combine_kernel<uint16_t, float>), grid, dim3(256), 0, s,
+            launch_timed((combine_kernel<uint16_t, float>), grid, dim3(256), 0, s,
                                (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows, chunk_rows, d_c,
                                (float *)o_lat, lse);
     } else {
         if (out_dt == MLA_DT_BF16)
-            hipLaunchKernelGGL((combine_kernel<float, uint16_t>), grid, dim3(256), 0, s,
+            launch_timed((combine_kernel<float, uint16_t>), grid, dim3(256), 0, s,
                                (const float *)o_part, lse_part, split_off, seq_flags, rows, chunk_rows, d_c,
                                (uint16_t *)o_lat, lse);
         else
-            hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(256), 0, s,
+            launch_timed((combine_kernel<float, float>), grid, dim3(256), 0, s,
                                (const float *)o_part, lse_part, split_off, seq_flags, rows, chunk_rows, d_c,
                                (float *)o_lat, lse);
     }

@@ -182,3 +182,32 @@ def test_score_chain_wait_states(decode_asm):
 def test_score_chain_result_latency(decode_asm):
     bad = check_results(decode_asm)
     assert not bad, "\n".join(f"line {a}: {b} -> {c}" for a, b, c in bad[:20])
+
+
+def kernel_bodies(lines):
+    """{kernel symbol: its instruction lines} of a gfx950 assembly listing."""
+    out = {}
+    for n, line in enumerate(lines):
+        m = re.match(r"^(_Z\w*(decode_mfma_kernel|decode_f8mma_kernel)\w*):", line)
+        if m:
+            end = next(k for k in range(n, len(lines)) if "s_endpgm" in lines[k])
+            out[m.group(1)] = lines[n:end]
+    return out
+
+
+def test_no_scratch_access_in_the_stage_loop(decode_asm):
+    """A spill reload inside the stage loop is a vector-memory load the
+    compiler waits for with vmcnt(0), which also waits for every stage copy
+    in flight (the copies are inline asm, invisible to its counting): one
+    such reload per iteration drains the copy pipeline.  The stage loop runs
+    from the first MFMA after the prologue to the last MFMA of the kernel
+    (the 16-bit kernel scores stage 0 in its prologue with 36 MFMAs; the
+    8-bit kernel has none before its loop)."""
+    bodies = kernel_bodies(decode_asm)
+    assert bodies
+    for name, body in bodies.items():
+        mf = [i for i, l in enumerate(body) if re.match(r"\s+v_mfma", l)]
+        skip = 36 if "decode_mfma_kernel" in name else 0
+        lo, hi = mf[skip], mf[-1]
+        bad = [body[i].strip() for i in range(lo, hi) if "scratch_" in body[i]]
+        assert not bad, f"{name}: {bad[:4]}"
