@@ -297,6 +297,27 @@ class Timer:
         per = [sum(evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(K)) / K for j in range(n_k)]
         return wall * 1e3 / K, e0.elapsed_time(e1) / K, per
 
+    def launch_means(self, lib, fn, argsets, K, check, n_max=16):
+        """Per-launch mean duration (us) of the kernels one call of fn makes,
+        stamped from their own dispatch, over K calls: [launch 0, launch 1, ...]."""
+        evs = [[self.ev() for _ in range(2 * n_max)] for _ in range(K)]
+        for e in (x for row in evs for x in row):
+            e.record(self.stream)
+        handles = [(ctypes.c_void_p * (2 * n_max))(*[e.cuda_event for e in row]) for row in evs]
+        self.torch.cuda.synchronize()
+        st, used = 0, None
+        for i in range(K):
+            st |= lib.mla_set_launch_events(handles[i], n_max)
+            st |= fn(*argsets[i % len(argsets)])
+            u = lib.mla_launch_events_used()
+            assert used in (None, u), "a call's launch count changed between calls"
+            used = u
+        st |= lib.mla_set_launch_events(None, 0)
+        self.torch.cuda.synchronize()
+        check(st)
+        return [round(sum(evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(K)) / K * 1e3, 2)
+                for j in range(used)]
+
     def per_call(self, step, n, check):
         pairs = [(self.ev(), self.ev()) for _ in range(n)]
         st = 0
@@ -671,6 +692,9 @@ def run_layer(args, wl, producers=False):
             "project_q_bytes": b_pq,
             "cache_append_us": round(ca_ms * 1e3, 2), "cache_append_gbs": round(b_ca / (ca_ms * 1e-3) / 1e9, 1),
             "cache_append_bytes": b_ca,
+            # each launch of one call, stamped from its own dispatch (us, in launch order)
+            "project_q_launch_us": timer.launch_means(lib, lib.mla_project_q, [pq], n_leg, L.check),
+            "cache_append_launch_us": timer.launch_means(lib, lib.mla_cache_append, cas, n_leg, L.check),
         }
         out["tflops"] = None
         del out["absorb_q_us"]

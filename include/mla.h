@@ -442,9 +442,12 @@ mla_status_t mla_clock_probe(int64_t *out, int32_t wgs, int32_t iters, mla_strea
  * the kernel's duration).  The timestamps come from the kernel's dispatch
  * (hipExtLaunchKernel), so no marker enters the stream between launches.
  * Pairs a call does not consume are dropped by the next call to this
- * function.  INVALID_ARG for pairs outside [0, 4] or NULL events.
+ * function.  INVALID_ARG for pairs outside [0, 16] or NULL events.
+ * mla_launch_events_used returns how many of the pairs set last have been
+ * consumed by launches on the calling thread.
  */
 mla_status_t mla_set_launch_events(void *const *events, int32_t pairs);
+int32_t mla_launch_events_used(void);
 
 /* Bytes of the whole pool described by `cache` (0 on bad arguments). */
 int64_t mla_cache_bytes(const mla_cache_desc_t *cache);

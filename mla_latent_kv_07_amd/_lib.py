@@ -104,6 +104,8 @@ def load() -> ctypes.CDLL:
                                 c_int32, c_int32, c_int32, ctypes.POINTER(Rope), P, P, P, c_int64, P]
     L.mla_set_launch_events.argtypes = [P, c_int32]
     L.mla_set_launch_events.restype = c_int32
+    L.mla_launch_events_used.argtypes = []
+    L.mla_launch_events_used.restype = c_int32
     L.mla_clock_probe.argtypes = [P, c_int32, c_int32, P]
     L.mla_clock_probe.restype = c_int32
     L.mla_last_error.restype = ctypes.c_char_p

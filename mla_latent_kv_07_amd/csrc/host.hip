@@ -18,7 +18,7 @@ namespace {
 thread_local char g_err[512] = "";
 
 // measurement events for the next kernel launches of this thread
-constexpr int kMaxTimedLaunches = 4;
+constexpr int kMaxTimedLaunches = 16;
 thread_local LaunchTiming g_timing[kMaxTimedLaunches];
 thread_local int g_timing_n = 0, g_timing_next = 0;
 
@@ -118,6 +118,8 @@ mla_status_t mla_set_launch_events(void *const *events, int32_t pairs) {
     g_timing_next = 0;
     return ok();
 }
+
+int32_t mla_launch_events_used(void) { return g_timing_next; }
 
 const char *mla_version(void) { return "mla-mi355x 0.1.0 (gfx950)"; }
 

@@ -8,7 +8,10 @@
 //                     (§3-1 absorption), q^R = RoPE(h W^QR) (§2-3)
 // Products run on the bf16 MFMA GEMM (split over K into fp32 partials when
 // the output is small); a finishing kernel sums the partials and applies the
-// rotation, the storage rounding and, for fp8 caches, the block scale.
+// rotation, the storage rounding and, for fp8 caches, the block scale.  On
+// the MFMA path the queries take three launches: h W^QR with h W^DQ, the
+// finish of both (q^R rotated, c^Q rounded to bf16), then c^Q W^UQ with the
+// absorption by W^UK^T fused behind it (q^C never leaves the chip).
 // RoPE frequencies are plain (theta_j = base^(-2j/d)) or YaRN-scaled; the
 // huny page names YaRN for 128K+ contexts (§6, YaRN item) without a
 // formula: the table follows the published YaRN NTK-by-parts interpolation.
@@ -26,6 +29,13 @@ hipError_t launch_gemm_nn_bf16(const void *A, int64_t lda, const void *B, int64_
                                int64_t ldc, int32_t M, int32_t N, int32_t K, hipStream_t s);
 hipError_t launch_split_sum_bf16(const float *ws, int splits, int64_t split_stride, int64_t n8,
                                  void *out, hipStream_t s);
+bool q_up_absorb_ok(int32_t T, int32_t n_h, int32_t d_nope, int32_t d_c, int32_t q_lora);
+hipError_t launch_q_up_absorb(const void *cq, int64_t ld_cq, const void *w_uq, const void *w_uk, void *q_lat,
+                              int32_t T, int32_t n_h, int32_t q_lora, hipStream_t s);
+void gemm_pair_splits(int32_t M, int32_t N0, int32_t K0, int32_t N1, int32_t K1, int *s0, int *s1);
+hipError_t launch_gemm_nn_f32_pair(const void *A, int64_t lda, int32_t M, int32_t K, const void *B0, int64_t ldb0,
+                                   float *ws0, int32_t N0, int splits0, const void *B1, int64_t ldb1, float *ws1,
+                                   int32_t N1, int splits1, hipStream_t s);
 
 bool rope_table(const mla_rope_t *r, int32_t d_r, RopeTab *t) {
     if (!r || d_r < 2 || d_r % 2 || d_r / 2 > kMaxRopePairs) return false;
@@ -105,18 +115,19 @@ __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
     return (c & 0x80) ? -v : v;
 }
 
-// sum over splits of ws[s * stride + i] (independent loads in flight)
+// sum over splits of ws[s * stride + i]: the first 16 splits' loads are all
+// issued before the first add (one memory latency for the usual split
+// counts), any further ones in turn
 __device__ __forceinline__ float split_sum(const float *__restrict__ ws, int64_t stride, int splits, int64_t i) {
-    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-    int s = 0;
-    for (; s + 4 <= splits; s += 4) {
-        v0 += ws[(s + 0) * stride + i];
-        v1 += ws[(s + 1) * stride + i];
-        v2 += ws[(s + 2) * stride + i];
-        v3 += ws[(s + 3) * stride + i];
-    }
-    for (; s < splits; ++s) v0 += ws[s * stride + i];
-    return (v0 + v1) + (v2 + v3);
+    float v[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) v[s] = s < splits ? ws[s * stride + i] : 0.f;
+#pragma unroll
+    for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+        for (int s = 0; s < w; ++s) v[s] += v[s + w];
+    for (int s = 16; s < splits; ++s) v[0] += ws[s * stride + i];
+    return v[0];
 }
 
 struct AppendArgs {
@@ -273,13 +284,11 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab 
 }
 
 // q^R: out[t][h][2j, 2j+1] = RoPE of the summed partials at pos[t], times
-// mscale; one thread per (token, head, pair), angle p theta_j in fp64.
+// mscale; item idx = (token, head, pair), angle p theta_j in fp64.
 template <typename OutT>
-__global__ __launch_bounds__(256) void rope_q_kernel(const float *__restrict__ ws, int64_t split_stride,
-                                                     int32_t splits, const int32_t *__restrict__ pos,
-                                                     int32_t T, int32_t n_h, int32_t d_r, OutT *__restrict__ out,
-                                                     RopeTab rt) {
-    const int64_t idx = blockIdx.x * 256ll + threadIdx.x;
+__device__ __forceinline__ void rope_q_item(int64_t idx, const float *__restrict__ ws, int64_t split_stride,
+                                            int32_t splits, const int32_t *__restrict__ pos, int32_t T, int32_t n_h,
+                                            int32_t d_r, OutT *__restrict__ out, const RopeTab &rt) {
     const int64_t per_t = (int64_t)n_h * rt.half;
     if (idx >= T * per_t) return;
     const int t = (int)(idx / per_t), hj = (int)(idx % per_t);
@@ -296,6 +305,59 @@ __global__ __launch_bounds__(256) void rope_q_kernel(const float *__restrict__ w
         out[o] = y0;
         out[o + 1] = y1;
     }
+}
+
+// one thread per (token, head, pair)
+template <typename OutT>
+__global__ __launch_bounds__(256) void rope_q_kernel(const float *__restrict__ ws, int64_t split_stride,
+                                                     int32_t splits, const int32_t *__restrict__ pos,
+                                                     int32_t T, int32_t n_h, int32_t d_r, OutT *__restrict__ out,
+                                                     RopeTab rt) {
+    rope_q_item(blockIdx.x * 256ll + threadIdx.x, ws, split_stride, splits, pos, T, n_h, d_r, out, rt);
+}
+
+// The two finishes of the low-rank query products in one launch: blocks
+// [0, nb_cq) write c^Q = bf16(sum of the h W^DQ partials), 8 consecutive
+// values per thread; the others q^R = RoPE(sum of the h W^QR partials), one
+// rotary pair per thread.
+__global__ __launch_bounds__(256) void q_finish_kernel(const float *__restrict__ ws1, int32_t sp1, int64_t n8,
+                                                       uint16_t *__restrict__ cq, int32_t nb_cq,
+                                                       const float *__restrict__ ws3, int32_t sp3,
+                                                       const int32_t *__restrict__ pos, int32_t T, int32_t n_h,
+                                                       int32_t d_r, uint16_t *__restrict__ q_rope, RopeTab rt) {
+    if ((int)blockIdx.x >= nb_cq) {
+        rope_q_item((blockIdx.x - nb_cq) * 256ll + threadIdx.x, ws3, (int64_t)T * n_h * d_r, sp3, pos, T, n_h, d_r,
+                    q_rope, rt);
+        return;
+    }
+    const int64_t i = blockIdx.x * 256ll + threadIdx.x;
+    if (i >= n8) return;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // four splits' loads in flight per round
+    for (int s0 = 0; s0 < sp1; s0 += 4) {
+        float4 x[4], y[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (s0 + k < sp1) {
+                const float4 *p = (const float4 *)(ws1 + (int64_t)(s0 + k) * n8 * 8 + 8 * i);
+                x[k] = p[0];
+                y[k] = p[1];
+            } else {
+                x[k] = y[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[0] += x[k].x; a[1] += x[k].y; a[2] += x[k].z; a[3] += x[k].w;
+            a[4] += y[k].x; a[5] += y[k].y; a[6] += y[k].z; a[7] += y[k].w;
+        }
+    }
+    uint4 pk;
+    pk.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
+    pk.z = (uint32_t)f32_to_bf16(a[4]) | ((uint32_t)f32_to_bf16(a[5]) << 16);
+    pk.w = (uint32_t)f32_to_bf16(a[6]) | ((uint32_t)f32_to_bf16(a[7]) << 16);
+    *(uint4 *)(cq + 8 * i) = pk;
 }
 
 template <typename T>
@@ -412,8 +474,9 @@ QPlan q_plan(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_
     const int32_t NQ = n_h * d_nope, NR = n_h * d_r;
     q.mfma = dt == MLA_DT_BF16 && gemm_nn_mfma_ok(q_lora, d_model) && gemm_nn_mfma_ok(NQ, q_lora) &&
              gemm_nn_mfma_ok(NR, d_model) && d_nope % 64 == 0 && d_c % 128 == 0;
-    q.sp1 = q.mfma ? gemm_splits(T, q_lora, d_model) : 1;
-    q.sp3 = q.mfma ? gemm_splits(T, NR, d_model) : 1;
+    q.sp1 = q.sp3 = 1;
+    // h W^QR and h W^DQ share one launch
+    if (q.mfma) gemm_pair_splits(T, NR, d_model, q_lora, d_model, &q.sp3, &q.sp1);
     // c^Q and q^C: bf16 on the MFMA path (the next product's operand), fp32 otherwise
     const int eb = q.mfma ? 2 : 4;
     int64_t o = 0;
@@ -442,21 +505,29 @@ hipError_t launch_project_q(const void *h, const void *w_dq, const void *w_uq, c
     uint8_t *w = (uint8_t *)ws;
     hipError_t e;
     if (q.mfma) {
-        // c^Q = h W^DQ (split over d_model, summed and rounded to bf16)
-        float *w1 = (float *)(w + q.off_w1);
-        e = launch_gemm_nn_f32(h, d_model, w_dq, q_lora, w1, T, q_lora, d_model, q.sp1, s);
+        // h W^QR and h W^DQ (split over d_model into fp32 partials) in one launch
+        float *w1 = (float *)(w + q.off_w1), *w3 = (float *)(w + q.off_w3);
+        e = launch_gemm_nn_f32_pair(h, d_model, T, d_model, w_qr, NR, w3, NR, q.sp3, w_dq, q_lora, w1, q_lora,
+                                    q.sp1, s);
         if (e != hipSuccess) return e;
-        e = launch_split_sum_bf16(w1, q.sp1, (int64_t)T * q_lora, (int64_t)T * q_lora / 8, w + q.off_cq, s);
+        // c^Q = bf16(sum of its partials) and q^R = RoPE(sum of its partials)
+        const int64_t n8 = (int64_t)T * q_lora / 8;
+        const int nb_cq = (int)((n8 + 255) / 256);
+        const int64_t nrope = (int64_t)T * n_h * (d_r / 2);
+        const unsigned nb = (unsigned)(nb_cq + (nrope + 255) / 256);
+        launch_timed(q_finish_kernel, dim3(nb), dim3(256), 0, s, (const float *)w1, (int32_t)q.sp1, n8,
+                     (uint16_t *)(w + q.off_cq), (int32_t)nb_cq, (const float *)w3, (int32_t)q.sp3, pos, T, n_h,
+                     d_r, (uint16_t *)q_rope, rt);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
+        // q~ = (c^Q W^UQ) W^UK^T per head, q^C kept on chip
+        if (q_up_absorb_ok(T, n_h, d_nope, d_c, q_lora))
+            return launch_q_up_absorb(w + q.off_cq, q_lora, w_uq, w_uk, q_lat, T, n_h, q_lora, s);
         // q^C = c^Q W^UQ
         e = launch_gemm_nn_bf16(w + q.off_cq, q_lora, w_uq, NQ, w + q.off_qc, NQ, T, NQ, q_lora, s);
         if (e != hipSuccess) return e;
         // q~ = q^C W^UK^T per head
-        e = launch_absorb_q(w + q.off_qc, NQ, w_uk, q_lat, T, n_h, d_nope, d_c, dt, s);
-        if (e != hipSuccess) return e;
-        // h W^QR, rotated below
-        e = launch_gemm_nn_f32(h, d_model, w_qr, NR, (float *)(w + q.off_w3), T, NR, d_model, q.sp3, s);
-        if (e != hipSuccess) return e;
+        return launch_absorb_q(w + q.off_qc, NQ, w_uk, q_lat, T, n_h, d_nope, d_c, dt, s);
     } else {
         float *cq = (float *)(w + q.off_cq), *qc = (float *)(w + q.off_qc), *w3 = (float *)(w + q.off_w3);
         if (dt == MLA_DT_BF16) {

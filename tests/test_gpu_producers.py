@@ -209,7 +209,7 @@ def test_append_full_size_decode_step():
     _check_16bit_rows(got, pool, mask, "bf16")
 
 
-@pytest.mark.parametrize("T", [128, 3])
+@pytest.mark.parametrize("T", [128, 3, 130])
 def test_project_q_full_shape(T):
     """DeepSeek-V2 query path, d_model 5120, q_lora 1536, 128 heads: the MFMA
     chain against the fp64 oracle from the same bf16 inputs."""
