@@ -478,14 +478,6 @@ def run_decode(args, wl):
         L.check(step(i))
     torch.cuda.synchronize()
     K = args.steps
-    # the timed steps: K back-to-back mla_decode calls between HIP events on
-    # the launch stream.  When the decode merges its own splits (the MFMA
-    # kernels with bf16 queries), a step is one launch and the decode
-    # kernel's average launch time is the step time by construction.
-    # Otherwise a second timed pass records events before, between and after
-    # the two launches of every step (decode, then combine) for the per-kernel
-    # split; those events lengthen the step, so the headline stays the plain
-    # pass.
     # The headline: K plain mla_decode calls between two HIP events on the
     # launch stream.  Then the same K calls again, each call's kernels
     # stamping their own start and stop times (mla_set_launch_events, from

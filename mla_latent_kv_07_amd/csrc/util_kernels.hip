@@ -175,8 +175,10 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
 #pragma unroll
     for (int u = 0; u < U; ++u)
         v[u] = u < n ? *(const uint4 *)(src0 + u * split_stride) : make_uint4(0, 0, 0, 0);
-    float m = -INFINITY;
-    for (int c = 0; c < n; c += 64)
+    // lane j holds the lse of split j (the first 64), loaded with the rows
+    const float l0 = lane < n ? lse_part[(int64_t)(k0 + lane) * rows + r] : -INFINITY;
+    float m = l0;
+    for (int c = 64; c < n; c += 64)
         if (c + lane < n) m = fmaxf(m, lse_part[(int64_t)(k0 + c + lane) * rows + r]);
     m = wave_max(m);
     uint4 *dst = (uint4 *)(o_lat + out_row * 512 + lane * 8);
@@ -196,8 +198,15 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
             for (int u = 0; u < U; ++u)
                 v[u] = c + u < n ? *(const uint4 *)(src0 + (c + u) * split_stride) : make_uint4(0, 0, 0, 0);
         }
-        // lane u of the wave holds the weight of split c + u
-        const float lk = lane < U && c + lane < n ? lse_part[(int64_t)(k0 + c + lane) * rows + r] : -INFINITY;
+        // lane u of the wave holds the weight of split c + u (the lse of the
+        // first 64 splits is already in l0, on lane c + u)
+        float lk;
+        if (c < 64) {
+            lk = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * ((c + lane) & 63), __float_as_int(l0)));
+            lk = lane < U && c + lane < n ? lk : -INFINITY;
+        } else {
+            lk = lane < U && c + lane < n ? lse_part[(int64_t)(k0 + c + lane) * rows + r] : -INFINITY;
+        }
         const float wk = lk == -INFINITY ? 0.f : __expf(lk - m);
         wsum += wave_sum(wk);
 #pragma unroll
