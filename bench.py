@@ -479,16 +479,22 @@ def run_decode(args, wl):
     torch.cuda.synchronize()
     K = args.steps
     # The headline: K plain mla_decode calls between two HIP events on the
-    # launch stream.  Then the same K calls again, each call's kernels
-    # stamping their own start and stop times (mla_set_launch_events, from
-    # the dispatch itself) for the per-kernel durations: the runtime follows
-    # such a stamped launch with a cache flush that lengthens the step, so
-    # that pass gives durations, not the step time.
+    # launch stream (the kernels run back to back, no gap between them).
+    # The decode kernel's average launch time: K back-to-back launches of the
+    # decode kernel alone (mla_decode_partial) right after, between two HIP
+    # events, in the same sustained-load state as the timed steps (the
+    # kernel runs markedly faster after an idle gap, so a launch timed
+    # alone would flatter it).  Then the same K steps again, each call's
+    # kernels stamping their own start and stop (mla_set_launch_events,
+    # from the dispatch itself) for the combine's share: the runtime follows
+    # such a stamped launch with a cache flush, so those durations run on an
+    # idler chip and are reported beside.  The combine's share of a step: the
+    # step less the decode leg.
     n_k = 2 if dec.info.needs_combine else 1
     ms_per_step, gpu_ms = timer.steps(step, K, L.check)
+    dec_ms = timer.legs(part, call_args, K, L.check)
     _, stamped_ms, per = timer.kernel_steps(lib, step, n_k, K, L.check)
-    dec_ms = per[0]
-    comb_ms = per[1] if n_k == 2 else 0.0
+    comb_ms = max(gpu_ms - dec_ms, 0.0) if n_k == 2 else 0.0
     n_leg = max(K, 50)
     call_us = timer.per_call(step, n_leg, L.check)
     clock = shader_clock_mhz(torch, timer, lib, step)
@@ -521,8 +527,10 @@ def run_decode(args, wl):
         "call_us": call_us,
         "decode_kernel_us": round(dec_ms * 1e3, 2),
         "combine_kernel_us": round(comb_ms * 1e3, 2),
+        "kernel_time_how": ("decode: K back-to-back mla_decode_partial launches right after the timed steps; "
+                            "combine: the timed step less that"),
         "launches_per_step": n_k,
-        "kernel_us_sum": round(sum(per) * 1e3, 2),
+        "stamped_launch_us": [round(x * 1e3, 2) for x in per],
         "stamped_pass_us_per_step": round(stamped_ms * 1e3, 2),
         "shader_clock_mhz": clock,
         "roofline": roofline(wl, kernel, dec_ms, cache_bytes, flops, traffic_for(kernel, wl.name)),
