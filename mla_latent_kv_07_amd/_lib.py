@@ -10,7 +10,9 @@ import ctypes
 import os
 from pathlib import Path
 
-LIB_PATH = Path(__file__).resolve().parent / "libmla.so"
+# MLA_LIB names another build of the same library (the host-sanitizer build
+# the CPU tests make); by default the in-tree one
+LIB_PATH = Path(os.environ.get("MLA_LIB") or Path(__file__).resolve().parent / "libmla.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(6)
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGN", 4: "WORKSPACE", 5: "HIP"}

@@ -118,7 +118,9 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        so = build_oracle()
+        # MLA_ORACLE_LIB names another build of mla_oracle.c (the
+        # host-sanitizer build the CPU tests make)
+        so = os.environ.get("MLA_ORACLE_LIB") or build_oracle()
         L = ctypes.CDLL(str(so))
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
