@@ -19,7 +19,9 @@
  * Conventions shared by every call:
  *   - Pointers are device pointers unless the name ends in _host.
  *   - The caller owns every buffer; the library allocates nothing and keeps
- *     no device state between calls.
+ *     no device state between calls, apart from mla_decode_noalloc's scratch
+ *     and the device checks' flag (mla_set_debug), both file-scope device
+ *     arrays.
  *   - Calls are asynchronous on `stream`; host-side argument checks run before
  *     any launch and a failing check launches nothing.
  *   - Every call returns an mla_status_t; mla_last_error() returns a
@@ -46,7 +48,9 @@ typedef enum {
     MLA_ERR_UNSUPPORTED = 2,  /* block size != 64, dtype or dims not instantiated */
     MLA_ERR_ALIGN = 3,        /* pointer or row not 16-byte aligned */
     MLA_ERR_WORKSPACE = 4,    /* workspace smaller than the plan needs */
-    MLA_ERR_HIP = 5           /* a HIP launch or runtime call failed */
+    MLA_ERR_HIP = 5,          /* a HIP launch or runtime call failed */
+    MLA_ERR_DEVICE_CHECK = 6  /* device checks on (mla_set_debug): the block table or
+                                 sequence lengths on the device are out of range */
 } mla_status_t;
 
 typedef enum {
@@ -448,6 +452,25 @@ mla_status_t mla_clock_probe(int64_t *out, int32_t wgs, int32_t iters, mla_strea
  */
 mla_status_t mla_set_launch_events(void *const *events, int32_t pairs);
 int32_t mla_launch_events_used(void);
+
+/*
+ * mla_set_debug / mla_debug — device checks of the data the host cannot see
+ * (SURVEY's sanitizer item for the decode: block ids and slots).  When on,
+ * mla_decode, mla_decode_partial, mla_decode_noalloc and mla_gather_paged,
+ * after their host checks, first run a check kernel on `stream` over the
+ * device block table and sequence lengths and wait for it; if any sequence
+ * length is negative or above 64 * bt_stride, or any table entry for a
+ * position below its sequence's length lies outside [0, num_blocks), the
+ * call launches nothing else and returns MLA_ERR_DEVICE_CHECK, naming the
+ * first offence in mla_last_error().  The checked calls synchronize the
+ * stream (not for graph capture) and share one flag per device, so checked
+ * calls that overlap on one GPU race.  Off by default; the environment
+ * variable MLA_DEBUG set to a non-zero integer turns it on at the first
+ * call that consults it.  mla_set_debug(0 | 1) overrides; mla_debug returns
+ * the current state.
+ */
+mla_status_t mla_set_debug(int32_t on);
+int32_t mla_debug(void);
 
 /* Bytes of the whole pool described by `cache` (0 on bad arguments). */
 int64_t mla_cache_bytes(const mla_cache_desc_t *cache);

@@ -14,8 +14,10 @@ from pathlib import Path
 # the CPU tests make); by default the in-tree one
 LIB_PATH = Path(os.environ.get("MLA_LIB") or Path(__file__).resolve().parent / "libmla.so")
 
-MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(6)
-STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGN", 4: "WORKSPACE", 5: "HIP"}
+(MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_HIP,
+ MLA_ERR_DEVICE_CHECK) = range(7)
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGN", 4: "WORKSPACE", 5: "HIP",
+                6: "DEVICE_CHECK"}
 DT_F32, DT_BF16, DT_FP8_E4M3, DT_F16, DT_FP8_E5M2, DT_FP8_E4M3_ROW = 0, 1, 2, 3, 4, 5
 BLOCK_SIZE = 64
 CACHE_FP8_EXACT = 1   # mla_cache_desc_t.flags: exact fp8 decode on 16-bit MFMAs
@@ -108,6 +110,10 @@ def load() -> ctypes.CDLL:
     L.mla_set_launch_events.restype = c_int32
     L.mla_launch_events_used.argtypes = []
     L.mla_launch_events_used.restype = c_int32
+    L.mla_set_debug.argtypes = [c_int32]
+    L.mla_set_debug.restype = c_int32
+    L.mla_debug.argtypes = []
+    L.mla_debug.restype = c_int32
     L.mla_clock_probe.argtypes = [P, c_int32, c_int32, P]
     L.mla_clock_probe.restype = c_int32
     L.mla_last_error.restype = ctypes.c_char_p

@@ -82,6 +82,8 @@ hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int64_t num_b
                          int32_t r_bytes, bool split_rows, const int32_t *bt, int32_t bt_stride,
                          const int32_t *seq_lens, int32_t B, int32_t max_tokens, uint8_t *out,
                          hipStream_t s);
+hipError_t launch_table_check(const int32_t *bt, int64_t bt_stride, const int32_t *seq_lens, int32_t B,
+                              int64_t num_blocks, int32_t *flag, hipStream_t s);
 hipError_t launch_clock_probe(int64_t *out, int32_t wgs, int32_t iters, hipStream_t s);
 hipError_t launch_absorb_q(const void *q_nope, int64_t ld_q, const void *w_uk, void *q_lat,
                            int32_t T, int32_t n_h, int32_t d_nope, int32_t d_c, mla_dtype_t dt,

@@ -2,8 +2,10 @@
 // dispatch.  Argument checks and the planner make no HIP call, so they run
 // (and are tested) on machines without a GPU.
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <queue>
@@ -422,6 +424,16 @@ mla_status_t finish_decode(const mla_plan_t *plan, const int32_t *plan_dev, void
 
 }  // namespace
 
+}  // extern "C"
+
+namespace {
+bool debug_on();
+mla_status_t device_check(const int32_t *bt, int32_t bt_stride, const int32_t *seq_lens, int32_t B,
+                          int64_t num_blocks, hipStream_t s);
+}  // namespace
+
+extern "C" {
+
 mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
                         const mla_cache_desc_t *cache, const int32_t *block_table,
                         int32_t bt_stride, const int32_t *seq_lens, int32_t B, int32_t q_len,
@@ -434,6 +446,10 @@ mla_status_t mla_decode(const void *q_lat, const void *q_rope, mla_dtype_t q_dty
                                      workspace_bytes, o_lat, lse, &a);
     if (st != MLA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (debug_on()) {
+        st = device_check(block_table, bt_stride, seq_lens, B, cache->num_blocks, s);
+        if (st != MLA_OK) return st;
+    }
     hipError_t e = launch_decode(a, s);
     if (e != hipSuccess) return hip_status(e, "decode launch");
     return finish_decode(plan, plan_dev, workspace, q_dtype, o_lat, lse, s);
@@ -472,7 +488,73 @@ mla_status_t scratch_address(void **ptr) {
 
 }  // namespace
 
+namespace {
+
+// Device checks (mla_set_debug): the offence counter and the first offence,
+// one copy per GPU, zero between checks (a failing check clears it).
+static __device__ __align__(16) int32_t check_flag[4];
+
+std::atomic<int> g_debug{-1};   // -1: MLA_DEBUG not read yet
+void *g_check_ptr[kMaxDevices] = {};
+
+bool debug_on() {
+    int d = g_debug.load();
+    if (d < 0) {
+        const char *e = std::getenv("MLA_DEBUG");
+        d = (e && std::atoi(e) != 0) ? 1 : 0;
+        int expect = -1;
+        if (!g_debug.compare_exchange_strong(expect, d)) d = g_debug.load();
+    }
+    return d > 0;
+}
+
+mla_status_t device_check(const int32_t *bt, int32_t bt_stride, const int32_t *seq_lens, int32_t B,
+                          int64_t num_blocks, hipStream_t s) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    int32_t *flag = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_check_ptr[dev]) {
+            void *p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(check_flag));
+            if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(check_flag)");
+            if (!p) return fail(MLA_ERR_HIP, "hipGetSymbolAddress(check_flag) returned NULL");
+            g_check_ptr[dev] = p;
+        }
+        flag = (int32_t *)g_check_ptr[dev];
+    }
+    e = launch_table_check(bt, bt_stride, seq_lens, B, num_blocks, flag, s);
+    if (e != hipSuccess) return hip_status(e, "device check launch");
+    int32_t h[4] = {0, 0, 0, 0};
+    e = hipMemcpyAsync(h, flag, sizeof(h), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "device check read-back");
+    if (h[0] == 0) return MLA_OK;
+    static const int32_t zeros[4] = {0, 0, 0, 0};
+    e = hipMemcpyAsync(flag, zeros, sizeof(zeros), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "device check reset");
+    if (h[2] < 0)
+        return fail(MLA_ERR_DEVICE_CHECK, "device check: %d offences; first: sequence %d has length %d, outside "
+                    "[0, 64 * bt_stride = %lld]", h[0], h[1], h[3], (long long)kBlock * bt_stride);
+    return fail(MLA_ERR_DEVICE_CHECK, "device check: %d offences; first: sequence %d, table entry %d holds block id "
+                "%d, outside [0, %lld)", h[0], h[1], h[2], h[3], (long long)num_blocks);
+}
+
+}  // namespace
+
 extern "C" {
+
+mla_status_t mla_set_debug(int32_t on) {
+    if (on != 0 && on != 1) return fail(MLA_ERR_INVALID_ARG, "mla_set_debug takes 0 or 1, not %d", on);
+    g_debug.store(on);
+    return ok();
+}
+
+int32_t mla_debug(void) { return debug_on() ? 1 : 0; }
 
 mla_status_t mla_decode_noalloc(const void *q_lat, const void *q_rope, mla_dtype_t q_dtype,
                                 const mla_cache_desc_t *cache, const int32_t *block_table,
@@ -499,6 +581,10 @@ mla_status_t mla_decode_noalloc(const void *q_lat, const void *q_rope, mla_dtype
                         plan, plan_dev, ws, MLA_NOALLOC_SCRATCH_BYTES, o_lat, lse, &a);
     if (st != MLA_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (debug_on()) {
+        st = device_check(block_table, bt_stride, seq_lens, B, cache->num_blocks, s);
+        if (st != MLA_OK) return st;
+    }
     hipError_t e = launch_decode(a, s);
     if (e != hipSuccess) return hip_status(e, "decode launch");
     return finish_decode(plan, plan_dev, ws, q_dtype, o_lat, lse, s);
@@ -516,6 +602,10 @@ mla_status_t mla_decode_partial(const void *q_lat, const void *q_rope, mla_dtype
                                      B, q_len, n_h, scale, plan, plan_dev, workspace,
                                      workspace_bytes, o_lat, lse, &a);
     if (st != MLA_OK) return st;
+    if (debug_on()) {
+        st = device_check(block_table, bt_stride, seq_lens, B, cache->num_blocks, (hipStream_t)stream);
+        if (st != MLA_OK) return st;
+    }
     return hip_status(launch_decode(a, (hipStream_t)stream), "decode launch");
 }
 
@@ -692,6 +782,10 @@ mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *bloc
         return fail(MLA_ERR_INVALID_ARG, "max_tokens %d > %d positions of a block-table row", max_tokens,
                     kBlock * bt_stride);
     if (!aligned(out, 16)) return fail(MLA_ERR_ALIGN, "out not 16-byte aligned");
+    if (debug_on()) {
+        st = device_check(block_table, bt_stride, seq_lens, B, cache->num_blocks, (hipStream_t)stream);
+        if (st != MLA_OK) return st;
+    }
     int eb = elem_bytes(cache->kv_dtype);
     bool split = cache->kv_dtype == MLA_DT_FP8_E4M3 || cache->kv_dtype == MLA_DT_FP8_E5M2;
     int32_t c_bytes = split ? cache->d_c : (cache->d_c + cache->d_r) * eb;

@@ -238,6 +238,44 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
 
 }  // namespace
 
+// Device checks (on request only): flag[0] counts offences; the first one's
+// sequence, block index (-1: the sequence length itself) and value go to
+// flag[1..3].  One thread per block-table entry; a sequence's length is
+// checked by its entry 0.
+__global__ __launch_bounds__(256) void table_check_kernel(const int32_t *__restrict__ bt, int64_t bt_stride,
+                                                          const int32_t *__restrict__ seq_lens, int32_t B,
+                                                          int64_t num_blocks, int32_t *__restrict__ flag) {
+    auto record = [&](int b, int j, int v) {
+        if (atomicAdd(&flag[0], 1) == 0) {
+            flag[1] = b;
+            flag[2] = j;
+            flag[3] = v;
+        }
+    };
+    const int64_t total = (int64_t)B * bt_stride;
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int b = (int)(i / bt_stride);
+        const int64_t j = i - (int64_t)b * bt_stride;
+        const int S = seq_lens[b];
+        if (S < 0 || (int64_t)S > kBlock * bt_stride) {
+            if (j == 0) record(b, -1, S);
+            continue;
+        }
+        if (j * kBlock < S) {
+            const int id = bt[i];
+            if (id < 0 || id >= num_blocks) record(b, (int)j, id);
+        }
+    }
+}
+
+hipError_t launch_table_check(const int32_t *bt, int64_t bt_stride, const int32_t *seq_lens, int32_t B,
+                              int64_t num_blocks, int32_t *flag, hipStream_t s) {
+    const int64_t nb = ((int64_t)B * bt_stride + 255) / 256;
+    const unsigned grid = (unsigned)(nb < 1024 ? (nb < 1 ? 1 : nb) : 1024);
+    launch_timed(table_check_kernel, dim3(grid), dim3(256), 0, s, bt, bt_stride, seq_lens, B, num_blocks, flag);
+    return hipGetLastError();
+}
+
 // Shader-clock probe (a measurement helper, no step of the path): every wave
 // runs a dependent chain of `iters` bf16 32x32x16 MFMAs; lane 0 of each
 // workgroup records the shader cycles (s_memtime) and the 100 MHz real-time

@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import oracle as O
+from mla_latent_kv_07_amd import _lib as L
 from mla_latent_kv_07_amd import api
 from mla_latent_kv_07_amd import inputs as I
 
@@ -257,3 +258,55 @@ def test_decode_cache_format_variants_generic(kv):
     d = small(kv, seq=(1, 70, 200), n_h=8, d_c=64, d_r=16, seed=33)
     o, lse, _ = run_decode(d, cus=4)
     compare_decode(d, o, lse)
+
+
+def test_debug_device_checks_reject_bad_tables():
+    """With device checks on (mla_set_debug), a used block-table entry outside
+    the pool, or a sequence length beyond the table, is reported as
+    MLA_ERR_DEVICE_CHECK before any decode launch (the outputs keep their
+    sentinel); valid inputs, unused entries holding anything, decode as
+    without the checks.  The check kernel only reads the table and the
+    lengths: no decode runs on the bad ones."""
+    lib = L.load()
+    d = small("bf16", seq=(1, 100, 333), seed=11)
+    cache, bt, sl, ql, qr = to_device(d)
+    dec = api.Decoder(d.cache.seq_lens, 1, d.wl.n_h, d.wl.d_c, d.wl.d_r, "bf16", DEV)
+    assert bt.shape[1] >= 6
+    assert lib.mla_set_debug(1) == L.MLA_OK
+    try:
+        # unused entries (sequence 0 has one block) may hold anything
+        ok_bt = bt.clone()
+        ok_bt[0, 1:] = -7
+        o, lse = dec(ql, qr, cache, ok_bt, sl, d.scale)
+        torch.cuda.synchronize()
+        compare_decode(d, o, lse)
+
+        def rejected(table, lens, what):
+            o2 = torch.full_like(o, 7.0)
+            lse2 = torch.full_like(lse, 7.0)
+            with pytest.raises(L.MLAError) as ex:
+                dec(ql, qr, cache, table, lens, d.scale, o_lat=o2, lse=lse2)
+            torch.cuda.synchronize()
+            assert ex.value.status == L.MLA_ERR_DEVICE_CHECK and what in str(ex.value), str(ex.value)
+            assert bool((o2 == 7.0).all()) and bool((lse2 == 7.0).all())
+
+        bad = bt.clone()
+        bad[2, 3] = cache.num_blocks + 5          # sequence 2 (333 tokens) uses entry 3
+        rejected(bad, sl, f"sequence 2, table entry 3 holds block id {cache.num_blocks + 5}")
+        bad = bt.clone()
+        bad[1, 0] = -1                            # an unallocated entry inside sequence 1
+        rejected(bad, sl, "sequence 1, table entry 0 holds block id -1")
+        long = sl.clone()
+        long[1] = 64 * bt.shape[1] + 1
+        rejected(bt, long, f"sequence 1 has length {64 * bt.shape[1] + 1}")
+        bad = bt.clone()
+        bad[2, 3] = cache.num_blocks
+        with pytest.raises(L.MLAError) as ex:
+            api.gather_paged(cache, bad, sl, 333)
+        assert ex.value.status == L.MLA_ERR_DEVICE_CHECK
+        # the flag was cleared: a valid call passes again
+        o, lse = dec(ql, qr, cache, bt, sl, d.scale)
+        torch.cuda.synchronize()
+        compare_decode(d, o, lse)
+    finally:
+        lib.mla_set_debug(0)

@@ -332,3 +332,21 @@ def test_noalloc_rejects_plans_beyond_its_scratch():
                                     ctypes.byref(info), A, A, A, None) == L.MLA_ERR_INVALID_ARG
     assert lib().mla_decode_noalloc(A, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 2, 1, 128, 0.07,
                                     None, A, A, A, None) == L.MLA_ERR_INVALID_ARG
+
+
+def test_debug_switch():
+    # device checks: off unless asked for; argument errors still come first,
+    # before any HIP call
+    lib().mla_set_debug(0)
+    assert lib().mla_debug() == 0
+    assert lib().mla_set_debug(2) == L.MLA_ERR_INVALID_ARG
+    assert lib().mla_set_debug(1) == L.MLA_OK and lib().mla_debug() == 1
+    try:
+        info, _ = plan([100, 200], cus=4)
+        d = _desc()
+        st = lib().mla_decode(A, A, L.DT_BF16, ctypes.byref(d), A, 3, A, 2, 1, 128, 0.07,
+                              ctypes.byref(info), A, A, info.workspace_bytes, A, A, None)
+        assert st == L.MLA_ERR_INVALID_ARG
+    finally:
+        lib().mla_set_debug(0)
+    assert lib().mla_debug() == 0
