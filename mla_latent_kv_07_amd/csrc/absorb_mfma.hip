@@ -495,6 +495,28 @@ hipError_t launch_gemm_nn_f32(const void *A, int64_t lda, const void *B, int64_t
     return launch_gemm<false, true>(g, 1, s);
 }
 
+// As launch_gemm_nn_f32 for a short product (the cache row's): 64-row tiles
+// and as many splits as put every workgroup's stages in flight at once
+// (at most one round of 256 workgroups, at most 32 splits).
+int gemm_splits_short(int32_t M, int32_t N, int32_t K) {
+    const int tiles = ((N + BN - 1) / BN) * ((M + 63) / 64);
+    const int nk = K / BK;
+    int sp = (nk + NST_STREAM - 1) / NST_STREAM;
+    sp = sp < 32 ? sp : 32;
+    while (sp > 1 && tiles * sp > 256) --sp;
+    return sp < 1 ? 1 : sp;
+}
+
+hipError_t launch_gemm_nn_f32_short(const void *A, int64_t lda, const void *B, int64_t ldb, float *ws,
+                                    int32_t M, int32_t N, int32_t K, int splits, hipStream_t s) {
+    GemmArgs g{};
+    g.A = (const uint16_t *)A; g.lda = lda; g.bsa = 0;
+    g.B = (const uint16_t *)B; g.ldb = ldb; g.bsb = 0;
+    g.C = ws; g.ldc = N; g.bsc = 0; g.css = (int64_t)M * N;
+    g.M = M; g.N = N; g.K = K; g.splits = splits; g.ntiles = 1;
+    return launch_gemm<false, true, NST_STREAM, 8, 64>(g, 1, s);
+}
+
 // C[m][n] = bf16(A[m][k] B[k][n]), one split.
 hipError_t launch_gemm_nn_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
                                int64_t ldc, int32_t M, int32_t N, int32_t K, hipStream_t s) {

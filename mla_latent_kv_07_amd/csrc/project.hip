@@ -32,6 +32,9 @@ hipError_t launch_split_sum_bf16(const float *ws, int splits, int64_t split_stri
 bool q_up_absorb_ok(int32_t T, int32_t n_h, int32_t d_nope, int32_t d_c, int32_t q_lora);
 hipError_t launch_q_up_absorb(const void *cq, int64_t ld_cq, const void *w_uq, const void *w_uk, void *q_lat,
                               int32_t T, int32_t n_h, int32_t q_lora, hipStream_t s);
+int gemm_splits_short(int32_t M, int32_t N, int32_t K);
+hipError_t launch_gemm_nn_f32_short(const void *A, int64_t lda, const void *B, int64_t ldb, float *ws,
+                                    int32_t M, int32_t N, int32_t K, int splits, hipStream_t s);
 void gemm_pair_splits(int32_t M, int32_t N0, int32_t K0, int32_t N1, int32_t K1, int *s0, int *s1);
 hipError_t launch_gemm_nn_f32_pair(const void *A, int64_t lda, int32_t M, int32_t K, const void *B0, int64_t ldb0,
                                    float *ws0, int32_t N0, int splits0, const void *B1, int64_t ldb1, float *ws1,
@@ -115,18 +118,19 @@ __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
     return (c & 0x80) ? -v : v;
 }
 
-// sum over splits of ws[s * stride + i]: the first 16 splits' loads are all
+// sum over splits of ws[s * stride + i]: the first U splits' loads are all
 // issued before the first add (one memory latency for the usual split
 // counts), any further ones in turn
+template <int U = 16>
 __device__ __forceinline__ float split_sum(const float *__restrict__ ws, int64_t stride, int splits, int64_t i) {
-    float v[16];
+    float v[U];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) v[s] = s < splits ? ws[s * stride + i] : 0.f;
+    for (int s = 0; s < U; ++s) v[s] = s < splits ? ws[s * stride + i] : 0.f;
 #pragma unroll
-    for (int w = 8; w > 0; w >>= 1)
+    for (int w = U / 2; w > 0; w >>= 1)
 #pragma unroll
         for (int s = 0; s < w; ++s) v[s] += v[s + w];
-    for (int s = 16; s < splits; ++s) v[0] += ws[s * stride + i];
+    for (int s = U; s < splits; ++s) v[0] += ws[s * stride + i];
     return v[0];
 }
 
@@ -261,8 +265,8 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab 
     const int64_t blk = a.bt[(int64_t)b * a.bt_stride + p / kBlock];
     if (blk < 0 || blk >= a.num_blocks) return;       // unallocated table slot: not written
     const int64_t o = (int64_t)t * N + 2 * k;
-    float y0 = split_sum(a.ws, a.split_stride, a.splits, o);
-    float y1 = split_sum(a.ws, a.split_stride, a.splits, o + 1);
+    float y0 = split_sum<32>(a.ws, a.split_stride, a.splits, o);
+    float y1 = split_sum<32>(a.ws, a.split_stride, a.splits, o + 1);
     if (2 * k >= a.d_c) {
         const int j = k - a.d_c / 2;
         double sn, cs;
@@ -413,7 +417,7 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int64_t cache_append_workspace(int32_t T, int32_t d_model, int32_t d_c, int32_t d_r, mla_dtype_t dt) {
     const int32_t N = d_c + d_r;
-    const int sp = append_mfma(dt, d_model, N) ? gemm_splits(T, N, d_model) : 1;
+    const int sp = append_mfma(dt, d_model, N) ? gemm_splits_short(T, N, d_model) : 1;
     return align256((int64_t)sp * T * N * 4);
 }
 
@@ -427,8 +431,8 @@ hipError_t launch_cache_append(const void *h, const void *w_kv, mla_dtype_t dt, 
     int sp = 1;
     hipError_t e;
     if (append_mfma(dt, d_model, N)) {
-        sp = gemm_splits(T, N, d_model);
-        e = launch_gemm_nn_f32(h, d_model, w_kv, N, ws, T, N, d_model, sp, s);
+        sp = gemm_splits_short(T, N, d_model);
+        e = launch_gemm_nn_f32_short(h, d_model, w_kv, N, ws, T, N, d_model, sp, s);
     } else if (dt == MLA_DT_BF16) {
         e = gemm_generic((const uint16_t *)h, d_model, 0, (const uint16_t *)w_kv, N, 1, 0, ws, N, 0, T, N,
                          d_model, 1, s);
