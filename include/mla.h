@@ -455,7 +455,9 @@ int32_t mla_launch_events_used(void);
 
 /*
  * mla_set_debug / mla_debug — device checks of the data the host cannot see
- * (SURVEY's sanitizer item for the decode: block ids and slots).  When on,
+ * (block ids and slots of a device-resident block table; the block and its
+ * 64 slots per position are the paged layout of vLLM MLA page,
+ * "FlashMLABackend: 하드웨어 요구사항").  When on,
  * mla_decode, mla_decode_partial, mla_decode_noalloc and mla_gather_paged,
  * after their host checks, first run a check kernel on `stream` over the
  * device block table and sequence lengths and wait for it; if any sequence
