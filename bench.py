@@ -488,13 +488,12 @@ def run_decode(args, wl):
     # kernels stamping their own start and stop (mla_set_launch_events,
     # from the dispatch itself) for the combine's share: the runtime follows
     # such a stamped launch with a cache flush, so those durations run on an
-    # idler chip and are reported beside.  The combine's share of a step: the
-    # step less the decode leg.
+    # idler chip; the combine's figure is its stamped duration.
     n_k = 2 if dec.info.needs_combine else 1
     ms_per_step, gpu_ms = timer.steps(step, K, L.check)
     dec_ms = timer.legs(part, call_args, K, L.check)
     _, stamped_ms, per = timer.kernel_steps(lib, step, n_k, K, L.check)
-    comb_ms = max(gpu_ms - dec_ms, 0.0) if n_k == 2 else 0.0
+    comb_ms = per[1] if n_k == 2 else 0.0
     n_leg = max(K, 50)
     call_us = timer.per_call(step, n_leg, L.check)
     clock = shader_clock_mhz(torch, timer, lib, step)
@@ -528,7 +527,7 @@ def run_decode(args, wl):
         "decode_kernel_us": round(dec_ms * 1e3, 2),
         "combine_kernel_us": round(comb_ms * 1e3, 2),
         "kernel_time_how": ("decode: K back-to-back mla_decode_partial launches right after the timed steps; "
-                            "combine: the timed step less that"),
+                            "combine: its launches stamped from their own dispatch in a second pass"),
         "launches_per_step": n_k,
         "stamped_launch_us": [round(x * 1e3, 2) for x in per],
         "stamped_pass_us_per_step": round(stamped_ms * 1e3, 2),

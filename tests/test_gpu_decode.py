@@ -14,10 +14,10 @@ from parity import DEV, FMT, TOL, compare_decode, oracle_decode, run_decode, say
 pytestmark = pytest.mark.gpu
 
 
-def small(kv="bf16", seq=(1, 100, 333), q_len=1, n_h=128, d_c=512, d_r=64, seed=7, heavy=0.0):
+def small(kv="bf16", seq=(1, 100, 333), q_len=1, n_h=128, d_c=512, d_r=64, seed=7, heavy=0.0, heavy_mult=8.0):
     return I.make_decode_inputs(I.Workload(
         f"small_{kv}_q{q_len}_h{n_h}", seed, kv, "f32" if kv == "f32" else "bf16", B=len(seq),
-        q_len=q_len, n_h=n_h, d_c=d_c, d_r=d_r, seq_lens=tuple(seq), heavy_frac=heavy))
+        q_len=q_len, n_h=n_h, d_c=d_c, d_r=d_r, seq_lens=tuple(seq), heavy_frac=heavy, heavy_mult=heavy_mult))
 
 
 @pytest.mark.parametrize("kv", ["f32", "bf16", "fp8_e4m3", "f16", "fp8_e5m2", "fp8_e4m3_row"])
@@ -60,6 +60,14 @@ def test_decode_reference_raise_every_format(kv):
     # stages' scores and rescales the value sum (the rare path of the lazy
     # max); few CUs give long items with many stages each
     d = small(kv, seq=(900, 1300, 40), seed=21, heavy=0.03)
+    o, lse, _ = run_decode(d, cus=4)
+    compare_decode(d, o, lse)
+
+
+def test_decode_bf16_reference_raise_large_jumps():
+    # rows scaled x32 push scores 100+ log2 units above a row's first-stage
+    # max: every row raises its reference several times, by large steps
+    d = small("bf16", seq=(900, 1300, 40), seed=22, heavy=0.03, heavy_mult=32.0)
     o, lse, _ = run_decode(d, cus=4)
     compare_decode(d, o, lse)
 
