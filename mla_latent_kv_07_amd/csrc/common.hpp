@@ -74,10 +74,12 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 // the same shape over an e4m3 latent cache on the 8-bit matrix cores
 hipError_t launch_decode_f8mma(const DecodeArgs &a, hipStream_t s);
 // split_off / seq_flags are indexed by b * ceil(rows / chunk_rows) + r / chunk_rows
+// segments with more splits than this merge on a workgroup per row
+constexpr int kWideCombineSplits = 16;
 hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *lse_part,
                           const int32_t *split_off, const int32_t *seq_flags, int32_t B,
                           int32_t rows, int32_t chunk_rows, int32_t d_c, void *o_lat,
-                          mla_dtype_t out_dt, float *lse, hipStream_t s);
+                          mla_dtype_t out_dt, float *lse, int32_t max_splits, hipStream_t s);
 hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int64_t num_blocks, int32_t c_bytes,
                          int32_t r_bytes, bool split_rows, const int32_t *bt, int32_t bt_stride,
                          const int32_t *seq_lens, int32_t B, int32_t max_tokens, uint8_t *out,

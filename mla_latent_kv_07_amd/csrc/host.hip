@@ -418,7 +418,8 @@ mla_status_t finish_decode(const mla_plan_t *plan, const int32_t *plan_dev, void
     const int32_t *split_off = plan_dev + plan_split_off(plan->num_items, plan->grid_wgs);
     const int32_t *flags = plan_dev + plan_flags_off(plan->num_items, plan->grid_wgs, nseg);
     return hip_status(launch_combine(o_part, pdt, lse_part, split_off, flags, plan->B,
-                                     (int32_t)rows, kRowsPerChunk, plan->d_c, o_lat, out_dtype, lse, s),
+                                     (int32_t)rows, kRowsPerChunk, plan->d_c, o_lat, out_dtype, lse,
+                                     plan->max_splits, s),
                       "combine launch");
 }
 
@@ -636,7 +637,7 @@ mla_status_t mla_combine_lse(const float *o_part, const float *lse_part,
     if (out_dtype != MLA_DT_F32 && out_dtype != MLA_DT_BF16)
         return fail(MLA_ERR_UNSUPPORTED, "out dtype %d unsupported", (int)out_dtype);
     return hip_status(launch_combine(o_part, MLA_DT_F32, lse_part, split_off, seq_flags, B, rows,
-                                     rows, d_c, o_lat, out_dtype, lse, (hipStream_t)stream),
+                                     rows, d_c, o_lat, out_dtype, lse, 0, (hipStream_t)stream),
                       "combine launch");
 }
 

@@ -236,6 +236,89 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
     if (lane == 0) lse[out_row] = m + __logf(wsum);
 }
 
+// The same merge for segments with many splits (long sequences): one
+// workgroup per output row, its four waves taking every fourth split, eight
+// partial rows in flight per wave, the four sums added through LDS.  Every
+// wave finds the max over all splits' LSEs itself.
+template <typename OutT>
+__global__ __launch_bounds__(256) void combine512_wide_kernel(const uint16_t *__restrict__ o_part,
+                                                              const float *__restrict__ lse_part,
+                                                              const int32_t *__restrict__ split_off,
+                                                              const int32_t *__restrict__ seq_flags,
+                                                              int32_t rows, int32_t chunk_rows,
+                                                              OutT *__restrict__ o_lat,
+                                                              float *__restrict__ lse) {
+    constexpr int U = 8;
+    __shared__ float red[4][9][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = blockIdx.x, b = blockIdx.y;
+    const int sc = b * ((rows + chunk_rows - 1) / chunk_rows) + r / chunk_rows;
+    if (seq_flags && seq_flags[sc] == 1) return;
+    const int k0 = split_off[sc], n = split_off[sc + 1] - k0;
+    const int64_t out_row = (int64_t)b * rows + r;
+    const uint16_t *src0 = o_part + ((int64_t)k0 * rows + r) * 512 + lane * 8;
+    const int64_t split_stride = (int64_t)rows * 512;
+
+    float m = -INFINITY;
+    for (int c = lane; c < n; c += 64) m = fmaxf(m, lse_part[(int64_t)(k0 + c) * rows + r]);
+    m = wave_max(m);
+    uint4 *dst = (uint4 *)(o_lat + out_row * 512 + lane * 8);
+    if (m == -INFINITY) {
+        if (wave == 0) {
+            *dst = make_uint4(0, 0, 0, 0);
+            if constexpr (sizeof(OutT) == 4) dst[1] = make_uint4(0, 0, 0, 0);
+            if (lane == 0) lse[out_row] = -INFINITY;
+        }
+        return;
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    for (int c = wave; c < n; c += 4 * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = c + 4 * u < n ? *(const uint4 *)(src0 + (c + 4 * u) * split_stride) : make_uint4(0, 0, 0, 0);
+        // lane u of the wave holds the weight of split c + 4 u
+        const float lk = lane < U && c + 4 * lane < n ? lse_part[(int64_t)(k0 + c + 4 * lane) * rows + r] : -INFINITY;
+        const float wk = lk == -INFINITY ? 0.f : __expf(lk - m);
+        wsum += wave_sum(wk);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), u));
+            if (w == 0.f) continue;   // split without visible tokens (or past n)
+            const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += w * __uint_as_float(x[e] << 16);
+                acc[2 * e + 1] += w * __uint_as_float(x[e] & 0xffff0000u);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[e];
+    red[wave][8][lane] = wsum;
+    __syncthreads();
+    if (wave != 0) return;
+    float ws = 0.f;
+#pragma unroll
+    for (int v2 = 0; v2 < 4; ++v2) ws += red[v2][8][lane];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = red[0][e][lane] + red[1][e][lane] + red[2][e][lane] + red[3][e][lane];
+    const float inv = 1.0f / ws;
+    if constexpr (sizeof(OutT) == 2) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pk[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+        *dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+        float4 *d4 = (float4 *)dst;
+        d4[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        d4[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    }
+    if (lane == 0) lse[out_row] = m + __logf(ws);
+}
+
 }  // namespace
 
 // Device checks (on request only): flag[0] counts offences; the first one's
@@ -323,9 +406,18 @@ hipError_t launch_gather(const uint8_t *pool, int64_t block_bytes, int64_t num_b
 hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *lse_part,
                           const int32_t *split_off, const int32_t *seq_flags, int32_t B,
                           int32_t rows, int32_t chunk_rows, int32_t d_c, void *o_lat,
-                          mla_dtype_t out_dt, float *lse, hipStream_t s) {
+                          mla_dtype_t out_dt, float *lse, int32_t max_splits, hipStream_t s) {
     dim3 grid((rows + 3) / 4, B);
-    if (part_dt == MLA_DT_BF16 && d_c == 512) {
+    if (part_dt == MLA_DT_BF16 && d_c == 512 && max_splits > kWideCombineSplits) {
+        // many splits per segment: a workgroup per row, four waves over the splits
+        const dim3 wide((unsigned)rows, (unsigned)B);
+        if (out_dt == MLA_DT_BF16)
+            launch_timed(combine512_wide_kernel<uint16_t>, wide, dim3(256), 0, s, (const uint16_t *)o_part,
+                         lse_part, split_off, seq_flags, rows, chunk_rows, (uint16_t *)o_lat, lse);
+        else
+            launch_timed(combine512_wide_kernel<float>, wide, dim3(256), 0, s, (const uint16_t *)o_part,
+                         lse_part, split_off, seq_flags, rows, chunk_rows, (float *)o_lat, lse);
+    } else if (part_dt == MLA_DT_BF16 && d_c == 512) {
         if (out_dt == MLA_DT_BF16)
             launch_timed(combine512_kernel<uint16_t>, grid, dim3(256), 0, s,
                                (const uint16_t *)o_part, lse_part, split_off, seq_flags, rows,

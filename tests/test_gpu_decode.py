@@ -45,6 +45,16 @@ def test_decode_bf16_mfma_splits_and_combine():
     compare_decode(d, o, lse)
 
 
+def test_decode_bf16_many_splits_wide_combine():
+    # a long sequence split over many CUs: more than 16 partial slots per
+    # segment take the workgroup-per-row merge; a short and an empty
+    # sequence ride along
+    d = small("bf16", seq=(6000, 70, 0), seed=12)
+    o, lse, dec = run_decode(d, cus=96)
+    assert dec.info.max_splits > 16, dec.info.max_splits
+    compare_decode(d, o, lse)
+
+
 def test_decode_bf16_heavy_rows_and_nan_tails():
     # 5 % of rows scaled x8 (large softmax range, exercises the running-max
     # raise); NaN tails and spare blocks must not leak
