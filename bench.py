@@ -46,7 +46,7 @@ FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector peak
 COPY_BYTES = 256 << 20          # calibration copy size
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "decode_mfma_bf16_traffic.json")
 DECODE_KERNEL = "decode_mfma_kernel<mla::kv::Bf16>"       # bf16 cache
-DECODE_KERNEL_FP8 = "decode_f8mma_kernel"   # e4m3 cache on the 8-bit MFMAs
+DECODE_KERNEL_FP8 = "decode_f8w8_kernel"    # e4m3 cache on the 8-bit MFMAs
 MFMA_KERNELS = {"bf16": DECODE_KERNEL, "fp8_e4m3": DECODE_KERNEL_FP8,
                 "f16": "decode_mfma_kernel<mla::kv::F16>",
                 "fp8_e5m2": "decode_mfma_kernel<mla::kv::E5m2>",

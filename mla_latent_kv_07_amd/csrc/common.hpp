@@ -71,8 +71,9 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 // MFMA decode of the DeepSeek-V2 shape (d_c 512, d_r 64, bf16 queries) for
 // every 16-bit and 8-bit cache format
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
-// the same shape over an e4m3 latent cache on the 8-bit matrix cores
-hipError_t launch_decode_f8mma(const DecodeArgs &a, hipStream_t s);
+// the same shape over an e4m3 latent cache on the 8-bit matrix cores (eight
+// waves per workgroup, two per SIMD)
+hipError_t launch_decode_f8w8(const DecodeArgs &a, hipStream_t s);
 // split_off / seq_flags are indexed by b * ceil(rows / chunk_rows) + r / chunk_rows
 // segments with more splits than this merge on a workgroup per row
 constexpr int kWideCombineSplits = 16;

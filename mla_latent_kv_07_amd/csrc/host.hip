@@ -396,7 +396,7 @@ mla_status_t prepare_decode(const void *q_lat, const void *q_rope, mla_dtype_t q
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     if (a.num_items == 0) return hipSuccess;
     if (is_fast_shape(a.kv_dtype, a.d_c, a.d_r) && a.q_dtype == MLA_DT_BF16) {
-        if (a.kv_dtype == MLA_DT_FP8_E4M3 && !(a.cache_flags & MLA_CACHE_FP8_EXACT)) return launch_decode_f8mma(a, s);
+        if (a.kv_dtype == MLA_DT_FP8_E4M3 && !(a.cache_flags & MLA_CACHE_FP8_EXACT)) return launch_decode_f8w8(a, s);
         return launch_decode_mfma(a, s);
     }
     return launch_decode_generic(a, s);

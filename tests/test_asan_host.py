@@ -51,7 +51,7 @@ def test_host_code_under_address_sanitizer(tmp_path):
              "m = open('/proc/self/maps').read(); print('libmla_asan' in m, 'liboracle_asan' in m)")
     r = subprocess.run([sys.executable, "-c", probe], cwd=ROOT, env=env, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.split() == ["True", "True"], r.stdout + r.stderr[-2000:]
-    tests = ["tests/test_host_abi.py", "tests/test_f8_layout_model.py",
+    tests = ["tests/test_host_abi.py", "tests/test_f8w8_layout_model.py",
              *sorted(str(p.relative_to(ROOT)) for p in (ROOT / "tests").glob("test_oracle_*.py"))]
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-m", "not gpu", "-p", "no:cacheprovider",
                         "-p", "no:xdist", *tests], cwd=ROOT, env=env, capture_output=True, text=True, timeout=840)

@@ -1,7 +1,9 @@
 """Wait states around the hand-written MFMAs of the decode kernels.
 
-The score chains of the MFMA decodes are inline asm, so the compiler's hazard
-recognizer does not see them as MFMAs.  gfx950 needs
+The score chains of the 16-bit MFMA decode are inline asm, so the compiler's
+hazard recognizer does not see them as MFMAs (the 8-bit decode issues every
+MFMA as a builtin, so it has no inline-asm MFMA to check; it is compiled here
+for the stage-loop scratch check below).  gfx950 needs
   - 2 wait states between a VALU write of a VGPR and an MFMA that reads it
     (A, B or C operand): the kernels place an ``s_nop 1`` only where such a
     write can precede a chain;
@@ -25,7 +27,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "mla_latent_kv_07_amd", "csrc")
-SOURCES = ["decode_mfma.hip", "decode_f8mma.hip"]
+SOURCES = ["decode_mfma.hip", "decode_f8w8.hip"]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 WINDOW = 2
@@ -188,7 +190,7 @@ def kernel_bodies(lines):
     """{kernel symbol: its instruction lines} of a gfx950 assembly listing."""
     out = {}
     for n, line in enumerate(lines):
-        m = re.match(r"^(_Z\w*(decode_mfma_kernel|decode_f8mma_kernel)\w*):", line)
+        m = re.match(r"^(_Z\w*(decode_mfma_kernel|decode_f8w8_kernel)\w*):", line)
         if m:
             end = next(k for k in range(n, len(lines)) if "s_endpgm" in lines[k])
             out[m.group(1)] = lines[n:end]
@@ -202,7 +204,8 @@ def test_no_scratch_access_in_the_stage_loop(decode_asm):
     such reload per iteration drains the copy pipeline.  The stage loop runs
     from the first MFMA after the prologue to the last MFMA of the kernel
     (the 16-bit kernel scores stage 0 in its prologue with 36 MFMAs; the
-    8-bit kernel has none before its loop)."""
+    8-bit kernel has none before its loop).  The 8-bit kernel runs two waves
+    per SIMD within 256 registers, where this is easy to break."""
     bodies = kernel_bodies(decode_asm)
     assert bodies
     for name, body in bodies.items():
