@@ -3,7 +3,8 @@ with a caller workspace and mla_decode_noalloc, each replayed three times with
 an eager decode of other inputs in between (which overwrites the workspace or
 the scratch array and the plan's partial slots), every replay bit-identical to
 the eager call on the same inputs.  The batch is split over few compute units
-so that the partials and the combine are part of the captured work."""
+so that the partials and the combine are part of the captured work; a bf16
+cache runs the 16-bit MFMA decode, an e4m3 one the 8-bit decode."""
 import ctypes
 
 import pytest
@@ -20,8 +21,8 @@ pytestmark = pytest.mark.gpu
 SEQ = (3000, 700, 1, 0, 2500)
 
 
-def _inputs(seed):
-    d = I.make_decode_inputs(I.Workload(f"graph_{seed}", seed, "bf16", "bf16", B=len(SEQ), q_len=1, n_h=128,
+def _inputs(seed, kv):
+    d = I.make_decode_inputs(I.Workload(f"graph_{seed}", seed, kv, "bf16", B=len(SEQ), q_len=1, n_h=128,
                                         d_c=512, d_r=64, seq_lens=SEQ))
     return d, to_device(d)
 
@@ -41,11 +42,12 @@ def _call(entry, d, dev_in, dec, o, lse, stream):
                                P(lse.data_ptr()), P(stream.cuda_stream)))
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 @pytest.mark.parametrize("entry", ["workspace", "noalloc"])
-def test_graph_replays_match_eager(entry):
-    d, dev_in = _inputs(41)
-    d2, dev_in2 = _inputs(42)                     # same lengths, other values
-    dec = api.Decoder(d.cache.seq_lens, 1, 128, 512, 64, "bf16", DEV, cus=16)
+def test_graph_replays_match_eager(entry, kv):
+    d, dev_in = _inputs(41, kv)
+    d2, dev_in2 = _inputs(42, kv)                 # same lengths, other values
+    dec = api.Decoder(d.cache.seq_lens, 1, 128, 512, 64, kv, DEV, cus=16)
     assert dec.info.num_partials > 0 and dec.info.needs_combine
     T = d.wl.B
     new = lambda: (torch.empty((T, 128, 512), dtype=torch.bfloat16, device=DEV),
