@@ -138,6 +138,17 @@ def test_decode_fp8_cache(exact):
     compare_decode(d, o, lse)
 
 
+@pytest.mark.parametrize("exact", [False, True], ids=["fp8_mfma", "exact_bf16"])
+def test_decode_fp8_long_items(exact):
+    # a 30,000-token sequence over two compute units: items of ~230 blocks,
+    # hundreds of stages per workgroup (block ids, stage buffers and the lazy
+    # reference max over a long loop), next to one-block and empty sequences
+    d = small("fp8_e4m3", seq=(30000, 5, 0, 64), q_len=1, seed=45, heavy=0.01)
+    o, lse, dec = run_decode(d, cus=2, fp8_exact=exact)
+    assert dec.info.blocks_per_item > 200
+    compare_decode(d, o, lse)
+
+
 def test_decode_fp8_mfma_path_tracks_exact_path():
     # the two arithmetics over one e4m3 cache: the 8-bit MFMA path (two-term
     # e4m3 query and probabilities) against the exact decode, row by row, and
