@@ -170,6 +170,16 @@ def test_decode_fp8_mfma_path_tracks_exact_path():
 
 
 @pytest.mark.parametrize("exact", [False, True], ids=["fp8_mfma", "exact_bf16"])
+def test_decode_fp8_ragged_row_chunks(exact):
+    # q_len 3 x 48 heads = 144 rows per sequence: a full 128-row chunk and one
+    # of 16 rows, with the causal limit moving inside each chunk
+    d = small("fp8_e4m3", seq=(5, 400, 129), q_len=3, n_h=48, seed=46)
+    o, lse, dec = run_decode(d, cus=6, fp8_exact=exact)
+    assert dec.info.row_chunks == 2
+    compare_decode(d, o, lse)
+
+
+@pytest.mark.parametrize("exact", [False, True], ids=["fp8_mfma", "exact_bf16"])
 def test_decode_fp8_few_heads_and_empty_rows(exact):
     # n_h = 16 with a query pair: 32 rows per sequence, so three of the four
     # waves hold only rows past the end; sequences shorter than the pair and
