@@ -163,10 +163,12 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
     const int b = blockIdx.y;
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
-    // the split list of the row's (sequence, row chunk)
-    const int sc = b * ((rows + chunk_rows - 1) / chunk_rows) + r / chunk_rows;
-    if (seq_flags && seq_flags[sc] == 1) return;
-    const int k0 = split_off[sc], n = split_off[sc + 1] - k0;
+    // the split list of the row's (sequence, row chunk), wave-uniform: read
+    // through the scalar cache
+    const int sc = __builtin_amdgcn_readfirstlane(b * ((rows + chunk_rows - 1) / chunk_rows) + r / chunk_rows);
+    if (seq_flags && ((const __attribute__((address_space(4))) int32_t *)seq_flags)[sc] == 1) return;
+    const int k0 = ((const __attribute__((address_space(4))) int32_t *)split_off)[sc];
+    const int n = ((const __attribute__((address_space(4))) int32_t *)split_off)[sc + 1] - k0;
     const int64_t out_row = (int64_t)b * rows + r;
     const uint16_t *src0 = o_part + ((int64_t)k0 * rows + r) * 512 + lane * 8;
     const int64_t split_stride = (int64_t)rows * 512;
