@@ -13,6 +13,7 @@
 // from HBM once per workgroup and from LDS by all four waves:
 //   score  S^T[32 tok x 32 rows] = K[32 x 576] . Q^T           (MFMA 32x32x16)
 //   p      = exp2(S*scale*log2e - m) with a lazily raised reference max m
+//            (raised only when a score passes it by a wide margin)
 //   value  O^T[512 x 32] += V^T[512 x 32] . P^T[32 x 32]       (MFMA 32x32x16)
 // V is the latent part of the same LDS rows, read transposed with
 // ds_read_b64_tr_b16; the score accumulator layout is already the value
@@ -192,6 +193,19 @@ template <typename KV>
 __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     constexpr bool FP8 = KV::fp8, ROW = KV::row, H16 = KV::half;
     constexpr int COPY_AT = copy_at<FP8>();
+    // Lazy reference max (log2 units): a row's reference m is raised only
+    // when a stage's max passes it by RAISE_T, and then to that max plus
+    // RAISE_H, so p = 2^(s - m) <= 2^RAISE_T.  A raise rescales the wave's
+    // whole O^T (256 products per lane), so it must stay rare.  fp16
+    // probabilities (65504 at most) and 8-bit caches (the block scale rides
+    // in the exp2 argument, down to 2^-64) keep p <= 2^8 with no headroom;
+    // bf16 ones have fp32's exponent range: p <= 2^40, and the max token's
+    // p = 2^-24 after a raise, so that outlier keys (scores tens of units
+    // above the rest) raise once instead of at every new record.  The fp32
+    // sums overflow only for |v| near 2^(128 - 40 - 17) = 2^71 over 2^17
+    // tokens, and products p v underflow only for |v| below about 2^-100.
+    constexpr float RAISE_T = (FP8 || H16) ? 8.0f : 40.0f;
+    constexpr float RAISE_H = (FP8 || H16) ? 0.0f : 24.0f;
     __shared__ __attribute__((aligned(1024))) uint8_t smem_[lds_total<FP8>()];
     lds_u8 *smem = (lds_u8 *)smem_;
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
@@ -673,9 +687,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx),
                                                                  false, false);
                 mx = __builtin_fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1])) * s_l2;
-                // raise the reference max only when a score exceeds it by 2^8
-                raise = mx > m_run + 8.0f;
-                m_new = raise ? mx : m_run;
+                // raise the reference max only when a score passes it by RAISE_T
+                raise = mx > m_run + RAISE_T;
+                m_new = raise ? mx + RAISE_H : m_run;
                 m_off = (m_new == -INFINITY ? 0.f : m_new) - l2sig;
             } else if (k < 28) {
                 if (k == 9) alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;

@@ -82,6 +82,21 @@ def test_decode_bf16_reference_raise_large_jumps():
     compare_decode(d, o, lse)
 
 
+@pytest.mark.parametrize("exp2", [40, -60])
+def test_decode_bf16_value_range_with_outlier_keys(exp2):
+    # The bf16 decode lets p reach 2^40 before it raises a row's reference max,
+    # and a raise leaves 2^24 of headroom.  Latent values scaled by 2^40 (fp32
+    # sums near 2^100) or by 2^-60 (products p v near 2^-84), with x8 outlier
+    # keys raising the reference, must still match the oracle.  The latent
+    # queries take the inverse power, so every score is unchanged.
+    d = small("bf16", seq=(900, 1300, 40), seed=23, heavy=0.03)
+    rows = d.cache.pool.view(torch.bfloat16).view(d.cache.pool.shape[0], 64, d.wl.d_c + d.wl.d_r)
+    rows[:, :, :d.wl.d_c] = (rows[:, :, :d.wl.d_c].float() * 2.0 ** exp2).to(torch.bfloat16)
+    d.q_lat.copy_((d.q_lat.float() * 2.0 ** -exp2).to(d.q_lat.dtype))
+    o, lse, _ = run_decode(d, cus=4)
+    compare_decode(d, o, lse)
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 def test_decode_many_ragged_sequences_dispatch_table(kv):
     # 300 sequences of 1-700 tokens with q_len 2 (two row chunks each): the
