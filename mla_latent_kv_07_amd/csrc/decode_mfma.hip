@@ -210,6 +210,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     lds_u8 *smem = (lds_u8 *)smem_;
     const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
 
+    // Every kernel argument that the first copies depend on, in one round
+    // trip: left alone, the compiler loaded each where it was first needed,
+    // and the prologue waited on the scalar cache five times before its first
+    // copy.
+    asm volatile("" ::"s"(a.plan), "s"(a.seq_lens), "s"(a.block_table), "s"(a.q_lat), "s"(a.q_rope), "s"(a.pool),
+                 "s"(a.num_items), "s"(a.row_chunks), "s"(a.bt_stride), "s"(a.rows), "s"(a.num_pool_blocks),
+                 "s"(a.q_len), "s"(a.n_h));
     // workgroup -> work item {sequence * row_chunks + chunk, blocks, slot},
     // from the plan's dispatch table (longest items first on each XCD; -1
     // pads the grid)
@@ -219,12 +226,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     const int sc = sload(a.plan, io);
     const int b = sc / a.row_chunks, chunk = sc - b * a.row_chunks;
     const int blk0 = sload(a.plan, io + 1), blk1 = sload(a.plan, io + 2), slot = sload(a.plan, io + 3);
-    const int S = sload(a.seq_lens, b);
+    // the sequence length: loaded here, waited for after the first query
+    // copies are issued (see the queries below), which do not need it
+    const int S_load = sload(a.seq_lens, b);
+    int S, nst_live;
     const int nst = 2 * (blk1 - blk0);   // 32-token stages in this item
-    // a stage holds tokens only if its first position is < S (the plan covers
-    // ceil(S/64) blocks, so the second half of the last block may be empty)
     const int p_first = blk0 * kBlock;
-    const int nst_live = min(nst, (S - p_first + HALF - 1) / HALF);
 
     // wave index as a wave-uniform (scalar) value: the stage copies use it in
     // their scalar source pointers and LDS destinations
@@ -234,7 +241,6 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     const int wrow = wave * 32 + ln;   // row inside the chunk
     const int row = chunk * kRowsPerChunk + wrow;
     const bool row_ok = row < a.rows;
-    const int lim = row_ok ? S - a.q_len + row / a.n_h + 1 : 0;   // visible positions < lim
     const int64_t grow = (int64_t)b * a.rows + row;
 
     const uint8_t *pool = (const uint8_t *)a.pool;
@@ -360,6 +366,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
             tv[k] = j < ntab ? a.block_table[bt_row + blk0 + j] : 0;
         }
         copy_half(0);
+        // a stage holds tokens only if its first position is < S (the plan
+        // covers ceil(S/64) blocks, so the second half of the last block may
+        // be empty)
+        S = S_load;
+        asm volatile("" : "+s"(S));
+        nst_live = min(nst, (S - p_first + HALF - 1) / HALF);
         issue(0, blk_id(0));
         if (nst_live > 1) issue(1, blk_id(1));
         // the first half has landed when at most the stage copies are in flight
@@ -400,6 +412,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(DecodeArgs a) {
     // every wave holds its queries (the query regions are free) and every
     // wave's copies of stages 0 and 1 are visible
     __syncthreads();
+    const int lim = row_ok ? S - a.q_len + row / a.n_h + 1 : 0;   // visible positions < lim
     f32x16 oacc[MBLOCKS];
 #pragma unroll
     for (int mb = 0; mb < MBLOCKS; ++mb) oacc[mb] = f32x16{};
