@@ -194,7 +194,6 @@ __global__ __launch_bounds__(512, 1) void decode_f8w8_kernel(DecodeArgs a) {
     auto sigma = [&](int st) { return *(const lds_f32 *)(smem + RING_OFF + RING_SLOT * (st & 3)); };
 
     if (nst_live > 0) issue(0);
-    if (nst_live > 1) issue(1);
 
     // ---- queries: sigma_q = max|q~| / 448 over the row (lane group G holds
     // features 128 G + 32 kc .. + 31 of every k-chunk kc), then
@@ -212,15 +211,21 @@ __global__ __launch_bounds__(512, 1) void decode_f8w8_kernel(DecodeArgs a) {
     const __bf16 *qrow = (const __bf16 *)a.q_lat + ((int64_t)b * a.rows + rr) * DC + 128 * G;
     i32x8 qh[KC], ql[KC];
     {
+        // the row's 256 bytes are loaded once and used by both passes (loaded
+        // in each, the second pass's loads were issued one at a time, each
+        // behind its own wait)
+        bf16x8 qx[KC][4];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) qx[kc][v] = *(const bf16x8 *)(qrow + 32 * kc + 8 * v);
         float amax = 0.f;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bf16x8 x = *(const bf16x8 *)(qrow + 32 * kc + 8 * v);
+            for (int v = 0; v < 4; ++v)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf((float)x[e]));
-            }
+                for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf((float)qx[kc][v][e]));
         amax = row_max4(amax);
         *(lds_f32 *)(smem + L_OFF + 4 * srow) = amax * (1.0f / 448.0f);   // sigma_q, equal in the row's 4 lanes
         const float inv = amax > 0.f ? 448.0f / amax : 0.f;
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(512, 1) void decode_f8w8_kernel(DecodeArgs a) {
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const bf16x8 x = *(const bf16x8 *)(qrow + 32 * kc + 8 * v);
+                const bf16x8 x = qx[kc][v];
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = (float)x[e] * inv;
@@ -251,6 +256,9 @@ __global__ __launch_bounds__(512, 1) void decode_f8w8_kernel(DecodeArgs a) {
         for (int j = 0; j < KR; ++j)
             *(bf16x8 *)(smem + QR_OFF + srow * QR_PITCH + 64 * j + 16 * G) = *(const bf16x8 *)(qrr + 32 * j);
     }
+    // stage 1 after the queries: vector loads complete in order, so a copy
+    // issued before them would hold back their first use
+    if (nst_live > 1) issue(1);
 
     f32x16 oacc[MBW][NB];
 #pragma unroll
