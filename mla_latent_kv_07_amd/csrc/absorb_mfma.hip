@@ -555,8 +555,9 @@ hipError_t launch_absorb_q_mfma(const void *q_nope, int64_t ld_q, const void *w_
     g.M = T; g.N = d_c; g.K = d_nope; g.splits = 1; g.ntiles = 1;
     // K = d_nope is at most two stages: one 128 x 128 tile per workgroup on
     // the short stage buffers, two workgroups per CU, every copy issued at
-    // the start
-    if (d_nope <= NST_SHORT * BK) return launch_gemm<true, false, NST_SHORT, 4, BM>(g, n_h, s);
+    // the start; eight waves (two per SIMD) measured faster than four, 64-row
+    // tiles (twice the workgroups) slower
+    if (d_nope <= NST_SHORT * BK) return launch_gemm<true, false, NST_SHORT, 8, BM>(g, n_h, s);
     return launch_gemm<true, false>(g, n_h, s);
 }
 
