@@ -547,9 +547,11 @@ def run_layer(args, wl, producers=False):
     """The whole absorbed layer at decode: absorb_q -> split decode + combine
     -> absorb_out, with q^C and q^R drawn N(0, 1) from the workload's
     generator after its cache.  With producers, one decode step from the
-    hidden states instead: mla_project_q (h -> q~, q^R at position S_b - 1)
-    and mla_cache_append (the new token's row written at S_b - 1, so the
-    decode attends to it) replace the drawn queries and absorb_q."""
+    hidden states instead: mla_project_step (h -> q~, q^R at position S_b - 1,
+    and the new token's cache row written at S_b - 1, so the decode attends
+    to it; the three down-projections of h as one weight) replaces the drawn
+    queries and absorb_q.  The separate mla_project_q and mla_cache_append
+    calls are timed beside it."""
     import torch
     from mla_latent_kv_07_amd import _lib as L
     from mla_latent_kv_07_amd import api
@@ -618,10 +620,19 @@ def run_layer(args, wl, producers=False):
                 bt.stride(0), P(pos.data_ptr()), wl.B, wl.q_len, wl.d_model, ctypes.byref(rope),
                 P(ws_a.data_ptr()), ws_a.numel(), sp) for r in range(R)]
         dargs = [(P(q_lat.data_ptr()), P(qr_p.data_ptr())) + a[2:] for a in dargs]
+        # [W^DQ | W^DKV | W^KR]: the layout mla_project_step reads the three down-projections in
+        w_dkvq = torch.cat([w["w_dq"], w["w_dkv"]], dim=1).contiguous()
+        ws_s_bytes = api.project_step_workspace_bytes(wl.B, wl.q_len, wl.d_model, wl.q_lora, wl.n_h, wl.d_nope,
+                                                      wl.d_c, wl.d_r, bf)
+        assert ws_s_bytes > 0, "no fused producer path at this shape"
+        ws_s = torch.empty(ws_s_bytes, dtype=torch.uint8, device=dev)
+        pss = [(P(h.data_ptr()), P(w_dkvq.data_ptr()), P(w["w_uq"].data_ptr()), P(w["w_qr"].data_ptr()),
+                P(w["w_uk"].data_ptr()), L.DT_BF16, ctypes.byref(descs[r]), P(bt.data_ptr()), bt.stride(0),
+                P(pos.data_ptr()), wl.B, wl.q_len, wl.d_model, wl.q_lora, wl.n_h, wl.d_nope, ctypes.byref(rope),
+                P(q_lat.data_ptr()), P(qr_p.data_ptr()), P(ws_s.data_ptr()), ws_s.numel(), sp) for r in range(R)]
 
         def step(i):
-            return (lib.mla_project_q(*pq) | lib.mla_cache_append(*cas[i % R]) | lib.mla_decode(*dargs[i % R])
-                    | lib.mla_absorb_out(*ao))
+            return lib.mla_project_step(*pss[i % R]) | lib.mla_decode(*dargs[i % R]) | lib.mla_absorb_out(*ao)
     else:
         def step(i):
             return lib.mla_absorb_q(*aq) | lib.mla_decode(*dargs[i % R]) | lib.mla_absorb_out(*ao)
@@ -634,6 +645,7 @@ def run_layer(args, wl, producers=False):
     n_leg = max(K, 20)
     q_ms = timer.legs(lib.mla_absorb_q, [aq], n_leg, L.check)
     if producers:
+        ps_ms = timer.legs(lib.mla_project_step, pss, n_leg, L.check)
         pq_ms = timer.legs(lib.mla_project_q, [pq], n_leg, L.check)
         ca_ms = timer.legs(lib.mla_cache_append, cas, n_leg, L.check)
     dec_ms = timer.legs(lib.mla_decode_partial, dargs, n_leg, L.check)
@@ -647,7 +659,7 @@ def run_layer(args, wl, producers=False):
     layer_bytes = cache_bytes + weight_bytes
     S = sl_h.tolist()
     out = {
-        "metric": (f"MLA decode step from hidden states (project_q, cache_append, decode, absorb_out) "
+        "metric": (f"MLA decode step from hidden states (project_step, decode, absorb_out) "
                    f"cache+weight GB/s, decode_step_b128_bf16" if producers else
                    f"MLA absorbed layer (absorb_q, decode, absorb_out) cache+weight GB/s, {wl.name}"),
         "value": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -686,7 +698,13 @@ def run_layer(args, wl, producers=False):
         b_pq = (sum(w[k].numel() for k in ("w_dq", "w_uq", "w_qr", "w_uk")) + h.numel()
                 + q_lat.numel() + qr_p.numel()) * 2
         b_ca = (w["w_dkv"].numel() + h.numel() + T * (wl.d_c + wl.d_r)) * 2
+        b_ps = b_pq + b_ca - h.numel() * 2   # h is read once
         out["producers"] = {
+            # the step's producers in one call (queries and cache rows)
+            "project_step_us": round(ps_ms * 1e3, 2), "project_step_gbs": round(b_ps / (ps_ms * 1e-3) / 1e9, 1),
+            "project_step_bytes": b_ps,
+            "project_step_launch_us": timer.launch_means(lib, lib.mla_project_step, pss, n_leg, L.check),
+            # the same work as two separate calls
             "project_q_us": round(pq_ms * 1e3, 2), "project_q_gbs": round(b_pq / (pq_ms * 1e-3) / 1e9, 1),
             "project_q_bytes": b_pq,
             "cache_append_us": round(ca_ms * 1e3, 2), "cache_append_gbs": round(b_ca / (ca_ms * 1e-3) / 1e9, 1),

@@ -427,6 +427,45 @@ mla_status_t mla_project_q(const void *h, const void *w_dq, const void *w_uq, co
                            mla_stream_t stream);
 
 /*
+ * mla_project_step — one decode step's producers from the same hidden states:
+ * the queries of mla_project_q and the cache rows of mla_cache_append in
+ * three launches instead of five.  Both read h through a down-projection
+ * (huny §2-2 c^Q = h W^DQ, §2-1 c = h W^DKV, §2-3 k^R = RoPE(h W^KR)), so
+ * the three weights come side by side in one matrix and share one product
+ * with h W^QR (§2-3 rotary query); one finishing launch sums the partials
+ * into c^Q, q^R and the cache rows; c^Q W^UQ with the W^UK absorption
+ * follows (§3-1).
+ *   token t = b * q_len + i of sequence b sits at p = pos0[b] + i: q^R of t is
+ *   rotated at p and its cache row [c | k^R] goes to slot p % 64 of block
+ *   block_table[b][p / 64], exactly as mla_cache_append writes it (same
+ *   storage rules, scale rule and skipped positions for every cache format).
+ * h [B q_len][d_model]; w_dkvq [d_model][q_lora + d_c + d_r] = the columns of
+ * W^DQ, then W^DKV, then W^KR (d_c, d_r from the cache descriptor); w_uq,
+ * w_qr, w_uk, q_lat, q_rope as in mla_project_q (T = B q_len).  All BF16,
+ * fp32 accumulation, c^Q rounded to bf16 before W^UQ.  q_lat and q_rope are
+ * bit-identical to mla_project_q's for the same inputs; the cache rows take
+ * another split of the d_model sum than mla_cache_append's (fp32 partials),
+ * so they may differ from its rows by rounding.  Sequences of one call must
+ * be distinct.  One rope configuration serves q^R and k^R.
+ * Shapes: the bf16 MFMA path of mla_project_q (d_model and q_lora multiples
+ * of 64, n_h d_nope and n_h d_r multiples of 8, d_nope a multiple of 64, d_c
+ * of 128, q_lora + d_c + d_r a multiple of 8); mla_project_step_workspace()
+ * returns 0 for any other shape or dtype, and the call UNSUPPORTED (use the
+ * two separate calls).
+ * workspace >= mla_project_step_workspace() bytes, 256-byte aligned.
+ * Errors: INVALID_ARG, UNSUPPORTED, ALIGN, WORKSPACE, HIP.
+ */
+int64_t mla_project_step_workspace(int32_t B, int32_t q_len, int32_t d_model, int32_t q_lora,
+                                   int32_t n_h, int32_t d_nope, int32_t d_c, int32_t d_r,
+                                   mla_dtype_t dt);
+mla_status_t mla_project_step(const void *h, const void *w_dkvq, const void *w_uq, const void *w_qr,
+                              const void *w_uk, mla_dtype_t dt, const mla_cache_desc_t *cache,
+                              const int32_t *block_table, int32_t bt_stride, const int32_t *pos0,
+                              int32_t B, int32_t q_len, int32_t d_model, int32_t q_lora, int32_t n_h,
+                              int32_t d_nope, const mla_rope_t *rope, void *q_lat, void *q_rope,
+                              void *workspace, int64_t workspace_bytes, mla_stream_t stream);
+
+/*
  * mla_clock_probe — measurement helper, not a step of the path: `wgs`
  * workgroups of 4 waves each run a dependent chain of `iters` bf16
  * 32x32x16 MFMAs, and out[2k], out[2k+1] (int64, device) receive the shader

@@ -106,6 +106,11 @@ def load() -> ctypes.CDLL:
     L.mla_project_q_workspace.restype = c_int64
     L.mla_project_q.argtypes = [P, P, P, P, P, c_int32, P, c_int32, c_int32, c_int32, c_int32,
                                 c_int32, c_int32, c_int32, ctypes.POINTER(Rope), P, P, P, c_int64, P]
+    L.mla_project_step_workspace.argtypes = [c_int32] * 9
+    L.mla_project_step_workspace.restype = c_int64
+    L.mla_project_step.argtypes = [P, P, P, P, P, c_int32, ctypes.POINTER(CacheDesc), P, c_int32, P, c_int32,
+                                   c_int32, c_int32, c_int32, c_int32, c_int32, ctypes.POINTER(Rope), P, P, P,
+                                   c_int64, P]
     L.mla_set_launch_events.argtypes = [P, c_int32]
     L.mla_set_launch_events.restype = c_int32
     L.mla_launch_events_used.argtypes = []
@@ -121,7 +126,7 @@ def load() -> ctypes.CDLL:
     for name in ("mla_decode_plan", "mla_decode", "mla_decode_partial", "mla_decode_finish",
                  "mla_combine_lse", "mla_absorb_q",
                  "mla_absorb_out", "mla_gather_paged", "mla_rope_freqs", "mla_cache_append",
-                 "mla_project_q"):
+                 "mla_project_q", "mla_project_step"):
         getattr(L, name).restype = c_int32
     _lib = L
     return L

@@ -233,3 +233,33 @@ def project_q(h, w_dq, w_uq, w_qr, w_uk, pos, n_h: int, d_nope: int, d_r: int, r
                                    q_lora, n_h, d_nope, d_c, d_r, ctypes.byref(rope_cfg), _p(q_lat), _p(q_rope),
                                    _p(ws), ws.numel(), _stream(stream)))
     return q_lat, q_rope
+
+
+def project_step_workspace_bytes(B, q_len, d_model, q_lora, n_h, d_nope, d_c, d_r, dtype) -> int:
+    """0 when the shape or dtype has no fused path (use project_q and cache_append)."""
+    return int(L.load().mla_project_step_workspace(B, q_len, d_model, q_lora, n_h, d_nope, d_c, d_r, _DT[dtype]))
+
+
+def project_step(h, w_dkvq, w_uq, w_qr, w_uk, cache: DeviceCache, block_table, pos0, q_len: int, n_h: int,
+                 d_nope: int, rope_cfg: L.Rope, q_lat=None, q_rope=None, ws=None, stream=None):
+    """mla_project_step: h [B*q_len, d_model], w_dkvq [d_model, q_lora + d_c + d_r]
+    (W^DQ | W^DKV | W^KR columns) -> (q_lat [T, n_h, d_c], q_rope [T, n_h, d_r]),
+    and the new tokens' rows written into `cache` at pos0[b] .. pos0[b] + q_len - 1."""
+    T, d_model = h.shape
+    B = T // q_len
+    d_c, d_r = cache.d_c, cache.d_r
+    q_lora = w_dkvq.shape[1] - d_c - d_r
+    dev, dt = h.device, h.dtype
+    if q_lat is None:
+        q_lat = torch.empty((T, n_h, d_c), dtype=dt, device=dev)
+    if q_rope is None:
+        q_rope = torch.empty((T, n_h, d_r), dtype=dt, device=dev)
+    need = project_step_workspace_bytes(B, q_len, d_model, q_lora, n_h, d_nope, d_c, d_r, dt)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    desc = cache.desc()
+    L.check(L.load().mla_project_step(_p(h), _p(w_dkvq), _p(w_uq), _p(w_qr), _p(w_uk), _DT[dt], ctypes.byref(desc),
+                                      _p(block_table), block_table.stride(0), _p(pos0), B, q_len, d_model, q_lora,
+                                      n_h, d_nope, ctypes.byref(rope_cfg), _p(q_lat), _p(q_rope), _p(ws), ws.numel(),
+                                      _stream(stream)))
+    return q_lat, q_rope

@@ -120,6 +120,16 @@ hipError_t launch_project_q(const void *h, const void *w_dq, const void *w_uq, c
                             int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope, int32_t d_c,
                             int32_t d_r, const RopeTab &rt, void *q_lat, void *q_rope, void *ws,
                             hipStream_t s);
+bool project_step_ok(mla_dtype_t dt, int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope,
+                     int32_t d_c, int32_t d_r);
+int64_t project_step_workspace(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_c,
+                               int32_t d_r);
+hipError_t launch_project_step(const void *h, const void *w_dkvq, const void *w_uq, const void *w_qr,
+                               const void *w_uk, uint8_t *pool, float *scales, int64_t block_bytes,
+                               int64_t num_blocks, mla_dtype_t kv, const int32_t *bt, int32_t bt_stride,
+                               const int32_t *pos0, int32_t B, int32_t q_len, int32_t d_model, int32_t q_lora,
+                               int32_t n_h, int32_t d_c, int32_t d_r, const RopeTab &rt, void *q_lat,
+                               void *q_rope, void *ws, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers
 

@@ -771,6 +771,55 @@ mla_status_t mla_project_q(const void *h, const void *w_dq, const void *w_uq, co
                       "project_q launch");
 }
 
+int64_t mla_project_step_workspace(int32_t B, int32_t q_len, int32_t d_model, int32_t q_lora, int32_t n_h,
+                                   int32_t d_nope, int32_t d_c, int32_t d_r, mla_dtype_t dt) {
+    if (B < 1 || q_len < 1 || (int64_t)B * q_len > INT32_MAX || d_model < 1 || q_lora < 1 || n_h < 1 ||
+        d_nope < 1 || d_c < 1 || d_r < 1)
+        return 0;
+    if (!project_step_ok(dt, B * q_len, d_model, q_lora, n_h, d_nope, d_c, d_r)) return 0;
+    return project_step_workspace(B * q_len, d_model, q_lora, n_h, d_c, d_r);
+}
+
+mla_status_t mla_project_step(const void *h, const void *w_dkvq, const void *w_uq, const void *w_qr,
+                              const void *w_uk, mla_dtype_t dt, const mla_cache_desc_t *cache,
+                              const int32_t *block_table, int32_t bt_stride, const int32_t *pos0, int32_t B,
+                              int32_t q_len, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope,
+                              const mla_rope_t *rope, void *q_lat, void *q_rope, void *workspace,
+                              int64_t workspace_bytes, mla_stream_t stream) {
+    mla_status_t st = check_cache(cache);
+    if (st != MLA_OK) return st;
+    if (!h || !w_dkvq || !w_uq || !w_qr || !w_uk || !block_table || !pos0 || !rope || !q_lat || !q_rope)
+        return fail(MLA_ERR_INVALID_ARG, "NULL h/w_dkvq/w_uq/w_qr/w_uk/block_table/pos0/rope/q_lat/q_rope");
+    if (B < 1 || q_len < 1 || (int64_t)B * q_len > INT32_MAX || d_model < 1 || q_lora < 1 || n_h < 1 ||
+        d_nope < 1 || bt_stride < 1)
+        return fail(MLA_ERR_INVALID_ARG, "bad sizes B=%d q_len=%d d_model=%d q_lora=%d n_h=%d d_nope=%d bt_stride=%d",
+                    B, q_len, d_model, q_lora, n_h, d_nope, bt_stride);
+    const int32_t d_c = cache->d_c, d_r = cache->d_r, T = B * q_len;
+    if (d_r < 1) return fail(MLA_ERR_UNSUPPORTED, "project_step needs d_r > 0");
+    if (!project_step_ok(dt, T, d_model, q_lora, n_h, d_nope, d_c, d_r))
+        return fail(MLA_ERR_UNSUPPORTED,
+                    "project_step shape (dt=%d T=%d d_model=%d q_lora=%d n_h=%d d_nope=%d d_c=%d d_r=%d): use "
+                    "mla_project_q and mla_cache_append", (int)dt, T, d_model, q_lora, n_h, d_nope, d_c, d_r);
+    RopeTab t{};
+    if (!rope_table(rope, d_r, &t))
+        return fail(MLA_ERR_INVALID_ARG, "bad rope (d_r=%d base=%g factor=%g orig_ctx=%g mscale=%g)", d_r,
+                    rope->base, rope->factor, rope->orig_ctx, rope->mscale);
+    const int64_t need = project_step_workspace(T, d_model, q_lora, n_h, d_c, d_r);
+    if (workspace_bytes < need)
+        return fail(MLA_ERR_WORKSPACE, "project_step workspace %lld < %lld", (long long)workspace_bytes,
+                    (long long)need);
+    if (!workspace || !aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace NULL or not 256-byte aligned");
+    if (!aligned(h, 16) || !aligned(w_dkvq, 16) || !aligned(w_uq, 16) || !aligned(w_qr, 16) || !aligned(w_uk, 16) ||
+        !aligned(q_lat, 16) || !aligned(q_rope, 16))
+        return fail(MLA_ERR_ALIGN, "project_step operands must be 16-byte aligned");
+    return hip_status(launch_project_step(h, w_dkvq, w_uq, w_qr, w_uk, (uint8_t *)cache->base,
+                                          (float *)cache->block_scales,
+                                          block_bytes_of(cache->kv_dtype, d_c, d_r), cache->num_blocks,
+                                          cache->kv_dtype, block_table, bt_stride, pos0, B, q_len, d_model, q_lora,
+                                          n_h, d_c, d_r, t, q_lat, q_rope, workspace, (hipStream_t)stream),
+                      "project_step launch");
+}
+
 mla_status_t mla_gather_paged(const mla_cache_desc_t *cache, const int32_t *block_table,
                               int32_t bt_stride, const int32_t *seq_lens, int32_t B,
                               int32_t max_tokens, void *out, mla_stream_t stream) {

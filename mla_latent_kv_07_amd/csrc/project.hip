@@ -135,8 +135,9 @@ __device__ __forceinline__ float split_sum(const float *__restrict__ ws, int64_t
 }
 
 struct AppendArgs {
-    const float *ws;          // fp32 partials [splits][T][d_c + d_r]
+    const float *ws;          // fp32 partials: split s, token t, value f at ws[s split_stride + t ws_ld + f]
     int64_t split_stride;
+    int64_t ws_ld;            // d_c + d_r, or wider when the row's columns share a partial buffer
     int32_t splits;
     uint8_t *pool;
     float *scales;
@@ -156,7 +157,7 @@ struct AppendArgs {
 // raises the block scale, earlier slots are re-encoded when it grows, then
 // the codes are written.
 template <int CODE>   // 0 e4m3 latent, 1 e5m2 latent, 2 e4m3 whole row
-__global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab rt) {
+__device__ __forceinline__ void append_fp8_seq(const AppendArgs &a, const RopeTab &rt, int b) {
     constexpr bool ROWC = CODE == 2;
     constexpr float TOP = CODE == 1 ? 57344.f : 448.f;
     auto enc = [](float v) { return CODE == 1 ? f32_to_e5m2(v) : f32_to_e4m3(v); };
@@ -164,10 +165,9 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab r
     const int W = ROWC ? a.d_c + a.d_r : a.d_c;   // code bytes per token
     __shared__ float red[4];
     __shared__ float sh[3];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int N = a.d_c + a.d_r;
+    const int tid = threadIdx.x;
     const int p0 = a.pos0[b];
-    auto xval = [&](int t, int f) { return split_sum(a.ws, a.split_stride, a.splits, (int64_t)t * N + f); };
+    auto xval = [&](int t, int f) { return split_sum(a.ws, a.split_stride, a.splits, (int64_t)t * a.ws_ld + f); };
     auto block_of = [&](int p) { return (int64_t)a.bt[(int64_t)b * a.bt_stride + p / kBlock]; };
     // rotary pair j of token t at position p: rotated, times mscale
     auto rot = [&](int t, int p, int j, float &y0, float &y1) {
@@ -252,19 +252,23 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab r
     }
 }
 
+template <int CODE>
+__global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a, RopeTab rt) {
+    append_fp8_seq<CODE>(a, rt, blockIdx.x);
+}
+
 // f32 / bf16 caches: one thread per (token, pair of row values); the rotary
 // pairs turn by p theta_j (fp64 angle), then every value is rounded once.
 template <int FMT>   // 0 f32, 1 bf16, 2 f16
-__global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab rt) {
+__device__ __forceinline__ void append_row_pair(const AppendArgs &a, const RopeTab &rt, int64_t idx) {
     const int N = a.d_c + a.d_r, P2 = N / 2;
-    const int64_t idx = blockIdx.x * 256ll + threadIdx.x;
     if (idx >= (int64_t)a.q_len * a.pos0_count * P2) return;
     const int t = (int)(idx / P2), k = (int)(idx % P2);
     const int b = t / a.q_len, p = a.pos0[b] + t % a.q_len;
     if (p < 0 || p / kBlock >= a.bt_stride) return;   // outside the table: not written
     const int64_t blk = a.bt[(int64_t)b * a.bt_stride + p / kBlock];
     if (blk < 0 || blk >= a.num_blocks) return;       // unallocated table slot: not written
-    const int64_t o = (int64_t)t * N + 2 * k;
+    const int64_t o = (int64_t)t * a.ws_ld + 2 * k;
     float y0 = split_sum<32>(a.ws, a.split_stride, a.splits, o);
     float y1 = split_sum<32>(a.ws, a.split_stride, a.splits, o + 1);
     if (2 * k >= a.d_c) {
@@ -287,12 +291,20 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab 
     }
 }
 
-// q^R: out[t][h][2j, 2j+1] = RoPE of the summed partials at pos[t], times
-// mscale; item idx = (token, head, pair), angle p theta_j in fp64.
+template <int FMT>
+__global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a, RopeTab rt) {
+    append_row_pair<FMT>(a, rt, blockIdx.x * 256ll + threadIdx.x);
+}
+
+// q^R: out[t][h][2j, 2j+1] = RoPE of the summed partials at token t's
+// position, times mscale; item idx = (token, head, pair), angle p theta_j in
+// fp64.  Positions: pos[t] (pos_q_len 1), or pos[t / q_len] + t % q_len when
+// pos holds each sequence's first new position (pos_q_len = q_len).
 template <typename OutT>
 __device__ __forceinline__ void rope_q_item(int64_t idx, const float *__restrict__ ws, int64_t split_stride,
-                                            int32_t splits, const int32_t *__restrict__ pos, int32_t T, int32_t n_h,
-                                            int32_t d_r, OutT *__restrict__ out, const RopeTab &rt) {
+                                            int32_t splits, const int32_t *__restrict__ pos, int32_t pos_q_len,
+                                            int32_t T, int32_t n_h, int32_t d_r, OutT *__restrict__ out,
+                                            const RopeTab &rt) {
     const int64_t per_t = (int64_t)n_h * rt.half;
     if (idx >= T * per_t) return;
     const int t = (int)(idx / per_t), hj = (int)(idx % per_t);
@@ -300,7 +312,8 @@ __device__ __forceinline__ void rope_q_item(int64_t idx, const float *__restrict
     const int64_t o = (int64_t)t * n_h * d_r + (int64_t)h * d_r + 2 * j;
     const float x0 = split_sum(ws, split_stride, splits, o), x1 = split_sum(ws, split_stride, splits, o + 1);
     double sn, cs;
-    sincos((double)pos[t] * rt.theta[j], &sn, &cs);
+    const int p = pos[t / pos_q_len] + t % pos_q_len;
+    sincos((double)p * rt.theta[j], &sn, &cs);
     const float c = (float)cs, s = (float)sn;
     const float y0 = (x0 * c - x1 * s) * rt.mscale, y1 = (x0 * s + x1 * c) * rt.mscale;
     if constexpr (sizeof(OutT) == 2) {
@@ -311,39 +324,104 @@ __device__ __forceinline__ void rope_q_item(int64_t idx, const float *__restrict
     }
 }
 
+// The q^R items [256 blk, 256 blk + 256) of one 256-thread block: every
+// head of a token turns by the same angles, so the block first forms the
+// (cos, sin) of each (token, pair) it touches once, in LDS, then each
+// thread rotates its item as rope_q_item does (the same values: the angle
+// is the same fp64 product).
+__device__ __forceinline__ void rope_q_block(int blk, const float *__restrict__ ws, int64_t split_stride,
+                                             int32_t splits, const int32_t *__restrict__ pos, int32_t pos_q_len,
+                                             int32_t T, int32_t n_h, int32_t d_r, uint16_t *__restrict__ out,
+                                             const RopeTab &rt) {
+    constexpr int TAB = 512;   // >= (256 / per_t + 2) * half entries for any per_t >= half
+    __shared__ float2 cs_tab[TAB];
+    const int half = rt.half;
+    const int64_t per_t = (int64_t)n_h * half;
+    const int64_t first = blk * 256ll, last = min(first + 255, (int64_t)T * per_t - 1);
+    const int t0 = (int)(first / per_t), t1 = (int)(last / per_t);
+    const int n_e = (t1 - t0 + 1) * half;
+    for (int e = threadIdx.x; e < n_e; e += 256) {
+        const int t = t0 + e / half, j = e % half;
+        const int p = pos[t / pos_q_len] + t % pos_q_len;
+        double sn, cs;
+        sincos((double)p * rt.theta[j], &sn, &cs);
+        cs_tab[e] = make_float2((float)cs, (float)sn);
+    }
+    __syncthreads();
+    const int64_t idx = first + threadIdx.x;
+    if (idx > last) return;
+    const int t = (int)(idx / per_t), hj = (int)(idx % per_t);
+    const int h = hj / half, j = hj % half;
+    const int64_t o = (int64_t)t * n_h * d_r + (int64_t)h * d_r + 2 * j;
+    const float x0 = split_sum(ws, split_stride, splits, o), x1 = split_sum(ws, split_stride, splits, o + 1);
+    const float2 r = cs_tab[(t - t0) * half + j];
+    const float y0 = (x0 * r.x - x1 * r.y) * rt.mscale, y1 = (x0 * r.y + x1 * r.x) * rt.mscale;
+    *(uint32_t *)(out + o) = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
+}
+
 // one thread per (token, head, pair)
 template <typename OutT>
 __global__ __launch_bounds__(256) void rope_q_kernel(const float *__restrict__ ws, int64_t split_stride,
                                                      int32_t splits, const int32_t *__restrict__ pos,
                                                      int32_t T, int32_t n_h, int32_t d_r, OutT *__restrict__ out,
                                                      RopeTab rt) {
-    rope_q_item(blockIdx.x * 256ll + threadIdx.x, ws, split_stride, splits, pos, T, n_h, d_r, out, rt);
+    rope_q_item(blockIdx.x * 256ll + threadIdx.x, ws, split_stride, splits, pos, 1, T, n_h, d_r, out, rt);
 }
 
-// The two finishes of the low-rank query products in one launch: blocks
-// [0, nb_cq) write c^Q = bf16(sum of the h W^DQ partials), 8 consecutive
-// values per thread; the others q^R = RoPE(sum of the h W^QR partials), one
+// Arguments of the finishing kernel of the low-rank query products.
+struct FinishArgs {
+    const float *ws1;          // h W^DQ partials: split s, token t, column c at ws1[(s T + t) ld1 + c]
+    int32_t sp1, ld1, q_lora;
+    uint16_t *cq;              // c^Q [T][q_lora], bf16
+    int32_t nb_cq;             // blocks of the c^Q part
+    const float *ws3;          // h W^QR partials [sp3][T][n_h d_r]
+    int32_t sp3;
+    const int32_t *pos;        // positions, as rope_q_item reads them (pos_q_len)
+    int32_t pos_q_len, T, n_h, d_r;
+    uint16_t *q_rope;          // q^R [T][n_h][d_r], bf16
+    int32_t nb_rope;           // blocks of the q^R part
+};
+
+// The finishes of the low-rank query products in one launch.  APP >= 0
+// (one decode step's producers): the first blocks finish the new cache rows,
+// whose partials share the h W^DQ buffer: APP 0-2 one row-value pair per
+// thread (append_row_pair, f32 / bf16 / f16 rows), APP 3-5 one block per
+// sequence (append_fp8_seq, e4m3 / e5m2 latent, whole row in e4m3); they
+// come first so that none of them trails the launch.  Then nb_cq blocks
+// write c^Q = bf16(sum of the h W^DQ partials), 8 consecutive values per
+// thread, and nb_rope blocks q^R = RoPE(sum of the h W^QR partials), one
 // rotary pair per thread.
-__global__ __launch_bounds__(256) void q_finish_kernel(const float *__restrict__ ws1, int32_t sp1, int64_t n8,
-                                                       uint16_t *__restrict__ cq, int32_t nb_cq,
-                                                       const float *__restrict__ ws3, int32_t sp3,
-                                                       const int32_t *__restrict__ pos, int32_t T, int32_t n_h,
-                                                       int32_t d_r, uint16_t *__restrict__ q_rope, RopeTab rt) {
-    if ((int)blockIdx.x >= nb_cq) {
-        rope_q_item((blockIdx.x - nb_cq) * 256ll + threadIdx.x, ws3, (int64_t)T * n_h * d_r, sp3, pos, T, n_h, d_r,
-                    q_rope, rt);
+template <int APP>
+__global__ __launch_bounds__(256) void q_finish_kernel(FinishArgs f, RopeTab rt, AppendArgs app) {
+    int blk = blockIdx.x;
+    if constexpr (APP >= 0) {
+        const int nb_app = (int)gridDim.x - f.nb_cq - f.nb_rope;
+        if (blk < nb_app) {
+            if constexpr (APP >= 3) append_fp8_seq<APP - 3>(app, rt, blk);
+            else append_row_pair<APP>(app, rt, blk * 256ll + threadIdx.x);
+            return;
+        }
+        blk -= nb_app;
+    }
+    if (blk >= f.nb_cq) {
+        rope_q_block(blk - f.nb_cq, f.ws3, (int64_t)f.T * f.n_h * f.d_r, f.sp3, f.pos, f.pos_q_len, f.T, f.n_h,
+                     f.d_r, f.q_rope, rt);
         return;
     }
-    const int64_t i = blockIdx.x * 256ll + threadIdx.x;
-    if (i >= n8) return;
+    const int64_t i = blk * 256ll + threadIdx.x;
+    const int per_t = f.q_lora / 8;
+    if (i >= (int64_t)f.T * per_t) return;
+    const int t = (int)(i / per_t), c8 = (int)(i % per_t);
+    const float *src = f.ws1 + (int64_t)t * f.ld1 + 8 * c8;
+    const int64_t sstride = (int64_t)f.T * f.ld1;
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     // four splits' loads in flight per round
-    for (int s0 = 0; s0 < sp1; s0 += 4) {
+    for (int s0 = 0; s0 < f.sp1; s0 += 4) {
         float4 x[4], y[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if (s0 + k < sp1) {
-                const float4 *p = (const float4 *)(ws1 + (int64_t)(s0 + k) * n8 * 8 + 8 * i);
+            if (s0 + k < f.sp1) {
+                const float4 *p = (const float4 *)(src + (s0 + k) * sstride);
                 x[k] = p[0];
                 y[k] = p[1];
             } else {
@@ -361,7 +439,7 @@ __global__ __launch_bounds__(256) void q_finish_kernel(const float *__restrict__
     pk.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
     pk.z = (uint32_t)f32_to_bf16(a[4]) | ((uint32_t)f32_to_bf16(a[5]) << 16);
     pk.w = (uint32_t)f32_to_bf16(a[6]) | ((uint32_t)f32_to_bf16(a[7]) << 16);
-    *(uint4 *)(cq + 8 * i) = pk;
+    *(uint4 *)(f.cq + (int64_t)t * f.q_lora + 8 * c8) = pk;
 }
 
 template <typename T>
@@ -442,7 +520,7 @@ hipError_t launch_cache_append(const void *h, const void *w_kv, mla_dtype_t dt, 
     }
     if (e != hipSuccess) return e;
     AppendArgs a{};
-    a.ws = ws; a.split_stride = (int64_t)T * N; a.splits = sp;
+    a.ws = ws; a.split_stride = (int64_t)T * N; a.ws_ld = N; a.splits = sp;
     a.pool = pool; a.scales = scales; a.block_bytes = block_bytes; a.num_blocks = num_blocks;
     a.bt = bt; a.bt_stride = bt_stride; a.pos0 = pos0; a.pos0_count = B; a.q_len = q_len;
     a.d_c = d_c; a.d_r = d_r;
@@ -465,6 +543,18 @@ hipError_t launch_cache_append(const void *h, const void *w_kv, mla_dtype_t dt, 
 // ---------------------------------------------------------------- queries
 
 namespace {
+
+FinishArgs finish_args(const float *ws1, int sp1, int32_t ld1, int32_t q_lora, uint16_t *cq, const float *ws3,
+                       int sp3, const int32_t *pos, int32_t pos_q_len, int32_t T, int32_t n_h, int32_t d_r,
+                       uint16_t *q_rope) {
+    FinishArgs f{};
+    f.ws1 = ws1; f.sp1 = sp1; f.ld1 = ld1; f.q_lora = q_lora; f.cq = cq;
+    f.nb_cq = (int32_t)(((int64_t)T * q_lora / 8 + 255) / 256);
+    f.ws3 = ws3; f.sp3 = sp3; f.pos = pos; f.pos_q_len = pos_q_len; f.T = T; f.n_h = n_h; f.d_r = d_r;
+    f.q_rope = q_rope;
+    f.nb_rope = (int32_t)(((int64_t)T * n_h * (d_r / 2) + 255) / 256);
+    return f;
+}
 
 struct QPlan {
     bool mfma;
@@ -515,13 +605,10 @@ hipError_t launch_project_q(const void *h, const void *w_dq, const void *w_uq, c
                                     q.sp1, s);
         if (e != hipSuccess) return e;
         // c^Q = bf16(sum of its partials) and q^R = RoPE(sum of its partials)
-        const int64_t n8 = (int64_t)T * q_lora / 8;
-        const int nb_cq = (int)((n8 + 255) / 256);
-        const int64_t nrope = (int64_t)T * n_h * (d_r / 2);
-        const unsigned nb = (unsigned)(nb_cq + (nrope + 255) / 256);
-        launch_timed(q_finish_kernel, dim3(nb), dim3(256), 0, s, (const float *)w1, (int32_t)q.sp1, n8,
-                     (uint16_t *)(w + q.off_cq), (int32_t)nb_cq, (const float *)w3, (int32_t)q.sp3, pos, T, n_h,
-                     d_r, (uint16_t *)q_rope, rt);
+        const FinishArgs f = finish_args(w1, q.sp1, q_lora, q_lora, (uint16_t *)(w + q.off_cq), w3, q.sp3, pos,
+                                         1, T, n_h, d_r, (uint16_t *)q_rope);
+        launch_timed(q_finish_kernel<-1>, dim3((unsigned)(f.nb_cq + f.nb_rope)), dim3(256), 0, s, f, rt,
+                     AppendArgs{});
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         // q~ = (c^Q W^UQ) W^UK^T per head, q^C kept on chip
@@ -569,6 +656,87 @@ hipError_t launch_project_q(const void *h, const void *w_dq, const void *w_uq, c
         launch_timed(rope_q_kernel<float>, dim3(rg), dim3(256), 0, s, w3, (int64_t)T * NR, q.sp3, pos,
                            T, n_h, d_r, (float *)q_rope, rt);
     return hipGetLastError();
+}
+
+// ------------------------------------------------- one decode step's producers
+
+namespace {
+
+// The three down-projections of h, side by side in one weight
+// [d_model][q_lora + d_c + d_r] (W^DQ, W^DKV, W^KR columns), are product 1
+// of the paired launch, h W^QR product 0: the cache row's product rides in
+// the query's launch, its finish in the query finish.
+struct StepPlan {
+    int sp1, sp3;
+    int32_t N1;
+    int64_t off_cq, off_w1, off_w3, total;
+};
+
+StepPlan step_plan(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_c, int32_t d_r) {
+    StepPlan p{};
+    p.N1 = q_lora + d_c + d_r;
+    const int32_t NR = n_h * d_r;
+    gemm_pair_splits(T, NR, d_model, p.N1, d_model, &p.sp3, &p.sp1);
+    int64_t o = 0;
+    p.off_cq = o; o = align256(o + (int64_t)T * q_lora * 2);
+    p.off_w1 = o; o = align256(o + (int64_t)p.sp1 * T * p.N1 * 4);
+    p.off_w3 = o; o = align256(o + (int64_t)p.sp3 * T * NR * 4);
+    p.total = o;
+    return p;
+}
+
+}  // namespace
+
+bool project_step_ok(mla_dtype_t dt, int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_nope,
+                     int32_t d_c, int32_t d_r) {
+    const int32_t NQ = n_h * d_nope, NR = n_h * d_r;
+    return dt == MLA_DT_BF16 && d_r > 0 && gemm_nn_mfma_ok(q_lora, d_model) && gemm_nn_mfma_ok(NQ, q_lora) &&
+           gemm_nn_mfma_ok(NR, d_model) && gemm_nn_mfma_ok(q_lora + d_c + d_r, d_model) && d_nope % 64 == 0 &&
+           d_c % 128 == 0 && (d_c + d_r) % 2 == 0 && q_up_absorb_ok(T, n_h, d_nope, d_c, q_lora);
+}
+
+int64_t project_step_workspace(int32_t T, int32_t d_model, int32_t q_lora, int32_t n_h, int32_t d_c,
+                               int32_t d_r) {
+    return step_plan(T, d_model, q_lora, n_h, d_c, d_r).total;
+}
+
+hipError_t launch_project_step(const void *h, const void *w_dkvq, const void *w_uq, const void *w_qr,
+                               const void *w_uk, uint8_t *pool, float *scales, int64_t block_bytes,
+                               int64_t num_blocks, mla_dtype_t kv, const int32_t *bt, int32_t bt_stride,
+                               const int32_t *pos0, int32_t B, int32_t q_len, int32_t d_model, int32_t q_lora,
+                               int32_t n_h, int32_t d_c, int32_t d_r, const RopeTab &rt, void *q_lat,
+                               void *q_rope, void *ws, hipStream_t s) {
+    const int32_t T = B * q_len, NR = n_h * d_r;
+    const StepPlan p = step_plan(T, d_model, q_lora, n_h, d_c, d_r);
+    uint8_t *w = (uint8_t *)ws;
+    float *w1 = (float *)(w + p.off_w1), *w3 = (float *)(w + p.off_w3);
+    // h W^QR, and h [W^DQ | W^DKV | W^KR] (split over d_model into fp32 partials), in one launch
+    hipError_t e = launch_gemm_nn_f32_pair(h, d_model, T, d_model, w_qr, NR, w3, NR, p.sp3, w_dkvq, p.N1, w1,
+                                           p.N1, p.sp1, s);
+    if (e != hipSuccess) return e;
+    // c^Q, q^R and the new cache rows from their partials
+    const FinishArgs f = finish_args(w1, p.sp1, p.N1, q_lora, (uint16_t *)(w + p.off_cq), w3, p.sp3, pos0, q_len,
+                                     T, n_h, d_r, (uint16_t *)q_rope);
+    AppendArgs a{};
+    a.ws = w1 + q_lora; a.split_stride = (int64_t)T * p.N1; a.ws_ld = p.N1; a.splits = p.sp1;
+    a.pool = pool; a.scales = scales; a.block_bytes = block_bytes; a.num_blocks = num_blocks;
+    a.bt = bt; a.bt_stride = bt_stride; a.pos0 = pos0; a.pos0_count = B; a.q_len = q_len;
+    a.d_c = d_c; a.d_r = d_r;
+    const unsigned nb = (unsigned)(f.nb_cq + f.nb_rope);
+    const unsigned rows = (unsigned)(((int64_t)T * ((d_c + d_r) / 2) + 255) / 256);
+    switch (kv) {
+    case MLA_DT_F32: launch_timed(q_finish_kernel<0>, dim3(nb + rows), dim3(256), 0, s, f, rt, a); break;
+    case MLA_DT_BF16: launch_timed(q_finish_kernel<1>, dim3(nb + rows), dim3(256), 0, s, f, rt, a); break;
+    case MLA_DT_F16: launch_timed(q_finish_kernel<2>, dim3(nb + rows), dim3(256), 0, s, f, rt, a); break;
+    case MLA_DT_FP8_E4M3: launch_timed(q_finish_kernel<3>, dim3(nb + B), dim3(256), 0, s, f, rt, a); break;
+    case MLA_DT_FP8_E5M2: launch_timed(q_finish_kernel<4>, dim3(nb + B), dim3(256), 0, s, f, rt, a); break;
+    case MLA_DT_FP8_E4M3_ROW: launch_timed(q_finish_kernel<5>, dim3(nb + B), dim3(256), 0, s, f, rt, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // q~ = (c^Q W^UQ) W^UK^T per head, q^C kept on chip
+    return launch_q_up_absorb(w + p.off_cq, q_lora, w_uq, w_uk, q_lat, T, n_h, q_lora, s);
 }
 
 }  // namespace mla

@@ -69,23 +69,60 @@ def _run_appends(fmt, B, calls, d_c, d_r, d_model, seed, rope=None, dt=torch.bfl
         h = h_dev.double().numpy()
         api.cache_append(h_dev.to(DEV), w_dev, cache, bt_dev, torch.from_numpy(pos).to(DEV), ql, cfg)
         O.cache_append(o_pool, o_scales, fmt, d_c, d_r, bt, pos, ql, h, w, inv_freq=inv, mscale=cfg.mscale)
-        for b in range(B):
-            for i in range(ql):
-                p = int(pos[b]) + i
-                blk, sl = bt[b, p // BLK], p % BLK
-                if fmt == O.FMT_FP8_E4M3_ROW:
-                    mask[blk, :(sl + 1) * (d_c + d_r)] = True   # earlier codes may be re-encoded
-                elif fmt in O.FP8_SPLIT:
-                    mask[blk, :(sl + 1) * d_c] = True     # earlier codes may be re-encoded
-                    off = BLK * d_c + sl * 2 * d_r
-                    mask[blk, off:off + 2 * d_r] = True
-                else:
-                    rb = O.block_bytes(fmt, d_c, d_r) // BLK
-                    mask[blk, sl * rb:(sl + 1) * rb] = True
+        _mark_written(mask, fmt, bt, pos, ql, d_c, d_r)
         pos += ql
     torch.cuda.synchronize()
     g_scales = cache.block_scales.cpu().numpy() if fmt in O.SCALED else None
     return cache.pool.cpu().numpy(), g_scales, o_pool, o_scales, pool0, mask
+
+
+def _mark_written(mask, fmt, bt, pos, q_len, d_c, d_r):
+    """Set the pool bytes that appending q_len tokens per sequence at pos may
+    change (for fp8 formats the earlier codes of a block, which a growing
+    scale re-encodes)."""
+    for b in range(len(pos)):
+        for i in range(q_len):
+            p = int(pos[b]) + i
+            blk, sl = bt[b, p // BLK], p % BLK
+            if fmt == O.FMT_FP8_E4M3_ROW:
+                mask[blk, :(sl + 1) * (d_c + d_r)] = True
+            elif fmt in O.FP8_SPLIT:
+                mask[blk, :(sl + 1) * d_c] = True
+                off = BLK * d_c + sl * 2 * d_r
+                mask[blk, off:off + 2 * d_r] = True
+            else:
+                rb = O.block_bytes(fmt, d_c, d_r) // BLK
+                mask[blk, sl * rb:(sl + 1) * rb] = True
+
+
+def _check_fp8(got, want, g_sc, w_sc, mask, fmt, d_c, d_r):
+    """fp8 payloads against the oracle: scales of the touched blocks within
+    1e-6, the others unchanged; codes at most one step apart where the fp32
+    and fp64 products fall on opposite sides of a rounding point; bf16
+    rotary keys as 16-bit rows."""
+    touched = np.unique(np.nonzero(mask)[0])
+    np.testing.assert_allclose(g_sc[touched], w_sc[touched], rtol=1e-6)
+    other = np.setdiff1d(np.arange(len(g_sc)), touched)
+    assert np.array_equal(g_sc[other], w_sc[other])
+    W = d_c + d_r if fmt == O.FMT_FP8_E4M3_ROW else d_c
+    codes = np.zeros(mask.shape, bool)
+    codes[:, :BLK * W] = True
+    cm = mask & codes
+    g, w = got[cm], want[cm]
+    gv, wv = O.fp8_decode(fmt, g), O.fp8_decode(fmt, w)
+    diff = np.count_nonzero(g != w)
+    say(f"  fp8 codes: {g.size}, {diff} differ")
+    assert diff <= max(4, g.size // 500)
+    step = (np.maximum(np.abs(wv) * 2.0 ** -3, 2.0 ** -9) if fmt != O.FMT_FP8_E5M2
+            else np.maximum(np.abs(wv) * 2.0 ** -2, 2.0 ** -16))
+    nan = np.isnan(wv)
+    assert np.array_equal(np.isnan(gv), nan)
+    # equal codes pass as they are (blocks written before may hold inf codes)
+    d = (g != w) & ~nan
+    assert np.all(np.abs(gv - wv)[d] <= step[d] * 1.0001)
+    if fmt != O.FMT_FP8_E4M3_ROW:
+        rm = mask & ~codes
+        _check_16bit_rows(got[:, BLK * d_c:], want[:, BLK * d_c:], rm[:, BLK * d_c:], "bf16")
 
 
 def _check_16bit_rows(got, want, mask, what):
@@ -156,28 +193,7 @@ def test_append_fp8_scale_growth(fmt):
     got, g_sc, want, w_sc, pool0, mask = _run_appends(fmt, B, [1, 3, 70, 1], d_c, d_r, dm,
                                                       seed=23, start=0, h_scale=[0.1, 1.0, 3.0, 10.0])
     assert np.array_equal(got[~mask], pool0[~mask])
-    touched = np.unique(np.nonzero(mask)[0])
-    np.testing.assert_allclose(g_sc[touched], w_sc[touched], rtol=1e-6)
-    other = np.setdiff1d(np.arange(len(g_sc)), touched)
-    assert np.array_equal(g_sc[other], w_sc[other])
-    W = d_c + d_r if fmt == O.FMT_FP8_E4M3_ROW else d_c
-    codes = np.zeros(mask.shape, bool)
-    codes[:, :BLK * W] = True
-    cm = mask & codes
-    g, w = got[cm], want[cm]
-    # one code step apart at most
-    gv, wv = O.fp8_decode(fmt, g), O.fp8_decode(fmt, w)
-    diff = np.count_nonzero(g != w)
-    say(f"  fp8 codes: {g.size}, {diff} differ")
-    assert diff <= max(4, g.size // 500)
-    step = (np.maximum(np.abs(wv) * 2.0 ** -3, 2.0 ** -9) if fmt != O.FMT_FP8_E5M2
-            else np.maximum(np.abs(wv) * 2.0 ** -2, 2.0 ** -16))
-    nan = np.isnan(wv)
-    assert np.array_equal(np.isnan(gv), nan)
-    assert np.all(np.abs(gv - wv)[~nan] <= step[~nan] * 1.0001)
-    if fmt != O.FMT_FP8_E4M3_ROW:
-        rm = mask & ~codes
-        _check_16bit_rows(got[:, BLK * d_c:], want[:, BLK * d_c:], rm[:, BLK * d_c:], "bf16")
+    _check_fp8(got, want, g_sc, w_sc, mask, fmt, d_c, d_r)
 
 
 def test_append_full_size_decode_step():
@@ -305,3 +321,53 @@ def test_append_skips_unallocated_table_slots(fmt):
         nan = np.isnan(wv)
         assert np.array_equal(np.isnan(gv), nan)
         assert np.all(np.abs(gv - wv)[~nan] <= step[~nan] * 1.0001)
+
+
+@pytest.mark.parametrize("fmt,B,q_len,dm,ql,n_h", [
+    (O.FMT_BF16, 128, 1, 5120, 1536, 128),     # the layer workload's decode step
+    (O.FMT_BF16, 5, 3, 256, 128, 4),           # three tokens per sequence, some crossing a block
+    (O.FMT_FP8_E4M3, 5, 3, 256, 128, 4),
+    (O.FMT_F16, 3, 2, 256, 128, 2),
+    (O.FMT_FP8_E4M3_ROW, 3, 2, 256, 64, 2),
+    (O.FMT_FP8_E5M2, 2, 70, 256, 128, 1)])      # 70 tokens: block crossings, scale growth
+def test_project_step_matches_the_separate_calls(fmt, B, q_len, dm, ql, n_h):
+    """mla_project_step (queries and cache rows from one hidden state, the
+    three down-projections as one weight): q_lat and q_rope bit-identical to
+    mla_project_q's on the same inputs (same products, same splits of h W^DQ
+    and h W^QR); the cache rows against the oracle within the append tests'
+    bounds; every other byte of the pool unchanged."""
+    dn, dc, dr = 128, 512, 64
+    T = B * q_len
+    rng, bt, pool, scales = _setup(fmt, B, q_len + 200, dc, dr, dm, seed=40 + B + q_len)
+    bf = lambda shape, std: _bf16(rng.standard_normal(shape) * std)
+    h = bf((T, dm), 1.0)
+    w_dkvq = bf((dm, ql + dc + dr), 1 / math.sqrt(dm))
+    w_uq, w_qr = bf((ql, n_h * dn), 1 / math.sqrt(ql)), bf((dm, n_h * dr), 1 / math.sqrt(dm))
+    w_uk = bf((n_h, dc, dn), 1 / math.sqrt(dc))
+    pos0 = rng.integers(0, 128, B).astype(np.int32)
+    cfg = api.rope(factor=40.0, mscale=1.0 + 0.1 * math.log(40.0))
+    pool0 = pool.copy()
+    cache = api.DeviceCache(torch.from_numpy(pool).to(DEV),
+                            torch.from_numpy(scales).to(DEV) if fmt in O.SCALED else None, KV[fmt], dc, dr)
+    D = lambda x: x.contiguous().to(DEV)
+    say(f"  project_step {KV[fmt]} B={B} q_len={q_len} d_model={dm} q_lora={ql} n_h={n_h}")
+    q_lat, q_rope = api.project_step(D(h), D(w_dkvq), D(w_uq), D(w_qr), D(w_uk), cache, D(torch.from_numpy(bt)),
+                                     D(torch.from_numpy(pos0)), q_len, n_h, dn, cfg)
+    pos_t = (pos0[:, None] + np.arange(q_len)[None, :]).reshape(-1).astype(np.int32)
+    ref_lat, ref_rope = api.project_q(D(h), D(w_dkvq[:, :ql]), D(w_uq), D(w_qr), D(w_uk),
+                                      D(torch.from_numpy(pos_t)), n_h, dn, dr, cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(q_lat, ref_lat) and torch.equal(q_rope, ref_rope)
+    got = cache.pool.cpu().numpy()
+    want, w_sc = pool.copy(), scales.copy()
+    inv = O.rope_inv_freq(dr, cfg.base, cfg.factor, cfg.orig_ctx, cfg.beta_fast, cfg.beta_slow)
+    O.cache_append(want, w_sc, fmt, dc, dr, bt, pos0, q_len, h.double().numpy(),
+                   w_dkvq[:, ql:].double().numpy(), inv_freq=inv, mscale=cfg.mscale)
+    mask = np.zeros(pool.shape, bool)
+    _mark_written(mask, fmt, bt, pos0, q_len, dc, dr)
+    assert np.array_equal(got[~mask], pool0[~mask])
+    if fmt in O.SCALED:
+        _check_fp8(got, want, cache.block_scales.cpu().numpy(), w_sc, mask, fmt, dc, dr)
+    else:
+        _check_16bit_rows(got, want, mask, KV[fmt])
+

@@ -314,6 +314,27 @@ def test_producers_reject_bad_arguments():
         a[i] = v
         assert l.mla_project_q(*a) == st, (i, v)
     assert l.mla_project_q_workspace(128, 5120, 1536, 128, 128, 512, 64, L.DT_BF16) > 0
+    # one decode step's producers: h, w_dkvq, w_uq, w_qr, w_uk, dt, cache, block table, bt_stride, pos0,
+    # B, q_len, d_model, q_lora, n_h, d_nope, rope, q_lat, q_rope, workspace, bytes, stream
+    step = [A, A, A, A, A, L.DT_BF16, ctypes.byref(d), A, 64, A, 4, 1, 5120, 1536, 128, 128, R, A, A, A, ws, None]
+    for i, v, st in [(0, None, L.MLA_ERR_INVALID_ARG), (1, None, L.MLA_ERR_INVALID_ARG),
+                     (9, None, L.MLA_ERR_INVALID_ARG), (18, None, L.MLA_ERR_INVALID_ARG),
+                     (10, 0, L.MLA_ERR_INVALID_ARG), (11, 0, L.MLA_ERR_INVALID_ARG), (8, 0, L.MLA_ERR_INVALID_ARG),
+                     (16, None, L.MLA_ERR_INVALID_ARG), (16, ctypes.byref(bad), L.MLA_ERR_INVALID_ARG),
+                     (5, L.DT_F32, L.MLA_ERR_UNSUPPORTED),        # the fused path is bf16 only
+                     (13, 1000, L.MLA_ERR_UNSUPPORTED),           # q_lora not a multiple of 64
+                     (15, 96, L.MLA_ERR_UNSUPPORTED),             # d_nope not a multiple of 64
+                     (6, ctypes.byref(_desc(block_size=32)), L.MLA_ERR_UNSUPPORTED),
+                     (20, 16, L.MLA_ERR_WORKSPACE), (1, A + 2, L.MLA_ERR_ALIGN), (17, A + 8, L.MLA_ERR_ALIGN)]:
+        a = list(step)
+        a[i] = v
+        assert l.mla_project_step(*a) == st, (i, v)
+    # its workspace: c^Q, then the two products' fp32 partials (at least one split each)
+    need = l.mla_project_step_workspace(4, 1, 5120, 1536, 128, 128, 512, 64, L.DT_BF16)
+    assert need >= 4 * 1536 * 2 + 4 * (1536 + 576) * 4 + 4 * 128 * 64 * 4
+    assert l.mla_project_step_workspace(4, 1, 5120, 1536, 128, 128, 512, 64, L.DT_F32) == 0
+    assert l.mla_project_step_workspace(4, 1, 5120, 1000, 128, 128, 512, 64, L.DT_BF16) == 0
+    assert l.mla_project_step_workspace(0, 1, 5120, 1536, 128, 128, 512, 64, L.DT_BF16) == 0
 
 
 def test_noalloc_rejects_plans_beyond_its_scratch():
