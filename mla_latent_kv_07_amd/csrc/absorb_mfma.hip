@@ -72,11 +72,14 @@ struct GemmArgs {
 // One launch over the workgroups of up to two products of the same kind
 // (one 1-D grid: units [0, units0) are product 0's, the rest product 1's).
 // Workgroup u of a product takes column-tile group x, row tile y and batch /
-// split z with u = x + tx (y + ty z).
+// split z with u = x + tx (y + ty z), or with z_first u = x + tx (z + nz y)
+// (nz = batch x splits): then the row tiles of one batch entry lie tx nz
+// apart in the grid, on one XCD when that is a multiple of 8.
 struct GemmPair {
     GemmArgs p0, p1;
     int32_t units0;
     int32_t tx0, ty0, tx1, ty1;
+    int32_t z_first, nz;   // product 0 only (single-product launches)
 };
 
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, const void *src) {
@@ -150,8 +153,9 @@ __global__ __launch_bounds__(64 * WV, NST <= NST_SHORT ? 2 : 1) void gemm_bf16_k
     const GemmArgs g = second ? G.p1 : G.p0;
     const int u = (int)blockIdx.x - (second ? G.units0 : 0);
     const int tx = second ? G.tx1 : G.tx0, ty = second ? G.ty1 : G.ty0;
-    const int ux = u % tx, uy = (u / tx) % ty;
-    const int z = u / (tx * ty), b = z / g.splits, s = z % g.splits;
+    const int ux = u % tx;
+    const int uy = G.z_first ? u / (tx * G.nz) : (u / tx) % ty;
+    const int z = G.z_first ? (u / tx) % G.nz : u / (tx * ty), b = z / g.splits, s = z % g.splits;
     const int m0 = uy * TM;
     for (int tj = 0; tj < g.ntiles; ++tj) {
     const int n0 = (ux * g.ntiles + tj) * BN;
@@ -404,11 +408,12 @@ Units units_of(const GemmArgs &g, int batch, int tm) {
 }
 
 template <bool B_KCONTIG, bool OUT_F32, int NST = NST_STREAM, int WV = WV_STREAM, int TM = BM>
-hipError_t launch_gemm(const GemmArgs &g, int batch, hipStream_t st) {
+hipError_t launch_gemm(const GemmArgs &g, int batch, hipStream_t st, bool z_first = false) {
     const Units u = units_of(g, batch, TM);
     GemmPair G{};
     G.p0 = g; G.p1 = g;
     G.units0 = u.n; G.tx0 = G.tx1 = u.tx; G.ty0 = G.ty1 = u.ty;
+    G.z_first = z_first ? 1 : 0; G.nz = batch * g.splits;
     launch_timed((gemm_bf16_kernel<B_KCONTIG, OUT_F32, NST, WV, TM>), dim3((unsigned)u.n), dim3(64 * WV), 0, st,
                  G);
     return hipGetLastError();
@@ -603,7 +608,13 @@ hipError_t launch_absorb_out_mfma(const void *o_lat, const void *w_uv, const voi
     g1.B = (const uint16_t *)w_uv;  g1.ldb = d_v; g1.bsb = (int64_t)d_c * d_v;
     g1.C = u_ws; g1.ldc = (int64_t)n_h * d_v; g1.bsc = d_v; g1.css = 0;
     g1.M = T; g1.N = d_v; g1.K = d_c; g1.splits = 1; g1.ntiles = 1;
-    hipError_t e = launch_gemm<false, false>(g1, n_h, s);
+    // few 128-row tiles (one per head at T <= 128): 64-row tiles double the
+    // workgroups, and the two of a head share an XCD (row tile slowest in the
+    // grid, n_h * column tiles apart) so its W_UV tile comes from L2 the second time
+    const int64_t tiles1 = (int64_t)n_h * ((d_v + BN - 1) / BN) * ((T + BM - 1) / BM);
+    const bool t64 = T > 64 && 2 * tiles1 <= 256 && ((int64_t)n_h * ((d_v + BN - 1) / BN)) % 8 == 0;
+    hipError_t e = t64 ? launch_gemm<false, false, NST_STREAM, 8, 64>(g1, n_h, s, true)
+                       : launch_gemm<false, false>(g1, n_h, s);
     if (e != hipSuccess) return e;
     // out = u . W_O over K = n_h d_v, split into fp32 partials, then summed
     const int32_t K = n_h * d_v;

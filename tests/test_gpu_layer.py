@@ -35,6 +35,8 @@ def test_absorb_q(dt, T, n_h, d_nope, d_c):
     ("f32", 3, 8, 64, 32, 256),
     ("bf16", 5, 16, 512, 128, 640),
     ("bf16", 130, 128, 512, 128, 5120),
+    ("bf16", 128, 128, 512, 128, 5120),   # W_UV on 64-row tiles, a head's two on one XCD
+    ("bf16", 100, 64, 512, 128, 1024),    # the same with a ragged second row tile
 ])
 def test_absorb_out(dt, T, n_h, d_c, d_v, d_model):
     g = torch.Generator()
