@@ -79,3 +79,65 @@ def test_graph_replays_match_eager(entry, kv):
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_ref) and torch.equal(l_g, l_ref)
     assert not torch.equal(o2, o_ref)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_project_step_graph_replays_match_eager(kv):
+    """mla_project_step captured in a HIP graph (its three launches): each of
+    three replays, from the same starting cache, writes the same q_lat,
+    q_rope, cache rows and block scales as the eager call, with an eager
+    call on other inputs (same workspace, another cache) between replays."""
+    B, q_len, dm, ql, n_h, dn, dc, dr = 5, 3, 256, 128, 4, 128, 512, 64
+    T = B * q_len
+    g = torch.Generator().manual_seed(43)
+    bf = torch.bfloat16
+    rnd = lambda *shape, std=1.0: (torch.randn(*shape, generator=g) * std).to(bf).to(DEV)
+    h, h2 = rnd(T, dm), rnd(T, dm)
+    w_dkvq = rnd(dm, ql + dc + dr, std=dm ** -0.5)
+    w_uq, w_qr, w_uk = rnd(ql, n_h * dn, std=ql ** -0.5), rnd(dm, n_h * dr, std=dm ** -0.5), rnd(n_h, dc, dn, std=dc ** -0.5)
+    nblk = 4
+    bt = torch.randperm(B * nblk + 3, generator=g)[:B * nblk].view(B, nblk).to(torch.int32).to(DEV)
+    pos0 = torch.randint(0, 190, (B,), generator=g, dtype=torch.int32).to(DEV)
+    bb = 64 * (dc + dr) * 2 if kv == "bf16" else 64 * dc + 64 * dr * 2   # bytes of one paged block
+    pool0 = torch.randint(0, 256, (B * nblk + 3, bb), generator=g, dtype=torch.uint8).to(DEV)
+    scales0 = (torch.rand(B * nblk + 3, generator=g) + 0.5).to(DEV) if kv != "bf16" else None
+    mk = lambda: api.DeviceCache(pool0.clone(), None if scales0 is None else scales0.clone(), kv, dc, dr)
+    cfg = api.rope()
+    need = api.project_step_workspace_bytes(B, q_len, dm, ql, n_h, dn, dc, dr, bf)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = lambda: (torch.empty((T, n_h, dc), dtype=bf, device=DEV), torch.empty((T, n_h, dr), dtype=bf, device=DEV))
+
+    ref_cache, (ql_ref, qr_ref) = mk(), out()
+    api.project_step(h, w_dkvq, w_uq, w_qr, w_uk, ref_cache, bt, pos0, q_len, n_h, dn, cfg, ql_ref, qr_ref, ws)
+    torch.cuda.synchronize()
+
+    cache, (ql_g, qr_g) = mk(), out()
+    other, (ql_o, qr_o) = mk(), out()
+    s0 = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(s0)
+    with torch.cuda.stream(side):                        # warm-up off the capture
+        api.project_step(h, w_dkvq, w_uq, w_qr, w_uk, cache, bt, pos0, q_len, n_h, dn, cfg, ql_g, qr_g, ws,
+                         stream=side)
+    s0.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        api.project_step(h, w_dkvq, w_uq, w_qr, w_uk, cache, bt, pos0, q_len, n_h, dn, cfg, ql_g, qr_g, ws,
+                         stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+
+    for _ in range(3):
+        cache.pool.copy_(pool0)
+        if scales0 is not None:
+            cache.block_scales.copy_(scales0)
+        ql_g.fill_(float("nan"))
+        qr_g.fill_(float("nan"))
+        api.project_step(h2, w_dkvq, w_uq, w_qr, w_uk, other, bt, pos0, q_len, n_h, dn, cfg, ql_o, qr_o, ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ql_g, ql_ref) and torch.equal(qr_g, qr_ref)
+        assert torch.equal(cache.pool, ref_cache.pool)
+        if scales0 is not None:
+            assert torch.equal(cache.block_scales, ref_cache.block_scales)
