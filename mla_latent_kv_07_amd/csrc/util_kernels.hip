@@ -145,6 +145,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const PartT *__restrict__ 
     if (lane == 0) lse[out_row] = m + logf(wsum);
 }
 
+// 8 merged features of a lane, times inv, as bf16 (one 16-byte store) or fp32
+template <typename OutT>
+__device__ __forceinline__ void store_row(uint4 *dst, const float (&acc)[8], float inv) {
+    if constexpr (sizeof(OutT) == 2) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pk[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+        *dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+        float4 *d4 = (float4 *)dst;
+        d4[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        d4[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    }
+}
+
 // Fast path for bf16 partials of 512 latent features (the MFMA decode's
 // split output): one wave per output row, lane owns features 8l..8l+7 (one
 // 16-byte load per split).  The partial rows of up to 8 splits are requested
@@ -177,13 +193,48 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
 #pragma unroll
     for (int u = 0; u < U; ++u)
         v[u] = u < n ? *(const uint4 *)(src0 + u * split_stride) : make_uint4(0, 0, 0, 0);
+    uint4 *dst = (uint4 *)(o_lat + out_row * 512 + lane * 8);
+    if (n <= U) {
+        // at most U splits: their LSEs are wave-uniform, so scalar loads
+        // beside the row loads, and the max and the weights take no
+        // cross-lane step (the shuffle reductions cost ~0.7 us per wave)
+        const __attribute__((address_space(4))) float *lse_s = (const __attribute__((address_space(4))) float *)lse_part;
+        float lk[U], m = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            lk[u] = u < n ? lse_s[(int64_t)(k0 + u) * rows + r] : -INFINITY;
+            m = fmaxf(m, lk[u]);
+        }
+        if (m == -INFINITY) {
+            *dst = make_uint4(0, 0, 0, 0);
+            if constexpr (sizeof(OutT) == 4) dst[1] = make_uint4(0, 0, 0, 0);
+            if (lane == 0) lse[out_row] = -INFINITY;
+            return;
+        }
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float wsum = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = lk[u] == -INFINITY ? 0.f : __expf(lk[u] - m);
+            wsum += w;
+            if (w == 0.f) continue;   // split without visible tokens (or past n)
+            const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += w * __uint_as_float(x[e] << 16);
+                acc[2 * e + 1] += w * __uint_as_float(x[e] & 0xffff0000u);
+            }
+        }
+        store_row<OutT>(dst, acc, 1.0f / wsum);
+        if (lane == 0) lse[out_row] = m + __logf(wsum);
+        return;
+    }
     // lane j holds the lse of split j (the first 64), loaded with the rows
     const float l0 = lane < n ? lse_part[(int64_t)(k0 + lane) * rows + r] : -INFINITY;
     float m = l0;
     for (int c = 64; c < n; c += 64)
         if (c + lane < n) m = fmaxf(m, lse_part[(int64_t)(k0 + c + lane) * rows + r]);
     m = wave_max(m);
-    uint4 *dst = (uint4 *)(o_lat + out_row * 512 + lane * 8);
     if (m == -INFINITY) {
         *dst = make_uint4(0, 0, 0, 0);
         if constexpr (sizeof(OutT) == 4) dst[1] = make_uint4(0, 0, 0, 0);
@@ -223,18 +274,7 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
             }
         }
     }
-    const float inv = 1.0f / wsum;
-    if constexpr (sizeof(OutT) == 2) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            pk[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
-        *dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    } else {
-        float4 *d4 = (float4 *)dst;
-        d4[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-        d4[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-    }
+    store_row<OutT>(dst, acc, 1.0f / wsum);
     if (lane == 0) lse[out_row] = m + __logf(wsum);
 }
 
