@@ -199,10 +199,11 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
         // beside the row loads, and the max and the weights take no
         // cross-lane step (the shuffle reductions cost ~0.7 us per wave)
         const __attribute__((address_space(4))) float *lse_s = (const __attribute__((address_space(4))) float *)lse_part;
+        const int ru = __builtin_amdgcn_readfirstlane(r);   // the wave's row, as a scalar
         float lk[U], m = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            lk[u] = u < n ? lse_s[(int64_t)(k0 + u) * rows + r] : -INFINITY;
+            lk[u] = u < n ? lse_s[(int64_t)(k0 + u) * rows + ru] : -INFINITY;
             m = fmaxf(m, lk[u]);
         }
         if (m == -INFINITY) {
