@@ -45,13 +45,15 @@ def test_decode_bf16_mfma_splits_and_combine():
     compare_decode(d, o, lse)
 
 
-def test_decode_bf16_many_splits_wide_combine():
+@pytest.mark.parametrize("seq,cus,min_splits", [((6000, 70, 0), 96, 16),
+                                               ((16384, 70, 0), 256, 96)])
+def test_decode_bf16_many_splits_wide_combine(seq, cus, min_splits):
     # a long sequence split over many CUs: more than 16 partial slots per
-    # segment take the workgroup-per-row merge; a short and an empty
-    # sequence ride along
-    d = small("bf16", seq=(6000, 70, 0), seed=12)
-    o, lse, dec = run_decode(d, cus=96)
-    assert dec.info.max_splits > 16, dec.info.max_splits
+    # segment take the workgroup-per-row merge (more than 96: several rounds
+    # of partial rows per wave); a short and an empty sequence ride along
+    d = small("bf16", seq=seq, seed=12)
+    o, lse, dec = run_decode(d, cus=cus)
+    assert dec.info.max_splits > min_splits, dec.info.max_splits
     compare_decode(d, o, lse)
 
 
