@@ -166,8 +166,15 @@ __device__ __forceinline__ void store_row(uint4 *dst, const float (&acc)[8], flo
 // 16-byte load per split).  The partial rows of up to 8 splits are requested
 // before the split weights are known, so a row costs one memory round trip
 // per 8 splits instead of one per split.
-template <typename OutT>
-__global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restrict__ o_part,
+// FEW: every segment of the launch has at most 8 splits (the plan's
+// max_splits), so only that path is compiled; it fits in 64 VGPRs, which
+// lets 8 waves per SIMD run at once: batches with more rows than one round of
+// waves at the general variant's 114 VGPRs (4 per SIMD, kCombineRound rows on
+// 256 CUs) wait out fewer rounds of memory latency.  Within one round the
+// general variant measured 0.1 us faster, so it keeps those.
+constexpr int64_t kCombineRound = 256 * 16;
+template <typename OutT, bool FEW = false>
+__global__ __launch_bounds__(256, FEW ? 8 : 1) void combine512_kernel(const uint16_t *__restrict__ o_part,
                                                          const float *__restrict__ lse_part,
                                                          const int32_t *__restrict__ split_off,
                                                          const int32_t *__restrict__ seq_flags,
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
     for (int u = 0; u < U; ++u)
         v[u] = u < n ? *(const uint4 *)(src0 + u * split_stride) : make_uint4(0, 0, 0, 0);
     uint4 *dst = (uint4 *)(o_lat + out_row * 512 + lane * 8);
-    if (n <= U) {
+    if (FEW || n <= U) {
         // at most U splits: their LSEs are wave-uniform, so scalar loads
         // beside the row loads, and the max and the weights take no
         // cross-lane step (the shuffle reductions cost ~0.7 us per wave)
@@ -230,6 +237,7 @@ __global__ __launch_bounds__(256) void combine512_kernel(const uint16_t *__restr
         if (lane == 0) lse[out_row] = m + __logf(wsum);
         return;
     }
+    if constexpr (FEW) return;
     // lane j holds the lse of split j (the first 64), loaded with the rows
     const float l0 = lane < n ? lse_part[(int64_t)(k0 + lane) * rows + r] : -INFINITY;
     float m = l0;
@@ -459,6 +467,13 @@ hipError_t launch_combine(const void *o_part, mla_dtype_t part_dt, const float *
                          lse_part, split_off, seq_flags, rows, chunk_rows, (uint16_t *)o_lat, lse);
         else
             launch_timed(combine512_wide_kernel<float>, wide, dim3(256), 0, s, (const uint16_t *)o_part,
+                         lse_part, split_off, seq_flags, rows, chunk_rows, (float *)o_lat, lse);
+    } else if (part_dt == MLA_DT_BF16 && d_c == 512 && max_splits <= 8 && (int64_t)B * rows > kCombineRound) {
+        if (out_dt == MLA_DT_BF16)
+            launch_timed(combine512_kernel<uint16_t, true>, grid, dim3(256), 0, s, (const uint16_t *)o_part,
+                         lse_part, split_off, seq_flags, rows, chunk_rows, (uint16_t *)o_lat, lse);
+        else
+            launch_timed(combine512_kernel<float, true>, grid, dim3(256), 0, s, (const uint16_t *)o_part,
                          lse_part, split_off, seq_flags, rows, chunk_rows, (float *)o_lat, lse);
     } else if (part_dt == MLA_DT_BF16 && d_c == 512) {
         if (out_dt == MLA_DT_BF16)
